@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the Lightning Attention layer.
+
+This module only draws numbers: it holds none of the layer's arithmetic, and
+both the GPU path and the CPU oracle are fed from it.  Every stream is
+numpy ``Generator(PCG64(SeedSequence(key)))`` with ``key = [2025, workload,
+tensor, chunk]``, so any piece of any workload can be regenerated on its own
+(the 1M-token workloads are generated chunk by chunk, never whole).
+
+Values are ``standard_normal(float32)`` times a scale (in fp32), then rounded
+to bf16 with round-to-nearest-even when the workload is bf16.  Arrays are
+returned as float32 holding exactly representable values, so converting them
+to torch bf16 or to float64 is exact.
+
+Workload distributions (the layer's inputs are pre-activation q/k/v/gate):
+  * "unit":    q, k, v, gate ~ N(0, 1), norm weight all ones;
+  * "minimax": q, k, v ~ N(0, 1)/sqrt(D), gate ~ N(0, 1), weight ~ N(1, 0.02).
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+SEED = 2025
+CHUNK_TOKENS = 65536
+
+# tensor ids inside a workload key
+Q, K, V, G, W, LENGTHS, HEAD_PICK, S0_K, S0_V = range(9)
+
+# workload ids (order of the workload list in the design doc)
+TINY_FP32, PREFILL_8K, DECODE, VARLEN_1M, PREFILL_1M = 1, 2, 3, 4, 5
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def stream(key, n: int) -> np.ndarray:
+    """First n standard normals (float32) of the stream named by key."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+    return g.standard_normal(n, dtype=np.float32)
+
+
+def normal(key, shape, scale: float = 1.0, mean: float = 0.0, bf16: bool = True) -> np.ndarray:
+    """Array of the given shape from one stream: mean + scale * N(0,1), fp32 math."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    x = stream(key, n).reshape(shape)
+    if scale != 1.0:
+        x = x * np.float32(scale)
+    if mean != 0.0:
+        x = x + np.float32(mean)
+    return round_bf16(x) if bf16 else x.astype(np.float32)
+
+
+def scales(dist: str, D: int):
+    """(q/k/v scale, gate scale, weight mean, weight std) for a distribution."""
+    if dist == "unit":
+        return 1.0, 1.0, 1.0, 0.0
+    if dist == "minimax":
+        return 1.0 / math.sqrt(D), 1.0, 1.0, 0.02
+    raise ValueError("unknown distribution %r" % dist)
+
+
+def token_tensor(workload: int, tensor: int, t0: int, t1: int, H: int, D: int, scale: float,
+                 bf16: bool = True, threads: int = 1) -> np.ndarray:
+    """Tokens [t0, t1) of a [T, H, D] activation, drawn per 65,536-token chunk.
+
+    Chunk c of the tensor is the stream [2025, workload, tensor, c]; its first
+    (t - 65536 c) * H * D values belong to tokens before t.
+    """
+    out = np.empty((t1 - t0, H, D), np.float32)
+    HD = H * D
+    pieces = []
+    c = t0 // CHUNK_TOKENS
+    while c * CHUNK_TOKENS < t1:
+        a = max(t0, c * CHUNK_TOKENS)
+        b = min(t1, (c + 1) * CHUNK_TOKENS)
+        pieces.append((c, a, b))
+        c += 1
+
+    def fill(p):
+        c, a, b = p
+        base = c * CHUNK_TOKENS
+        x = stream((SEED, workload, tensor, c), (b - base) * HD)[(a - base) * HD:]
+        x = x.reshape(b - a, H, D)
+        if scale != 1.0:
+            x = x * np.float32(scale)
+        out[a - t0:b - t0] = round_bf16(x) if bf16 else x
+
+    if threads > 1 and len(pieces) > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, pieces))
+    else:
+        for p in pieces:
+            fill(p)
+    return out
+
+
+def layer_inputs(workload: int, T: int, H: int, D: int, dist: str, bf16: bool = True,
+                 t0: int = 0, threads: int = 1):
+    """q, k, v, gate for tokens [t0, t0+T) and the norm weight [H*D]."""
+    s, gs, wm, ws = scales(dist, D)
+    q = token_tensor(workload, Q, t0, t0 + T, H, D, s, bf16, threads)
+    k = token_tensor(workload, K, t0, t0 + T, H, D, s, bf16, threads)
+    v = token_tensor(workload, V, t0, t0 + T, H, D, s, bf16, threads)
+    g = token_tensor(workload, G, t0, t0 + T, H, D, gs, bf16, threads)
+    w = norm_weight(workload, H, D, dist, bf16)
+    return q, k, v, g, w
+
+
+def norm_weight(workload: int, H: int, D: int, dist: str, bf16: bool = True) -> np.ndarray:
+    _, _, wm, ws = scales(dist, D)
+    if ws == 0.0:
+        return np.full(H * D, np.float32(wm), np.float32)
+    return normal((SEED, workload, W, 0), (H * D,), scale=ws, mean=wm, bf16=bf16)
+
+
+def varlen_lengths(total: int, lo: int = 1024, hi: int = 131072, workload: int = VARLEN_1M):
+    """Sequence lengths drawn log-uniform in [lo, hi) until they reach `total`.
+
+    L = floor(exp(U[ln lo, ln hi))); drawing stops once the running sum reaches
+    `total` and the last length is cut so the sum is exactly `total`.
+    """
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, workload, LENGTHS, 0])))
+    lens = []
+    acc = 0
+    while acc < total:
+        L = int(math.floor(math.exp(g.uniform(math.log(lo), math.log(hi)))))
+        L = min(L, total - acc)
+        lens.append(L)
+        acc += L
+    return lens
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int64)
+
+
+def decode_prefix_lengths(nseq: int, lo: int = 1024, hi: int = 32768, workload: int = DECODE):
+    """Per-sequence prefill length for the decode workload's initial state, U{lo..hi}."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, workload, LENGTHS, 0])))
+    return [int(x) for x in g.integers(lo, hi, size=nseq, endpoint=True)]
+
+
+def decode_prefix_kv(seq: int, L: int, H: int, D: int, dist: str = "unit",
+                     workload: int = DECODE):
+    """k, v [L, H, D] of sequence `seq`'s prefill that defines its initial state."""
+    s, _, _, _ = scales(dist, D)
+    k = normal((SEED, workload, S0_K, seq), (L, H, D), scale=s)
+    v = normal((SEED, workload, S0_V, seq), (L, H, D), scale=s)
+    return k, v
+
+
+def decode_step_inputs(step: int, nseq: int, H: int, D: int, dist: str = "unit",
+                       workload: int = DECODE):
+    """Fresh q, k, v, gate [nseq, H, D] for decode step `step`."""
+    s, gs, _, _ = scales(dist, D)
+    return tuple(normal((SEED, workload, t, 1000 + step), (nseq, H, D), scale=(gs if t == G else s))
+                 for t in (Q, K, V, G))
+
+
+def pick_heads(n: int, H: int, workload: int) -> list:
+    """n distinct heads chosen by the seeded stream of a workload."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, workload, HEAD_PICK, 0])))
+    return sorted(int(h) for h in g.choice(H, size=n, replace=False))

@@ -1,0 +1,229 @@
+/*
+ * Lightning Attention CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64 statement of what the Lightning Attention layer computes.
+ * Only tests/, the smoke check and the bench's cpu_baseline leg may load it;
+ * the GPU library shares no code with it and never calls it.
+ *
+ * Source of the method: "Diving into MiniMax01 405B MoE" (Hugging Face blog),
+ * section "Hybrid Modeling", 7/8 Linear Attention (Lightning Attention-2),
+ * Mechanism steps 1-4:  Q, K, V = SiLU(input); Y = Q (K^T V) at O(d^2) per
+ * token; output = RMSNorm(Y) * sigmoid(gate input).  The model card
+ * ("2. Model Architecture") fixes 64 heads of dimension 128.
+ *
+ * Readings taken where the page is silent (each is listed in the design doc):
+ *  - causal, the current token included: the state after token t holds
+ *    sum_{u<=t} k~_u^T v~_u and y_t = q~_t S_t (decode order "kv += k^T v,
+ *    then y = q kv");
+ *  - no 1/sqrt(d) scale, no decay, no normaliser (NormAttention family: the
+ *    output norm replaces the softmax denominator);
+ *  - RMSNorm over all H*D values of a token: mean of squares, eps inside the
+ *    square root, then the weight w[h*D+d], then the elementwise sigmoid gate;
+ *  - the state S is D_k x D_v, row = key dimension: S[i][j] += k~_i v~_j.
+ *
+ * Layouts: activations token-major [T][H][D]; states [nseq][H][D][D].
+ * Segments (batch rows or packed varlen sequences) are given by seg[0..nseq],
+ * seg[0] = 0, nondecreasing, seg[nseq] = T; each starts from its own state.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* logistic function, 1 / (1 + e^-x), straight from its definition */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+/* SiLU(x) = x * sigmoid(x)  (Mechanism step 2) */
+static double silu(double x) { return x * sigmoid(x); }
+
+double la_oracle_sigmoid(double x) { return sigmoid(x); }
+double la_oracle_silu(double x) { return silu(x); }
+
+/*
+ * Mechanism step 4 for one token: y holds the H*D raw attention outputs of
+ * the token; it is overwritten with RMSNorm(y) * w * sigmoid(g).
+ */
+static void norm_gate_token(double* y, const double* g, const double* w, int64_t HD, double eps) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < HD; ++i) ss += y[i] * y[i];
+    double r = 1.0 / sqrt(ss / (double)HD + eps);
+    for (int64_t i = 0; i < HD; ++i) y[i] = y[i] * r * w[i] * sigmoid(g[i]);
+}
+
+/*
+ * Prefill by the token recurrence (Mechanism steps 2-4, causal reading):
+ *   S <- S0;  for each token t:  S <- S + k~_t^T v~_t ;  y_t = q~_t S.
+ * out receives the final layer output [T][H][D]; y_raw (optional) the
+ * pre-norm y; final_state (optional) the state after the last token.
+ */
+int la_oracle_prefill(const double* q, const double* k, const double* v, const double* g,
+                      const double* w, const int64_t* seg, int64_t nseq, int64_t H, int64_t D,
+                      double eps, const double* init_state, double* out, double* y_raw,
+                      double* final_state) {
+    const int64_t HD = H * D;
+    const int64_t T = seg[nseq];
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t s = 0; s < nseq; ++s) {
+        for (int64_t h = 0; h < H; ++h) {
+            double* S = (double*)malloc(sizeof(double) * D * D);
+            double* qt = (double*)malloc(sizeof(double) * D * 3);
+            double* kt = qt + D;
+            double* vt = qt + 2 * D;
+            if (init_state) memcpy(S, init_state + (s * H + h) * D * D, sizeof(double) * D * D);
+            else memset(S, 0, sizeof(double) * D * D);
+            for (int64_t t = seg[s]; t < seg[s + 1]; ++t) {
+                const int64_t base = t * HD + h * D;
+                for (int64_t i = 0; i < D; ++i) {
+                    qt[i] = silu(q[base + i]);
+                    kt[i] = silu(k[base + i]);
+                    vt[i] = silu(v[base + i]);
+                }
+                /* state update first: the current token attends to itself */
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[i] * vt[j];
+                /* y_t = q~_t S */
+                for (int64_t j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < D; ++i) acc += qt[i] * S[i * D + j];
+                    out[base + j] = acc;
+                }
+            }
+            if (final_state) memcpy(final_state + (s * H + h) * D * D, S, sizeof(double) * D * D);
+            free(qt);
+            free(S);
+        }
+    }
+    if (y_raw) memcpy(y_raw, out, sizeof(double) * T * HD);
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) norm_gate_token(out + t * HD, g + t * HD, w, HD, eps);
+    return 0;
+}
+
+/*
+ * Prefill by the block-tiled form the Lightning Attention-2 design implies
+ * (intra-block masked product plus inter-block product against the running
+ * state), used to pin block-size invariance.  Per segment and head, with
+ * blocks of `block` tokens and S the state before the block:
+ *   Y_b = (Q~_b K~_b^T (.) M) V~_b + Q~_b S,   M_ij = 1 iff j <= i
+ *   S  <- S + K~_b^T V~_b
+ */
+int la_oracle_prefill_blocked(const double* q, const double* k, const double* v, const double* g,
+                              const double* w, const int64_t* seg, int64_t nseq, int64_t H,
+                              int64_t D, int64_t block, double eps, const double* init_state,
+                              double* out, double* final_state) {
+    const int64_t HD = H * D;
+    const int64_t T = seg[nseq];
+    if (block < 1) return 1;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t s = 0; s < nseq; ++s) {
+        for (int64_t h = 0; h < H; ++h) {
+            double* S = (double*)malloc(sizeof(double) * D * D);
+            double* Qb = (double*)malloc(sizeof(double) * block * D * 3);
+            double* Kb = Qb + block * D;
+            double* Vb = Qb + 2 * block * D;
+            if (init_state) memcpy(S, init_state + (s * H + h) * D * D, sizeof(double) * D * D);
+            else memset(S, 0, sizeof(double) * D * D);
+            for (int64_t t0 = seg[s]; t0 < seg[s + 1]; t0 += block) {
+                int64_t n = seg[s + 1] - t0;
+                if (n > block) n = block;
+                for (int64_t a = 0; a < n; ++a)
+                    for (int64_t i = 0; i < D; ++i) {
+                        const int64_t idx = (t0 + a) * HD + h * D + i;
+                        Qb[a * D + i] = silu(q[idx]);
+                        Kb[a * D + i] = silu(k[idx]);
+                        Vb[a * D + i] = silu(v[idx]);
+                    }
+                for (int64_t a = 0; a < n; ++a) {
+                    double* y = out + (t0 + a) * HD + h * D;
+                    /* inter-block: q~_a S (state before this block) */
+                    for (int64_t j = 0; j < D; ++j) {
+                        double acc = 0.0;
+                        for (int64_t i = 0; i < D; ++i) acc += Qb[a * D + i] * S[i * D + j];
+                        y[j] = acc;
+                    }
+                    /* intra-block: sum over c <= a of (q~_a . k~_c) v~_c */
+                    for (int64_t c = 0; c <= a; ++c) {
+                        double sc = 0.0;
+                        for (int64_t i = 0; i < D; ++i) sc += Qb[a * D + i] * Kb[c * D + i];
+                        for (int64_t j = 0; j < D; ++j) y[j] += sc * Vb[c * D + j];
+                    }
+                }
+                for (int64_t a = 0; a < n; ++a)
+                    for (int64_t i = 0; i < D; ++i)
+                        for (int64_t j = 0; j < D; ++j) S[i * D + j] += Kb[a * D + i] * Vb[a * D + j];
+            }
+            if (final_state) memcpy(final_state + (s * H + h) * D * D, S, sizeof(double) * D * D);
+            free(Qb);
+            free(S);
+        }
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) norm_gate_token(out + t * HD, g + t * HD, w, HD, eps);
+    return 0;
+}
+
+/*
+ * One decode step: every sequence receives one token; its state is read,
+ * updated in place (S += k~^T v~) and used for y = q~ S, then the token's
+ * output is normalised and gated (constant memory per layer, which is what
+ * cached generation with a linear-attention layer requires).
+ * q, k, v, g, out: [nseq][H][D]; state: [nseq][H][D][D], updated in place.
+ */
+int la_oracle_decode(const double* q, const double* k, const double* v, const double* g,
+                     const double* w, int64_t nseq, int64_t H, int64_t D, double eps,
+                     double* state, double* out) {
+    const int64_t HD = H * D;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t s = 0; s < nseq; ++s) {
+        for (int64_t h = 0; h < H; ++h) {
+            double* S = state + (s * H + h) * D * D;
+            const int64_t base = s * HD + h * D;
+            for (int64_t i = 0; i < D; ++i)
+                for (int64_t j = 0; j < D; ++j) S[i * D + j] += silu(k[base + i]) * silu(v[base + j]);
+            for (int64_t j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < D; ++i) acc += silu(q[base + i]) * S[i * D + j];
+                out[base + j] = acc;
+            }
+        }
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < nseq; ++s) norm_gate_token(out + s * HD, g + s * HD, w, HD, eps);
+    return 0;
+}
+
+/*
+ * State after a prefill without its outputs: S = S0 + sum_t k~_t^T v~_t per
+ * segment and head (the decode workload's initial state is defined this way).
+ */
+int la_oracle_state(const double* k, const double* v, const int64_t* seg, int64_t nseq, int64_t H,
+                    int64_t D, double* state) {
+    const int64_t HD = H * D;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t s = 0; s < nseq; ++s) {
+        for (int64_t h = 0; h < H; ++h) {
+            double* S = state + (s * H + h) * D * D;
+            double* kt = (double*)malloc(sizeof(double) * D * 2);
+            double* vt = kt + D;
+            for (int64_t t = seg[s]; t < seg[s + 1]; ++t) {
+                for (int64_t i = 0; i < D; ++i) {
+                    kt[i] = silu(k[t * HD + h * D + i]);
+                    vt[i] = silu(v[t * HD + h * D + i]);
+                }
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[i] * vt[j];
+            }
+            free(kt);
+        }
+    }
+    return 0;
+}
+
+/* thread control for the timed baseline (OpenMP over segments x heads) */
+#ifdef _OPENMP
+#include <omp.h>
+void la_oracle_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+int la_oracle_max_threads(void) { return omp_get_max_threads(); }
+#else
+void la_oracle_set_threads(int n) { (void)n; }
+int la_oracle_max_threads(void) { return 1; }
+#endif

@@ -1,0 +1,225 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each pin takes the oracle module (so the mutation test can run it against
+copies of the oracle with a planted mistake) and raises AssertionError when
+the oracle disagrees with:
+  * a different algorithm (the quadratic left product, tests/brute.py);
+  * closed forms derived by hand for special inputs;
+  * invariants of the definition (causality, RMSNorm, head permutation,
+    block-size invariance, decode-after-prefill, segment independence);
+  * library routines for the elementwise functions (scipy.special.expit).
+The layer is the Lightning Attention Mechanism of "Diving into MiniMax01 405B
+MoE" (section "Hybrid Modeling"), under the causal reading with the current
+token included.
+"""
+import math
+
+import numpy as np
+from scipy.special import expit
+
+import brute
+
+TIGHT = 1e-12
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    m = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / m)
+
+
+def rnd(seed, shape, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def pin_elementwise(orc):
+    """sigmoid/SiLU against scipy's expit and textbook identities."""
+    xs = np.linspace(-30.0, 30.0, 241)
+    for x in xs:
+        s = orc.sigmoid(x)
+        assert abs(s - expit(x)) <= 1e-15 + 1e-13 * abs(expit(x)), (x, s)
+        assert abs(orc.silu(x) - x * expit(x)) <= 1e-13 * max(1.0, abs(x)), x
+        assert abs(orc.sigmoid(x) + orc.sigmoid(-x) - 1.0) < 1e-15
+        assert abs((orc.silu(x) - orc.silu(-x)) - x) < 1e-12 * max(1.0, abs(x))
+    assert orc.sigmoid(0.0) == 0.5 and orc.silu(0.0) == 0.0
+    # sigmoid(ln 3) = 3/4 exactly in real arithmetic
+    assert abs(orc.sigmoid(math.log(3.0)) - 0.75) < 1e-15
+
+
+def pin_brute_force(orc):
+    """Recurrence == left product (Q~K~^T (.) M)V~ + Q~ S0 on tiny random inputs,
+    several segment layouts (including empty segments) and initial states."""
+    cases = [
+        (1, 1, [0, 5]),
+        (2, 3, [0, 7]),
+        (3, 4, [0, 3, 3, 9, 10]),
+        (2, 8, [0, 0, 16, 17, 40]),
+    ]
+    for ci, (H, D, seg) in enumerate(cases):
+        T = seg[-1]
+        q, k, v, g = (rnd(100 * ci + j, (T, H, D)) for j in range(4))
+        w = rnd(100 * ci + 5, (H * D,), 0.3) + 1.0
+        nseq = len(seg) - 1
+        for init in (None, rnd(100 * ci + 6, (nseq, H, D, D), 0.5)):
+            out, y = orc.prefill(q, k, v, g, w, cu_seqlens=seg, eps=1e-6, init_state=init,
+                                 return_y=True)
+            yb = brute.attention(q, k, v, seg, init)
+            ob = brute.layer(q, k, v, g, w, seg, 1e-6, init)
+            if T:
+                assert rel(y, yb) < TIGHT, ("y", H, D, seg, rel(y, yb))
+                assert rel(out, ob) < TIGHT, ("out", H, D, seg, rel(out, ob))
+
+
+def pin_first_token(orc):
+    """Closed form of the first token: y_0 = (q~_0 . k~_0) v~_0 + q~_0 S0."""
+    H, D, T = 2, 6, 4
+    q, k, v, g = (rnd(7 + j, (T, H, D)) for j in range(4))
+    w = np.ones(H * D)
+    s0 = rnd(11, (1, H, D, D))
+    _, y = orc.prefill(q, k, v, g, w, init_state=s0, return_y=True)
+    for h in range(H):
+        qs, ks, vs = (a[0, h] * expit(a[0, h]) for a in (q, k, v))
+        expect = np.dot(qs, ks) * vs + qs @ s0[0, h]
+        assert rel(y[0, h], expect) < TIGHT
+
+
+def pin_constant_closed_form(orc):
+    """All-constant input, derived by hand: with q = k = v = c, s = SiLU(c),
+    S0 = a * ones:  S_t = (a + (t+1) s^2) ones,  y_t = s D (a + (t+1) s^2) in
+    every entry; every entry of a token is equal so mean(y^2) = y^2 and
+    out_t = y_t / sqrt(y_t^2 + eps) * w * sigmoid(gam)."""
+    H, D, T = 3, 5, 9
+    for c, a, gam, wv, eps in ((1.0, 0.0, 0.0, 1.0, 1e-6), (-0.7, 0.25, 1.3, 0.5, 1e-2),
+                               (0.02, 0.0, -2.0, 2.0, 1e-6)):
+        s = c / (1.0 + math.exp(-c))
+        q = np.full((T, H, D), c)
+        g = np.full((T, H, D), gam)
+        w = np.full(H * D, wv)
+        init = np.full((1, H, D, D), a)
+        out, y = orc.prefill(q, q, q, g, w, eps=eps, init_state=init, return_y=True)
+        sg = 1.0 / (1.0 + math.exp(-gam))
+        for t in range(T):
+            yt = s * D * (a + (t + 1) * s * s)
+            ot = yt / math.sqrt(yt * yt + eps) * wv * sg
+            assert abs(y[t] - yt).max() <= 1e-12 * abs(yt) + 1e-300, (c, t)
+            assert abs(out[t] - ot).max() <= 1e-12 * abs(ot) + 1e-300, (c, t)
+
+
+def pin_rmsnorm_invariant(orc):
+    """Per token: mean_{h,d} (out / (w sigmoid(g)))^2 = ms / (ms + eps) with
+    ms = mean_{h,d} y^2 -- the norm runs over all heads of a token."""
+    H, D, T = 4, 8, 12
+    q, k, v, g = (rnd(20 + j, (T, H, D)) for j in range(4))
+    w = rnd(25, (H * D,), 0.1) + 1.0
+    for eps in (1e-6, 0.5):
+        out, y = orc.prefill(q, k, v, g, w, eps=eps, return_y=True)
+        z = out.reshape(T, -1) / (w[None, :] * expit(g.reshape(T, -1)))
+        ms = np.mean(y.reshape(T, -1) ** 2, axis=1)
+        lhs = np.mean(z * z, axis=1)
+        assert rel(lhs, ms / (ms + eps)) < 1e-12
+    # zero queries give y = 0 and an output of exactly 0 (eps avoids 0/0)
+    out = orc.prefill(np.zeros((T, H, D)), k, v, g, w)
+    assert np.all(out == 0.0)
+
+
+def pin_causality(orc):
+    """Changing token t's inputs leaves earlier outputs unchanged and changes
+    token t itself (the diagonal is included); the norm couples heads."""
+    H, D, T = 3, 4, 10
+    q, k, v, g = (rnd(30 + j, (T, H, D)) for j in range(4))
+    w = np.ones(H * D)
+    base = orc.prefill(q, k, v, g, w)
+    for t in (0, 4, 9):
+        for arr_i in (1, 2):  # k and v of token t
+            arrs = [q.copy(), k.copy(), v.copy()]
+            arrs[arr_i][t] += 0.5
+            o = orc.prefill(arrs[0], arrs[1], arrs[2], g, w)
+            assert np.array_equal(o[:t], base[:t])
+            assert rel(o[t], base[t]) > 1e-6
+    # perturbing head 0 only changes head 1's output at that token (norm)
+    q2 = q.copy()
+    q2[5, 0] *= 3.0
+    o = orc.prefill(q2, k, v, g, w)
+    assert rel(o[5, 1], base[5, 1]) > 1e-9
+    assert np.array_equal(o[:5], base[:5])
+
+
+def pin_head_permutation(orc):
+    """Permuting heads (q, k, v, g and the weight blocks) permutes the output."""
+    H, D, T = 4, 3, 7
+    q, k, v, g = (rnd(40 + j, (T, H, D)) for j in range(4))
+    w = rnd(45, (H * D,), 0.2) + 1.0
+    perm = np.array([2, 0, 3, 1])
+    out = orc.prefill(q, k, v, g, w)
+    wp = w.reshape(H, D)[perm].reshape(-1)
+    outp = orc.prefill(q[:, perm], k[:, perm], v[:, perm], g[:, perm], wp)
+    assert rel(outp, out[:, perm]) < TIGHT
+
+
+def pin_blocked(orc):
+    """Block-tiled form == token recurrence for block sizes 1, 7, 32, 64 and L;
+    block 1 is the recurrence, block L the full masked product."""
+    H, D = 2, 8
+    seg = [0, 50, 50, 123]
+    T = seg[-1]
+    q, k, v, g = (rnd(50 + j, (T, H, D)) for j in range(4))
+    w = rnd(55, (H * D,), 0.1) + 1.0
+    init = rnd(56, (3, H, D, D), 0.3)
+    ref, st = orc.prefill(q, k, v, g, w, cu_seqlens=seg, init_state=init, return_state=True)
+    for blk in (1, 7, 32, 64, T):
+        out, st2 = orc.prefill_blocked(q, k, v, g, w, blk, cu_seqlens=seg, init_state=init,
+                                       return_state=True)
+        assert rel(out, ref) < TIGHT, blk
+        assert rel(st2, st) < TIGHT, blk
+
+
+def pin_decode_after_prefill(orc):
+    """Rows L..L+m-1 of a prefill of L+m tokens == a prefill of L tokens
+    followed by m single-token decode steps carrying the state."""
+    H, D, L, m = 3, 6, 11, 4
+    q, k, v, g = (rnd(60 + j, (L + m, H, D)) for j in range(4))
+    w = rnd(65, (H * D,), 0.1) + 1.0
+    full = orc.prefill(q, k, v, g, w)
+    _, st = orc.prefill(q[:L], k[:L], v[:L], g[:L], w, return_state=True)
+    for i in range(m):
+        t = L + i
+        o, st = orc.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], w, st)
+        assert rel(o[0], full[t]) < TIGHT, i
+    # state == S0 + K~^T V~ (matrix product from numpy)
+    ks = k * expit(k)
+    vs = v * expit(v)
+    for h in range(H):
+        assert rel(st[0, h], ks[:, h].T @ vs[:, h]) < TIGHT
+
+
+def pin_segments_and_resume(orc):
+    """Packed segments == separate calls; prefill(a+b) == prefill(b) resumed
+    from the state after a; the state routine equals the prefill's state."""
+    H, D = 2, 5
+    lens = [6, 0, 13, 1]
+    seg = np.concatenate([[0], np.cumsum(lens)])
+    T = int(seg[-1])
+    q, k, v, g = (rnd(70 + j, (T, H, D)) for j in range(4))
+    w = np.ones(H * D)
+    packed, st = orc.prefill(q, k, v, g, w, cu_seqlens=seg, return_state=True)
+    for s in range(len(lens)):
+        a, b = int(seg[s]), int(seg[s + 1])
+        if a == b:
+            assert np.all(st[s] == 0.0)
+            continue
+        o, st1 = orc.prefill(q[a:b], k[a:b], v[a:b], g[a:b], w, return_state=True)
+        assert rel(packed[a:b], o) < TIGHT
+        assert rel(st[s], st1[0]) < TIGHT
+    assert rel(orc.state(k, v, cu_seqlens=seg), st) < TIGHT
+    a = 9
+    o_all, st_all = orc.prefill(q, k, v, g, w, return_state=True)
+    _, st_a = orc.prefill(q[:a], k[:a], v[:a], g[:a], w, return_state=True)
+    o_b, st_b = orc.prefill(q[a:], k[a:], v[a:], g[a:], w, init_state=st_a, return_state=True)
+    assert rel(o_b, o_all[a:]) < TIGHT
+    assert rel(st_b, st_all) < TIGHT
+
+
+ALL_PINS = [pin_elementwise, pin_brute_force, pin_first_token, pin_constant_closed_form,
+            pin_rmsnorm_invariant, pin_causality, pin_head_permutation, pin_blocked,
+            pin_decode_after_prefill, pin_segments_and_resume]

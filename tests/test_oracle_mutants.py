@@ -1,0 +1,111 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them: evidence that the pins constrain each part
+of the definition, not only the oracle's own formula."""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle  # noqa: E402
+import pins  # noqa: E402
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "la_oracle.c")
+
+# (name, original text, mutated text): each must occur exactly once
+MUTANTS = [
+    ("diagonal_excluded",
+     "                /* state update first: the current token attends to itself */\n"
+     "                for (int64_t i = 0; i < D; ++i)\n"
+     "                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[i] * vt[j];\n"
+     "                /* y_t = q~_t S */\n"
+     "                for (int64_t j = 0; j < D; ++j) {\n"
+     "                    double acc = 0.0;\n"
+     "                    for (int64_t i = 0; i < D; ++i) acc += qt[i] * S[i * D + j];\n"
+     "                    out[base + j] = acc;\n"
+     "                }\n",
+     "                for (int64_t j = 0; j < D; ++j) {\n"
+     "                    double acc = 0.0;\n"
+     "                    for (int64_t i = 0; i < D; ++i) acc += qt[i] * S[i * D + j];\n"
+     "                    out[base + j] = acc;\n"
+     "                }\n"
+     "                for (int64_t i = 0; i < D; ++i)\n"
+     "                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[i] * vt[j];\n"),
+    ("state_transposed",
+     "for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[i] * vt[j];\n                /* y_t",
+     "for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[j] * vt[i];\n                /* y_t"),
+    ("norm_sum_not_mean", "sqrt(ss / (double)HD + eps)", "sqrt(ss + eps)"),
+    ("eps_outside_sqrt", "sqrt(ss / (double)HD + eps)", "(sqrt(ss / (double)HD) + eps)"),
+    ("gate_silu", "y[i] * r * w[i] * sigmoid(g[i])", "y[i] * r * w[i] * silu(g[i])"),
+    ("gate_missing", "y[i] * r * w[i] * sigmoid(g[i])", "y[i] * r * w[i]"),
+    ("weight_per_dim", "y[i] * r * w[i] * sigmoid(g[i])", "y[i] * r * w[i % 2] * sigmoid(g[i])"),
+    ("no_silu_on_v", "vt[i] = silu(v[base + i]);", "vt[i] = v[base + i];"),
+    ("sigmoid_sign", "1.0 / (1.0 + exp(-x))", "1.0 / (1.0 + exp(x))"),
+    ("init_state_ignored",
+     "            if (init_state) memcpy(S, init_state + (s * H + h) * D * D, sizeof(double) * D * D);\n"
+     "            else memset(S, 0, sizeof(double) * D * D);\n"
+     "            for (int64_t t = seg[s]",
+     "            memset(S, 0, sizeof(double) * D * D);\n"
+     "            for (int64_t t = seg[s]"),
+    ("init_state_wrong_segment",
+     "            if (init_state) memcpy(S, init_state + (s * H + h) * D * D, sizeof(double) * D * D);\n"
+     "            else memset(S, 0, sizeof(double) * D * D);\n"
+     "            for (int64_t t = seg[s]",
+     "            if (init_state) memcpy(S, init_state + h * D * D, sizeof(double) * D * D);\n"
+     "            else memset(S, 0, sizeof(double) * D * D);\n"
+     "            for (int64_t t = seg[s]"),
+    ("decode_uses_old_state",
+     "                for (int64_t j = 0; j < D; ++j) S[i * D + j] += silu(k[base + i]) * silu(v[base + j]);\n"
+     "            for (int64_t j = 0; j < D; ++j) {\n"
+     "                double acc = 0.0;\n"
+     "                for (int64_t i = 0; i < D; ++i) acc += silu(q[base + i]) * S[i * D + j];\n"
+     "                out[base + j] = acc;\n"
+     "            }\n",
+     "                ;\n"
+     "            for (int64_t j = 0; j < D; ++j) {\n"
+     "                double acc = 0.0;\n"
+     "                for (int64_t i = 0; i < D; ++i) acc += silu(q[base + i]) * S[i * D + j];\n"
+     "                out[base + j] = acc;\n"
+     "            }\n"
+     "            for (int64_t i = 0; i < D; ++i)\n"
+     "                for (int64_t j = 0; j < D; ++j) S[i * D + j] += silu(k[base + i]) * silu(v[base + j]);\n"),
+    ("blocked_mask_strict", "for (int64_t c = 0; c <= a; ++c)", "for (int64_t c = 0; c < a; ++c)"),
+]
+
+
+def _build_mutant(tmpdir, orig, new):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, "mutation anchor must occur once: %r" % orig[:60]
+    path = os.path.join(tmpdir, "m.c")
+    with open(path, "w") as f:
+        f.write(src.replace(orig, new))
+    so = os.path.join(tmpdir, "libm.so")
+    subprocess.run(["gcc", "-O1", "-std=gnu99", "-fopenmp", "-fPIC", "-shared", path, "-o", so,
+                    "-lm"], check=True)
+    return so
+
+
+@pytest.mark.parametrize("name,orig,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, orig, new):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc missing")
+    tmp = tempfile.mkdtemp(prefix="la_mut_")
+    try:
+        so = _build_mutant(tmp, orig, new)
+        saved = oracle._load()
+        oracle._lib = oracle._bind(so)
+        failed = []
+        try:
+            for pin in pins.ALL_PINS:
+                try:
+                    pin(oracle)
+                except AssertionError:
+                    failed.append(pin.__name__)
+        finally:
+            oracle._lib = saved
+        assert failed, "no pin caught the planted mistake %s" % name
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
