@@ -1,0 +1,134 @@
+/*
+ * lightning_attn.h -- C ABI of the MI355X (gfx950) Lightning Attention library.
+ *
+ * The layer (blog "Diving into MiniMax01 405B MoE", section "Hybrid Modeling",
+ * 7/8 Linear Attention (Lightning Attention-2), Mechanism steps 1-4):
+ *     q~, k~, v~ = SiLU(q), SiLU(k), SiLU(v)                   (step 2)
+ *     y_t        = q~_t S_t,  S_t = S_0 + sum_{u<=t} k~_u^T v~_u  (step 3, causal)
+ *     out_t      = y_t / sqrt(mean_{h,d} y_t^2 + eps) * w * sigmoid(gate_t)   (step 4)
+ * with no 1/sqrt(d) scale, no decay and no normaliser.  The model card
+ * ("2. Model Architecture") fixes 64 heads of dimension 128.  y is computed
+ * blockwise: a masked intra-block product (Q~ K~^T (.) M) V~ plus an
+ * inter-block product Q~ S against a running fp32 state, the O(d^2)-per-token
+ * right product of Mechanism step 3.
+ *
+ * Conventions shared by every call
+ *   - Layout: activations token-major, element (t, h, d) at ((t*H)+h)*D + d;
+ *     norm weight [H*D] indexed h*D + d; states [nseq][H][D][D] fp32 with
+ *     state[i][j] = sum k~_i v~_j (row = key dimension, column = value dim).
+ *   - q, k, v, gate, norm_weight and out share one dtype (la_dtype).  The
+ *     state is always fp32.  Arithmetic is fp32 (bf16 MFMA operands with fp32
+ *     accumulation for bf16 inputs); out is rounded to the input dtype.
+ *   - All pointers are device pointers (hipMalloc'd or from a framework
+ *     allocator) and must be 16-byte aligned.  The caller owns all memory;
+ *     the library allocates nothing and keeps no global mutable state, so
+ *     calls are reentrant and thread-safe.
+ *   - Work is enqueued asynchronously on `stream`; calls do not synchronize.
+ *   - Errors: arguments are validated on the host before any HIP call; on a
+ *     validation error nothing is enqueued.  A launch failure reported by
+ *     hipGetLastError returns LA_ERR_HIP.  Device-side contents (cu_seqlens
+ *     values, non-finite inputs) are not checked; invalid cu_seqlens leave
+ *     `out` unspecified.  `out` must not alias an input.
+ */
+#ifndef LIGHTNING_ATTN_H
+#define LIGHTNING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_API __attribute__((visibility("default")))
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+    LA_ERR_BAD_SHAPE = 2,          /* a size is negative / zero where not allowed / inconsistent */
+    LA_ERR_UNSUPPORTED = 3,        /* head_dim, block, chunk or dtype outside the supported set */
+    LA_ERR_MISALIGNED = 4,         /* a pointer is not 16-byte aligned */
+    LA_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below the matching *_workspace_size() */
+    LA_ERR_HIP = 6                 /* the HIP runtime reported an error while enqueueing */
+} la_status;
+
+typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+LA_API const char* lightning_attn_status_string(la_status s);
+
+/*
+ * Supported shapes: head_dim in {16, 32, 64, 128}; block in {16, 32, 64} and
+ * block <= chunk; heads >= 1.  bf16 with head_dim 128 and block 64 runs the
+ * MFMA kernels; every other supported combination runs the fp32 vector-ALU
+ * kernels (same results up to rounding).
+ *
+ * chunk_tokens: the sequence is cut into chunks of this many tokens that are
+ * processed in parallel (the running state entering each chunk is an
+ * exclusive prefix sum of per-chunk states).  0 lets the library choose; a
+ * nonzero value must be a multiple of `block`.  The result does not depend on
+ * it beyond rounding.
+ *
+ * Workspace bytes needed by a prefill over `total_tokens` tokens in `nseq`
+ * sequences (a batch of B rows of N tokens is nseq = B, total = B*N).
+ * Returns 0 for unsupported arguments.
+ */
+LA_API size_t lightning_attn_prefill_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                             int head_dim, int block, int chunk_tokens,
+                                             la_dtype dtype);
+
+/*
+ * Causal prefill of `batch` independent rows of `seqlen` tokens.
+ *   q, k, v, gate, out: [batch][seqlen][heads][head_dim]
+ *   norm_weight:        [heads*head_dim]
+ *   initial_state:      [batch][heads][head_dim][head_dim] fp32, or NULL (zeros)
+ *   final_state:        same shape, or NULL (not written); may alias initial_state
+ *   eps:                RMSNorm epsilon (added to the mean of squares), >= 0
+ * seqlen may be 0 (nothing is written except final_state = initial_state).
+ */
+LA_API la_status lightning_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
+                                 const void* norm_weight, void* out, const float* initial_state,
+                                 float* final_state, int batch, int64_t seqlen, int heads,
+                                 int head_dim, int block, int chunk_tokens, float eps,
+                                 la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Causal prefill of `nseq` sequences packed back to back (varlen): sequence s
+ * owns tokens [cu_seqlens[s], cu_seqlens[s+1]) and starts from its own state
+ * (initial_state[s], or zeros); no token attends across a boundary.
+ *   q, k, v, gate, out: [total_tokens][heads][head_dim]
+ *   cu_seqlens:         device int32 [nseq+1]: cu[0] = 0, nondecreasing,
+ *                       cu[nseq] = total_tokens (empty sequences allowed)
+ *   initial_state / final_state: [nseq][heads][head_dim][head_dim] fp32 or NULL
+ */
+LA_API la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void* v,
+                                        const void* gate, const void* norm_weight, void* out,
+                                        const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+                                        const float* initial_state, float* final_state, int heads,
+                                        int head_dim, int block, int chunk_tokens, float eps,
+                                        la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* Workspace bytes needed by lightning_attn_decode. */
+LA_API size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim);
+
+/*
+ * One decode step: each of `nseq` sequences receives one token; its state is
+ * read, updated in place (S += k~^T v~) and used for y = q~ S (the new token
+ * included), then out = RMSNorm(y) * w * sigmoid(gate) over the heads*head_dim
+ * values of the token.
+ *   q, k, v, gate, out: [nseq][heads][head_dim]
+ *   state:              [nseq][heads][head_dim][head_dim] fp32, updated in place
+ */
+LA_API la_status lightning_attn_decode(const void* q, const void* k, const void* v, const void* gate,
+                                const void* norm_weight, void* out, float* state, int nseq,
+                                int heads, int head_dim, float eps, la_dtype dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_ATTN_H */

@@ -1,0 +1,233 @@
+// C ABI of the Lightning Attention library: host-side validation, workspace
+// layout and kernel dispatch.  See include/lightning_attn.h for the contract.
+#include "lightning_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "la_internal.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_block(int b) { return b == 16 || b == 32 || b == 64; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Chunk length when the caller leaves it to the library: aim for about
+// 1024 (chunk, head) work items so every one of the 256 CUs gets several,
+// while keeping chunks long (the per-chunk state is D*D*4 bytes per head).
+int auto_chunk(int64_t total, int nseq, int heads, int block) {
+    const int64_t target_items = 1024;
+    int64_t per = total * heads / target_items;
+    int64_t c = block;
+    while (c * 2 <= per && c < 8192) c *= 2;
+    (void)nseq;
+    return (int)c;
+}
+
+struct Layout {
+    int chunk = 0;
+    int max_chunks = 0;
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, bytes = 0;
+};
+
+// Workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks][states]
+bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
+                 Layout* L) {
+    if (total < 0 || nseq < 0 || heads < 1 || !supported_dim(head_dim) || !supported_block(block))
+        return false;
+    int chunk = chunk_tokens;
+    if (chunk == 0) chunk = auto_chunk(total, nseq, heads, block);
+    if (chunk < block || chunk % block != 0) return false;
+    const int64_t maxc = total / chunk + nseq;  // >= sum over sequences of ceil(L_s / chunk)
+    if (maxc > (int64_t)0x7fffffff / 2 || maxc * heads > (int64_t)0xffffffffLL) return false;
+    L->chunk = chunk;
+    L->max_chunks = (int)maxc;
+    size_t off = align_up(sizeof(la::PlanHeader));
+    L->off_segs = off;
+    off = align_up(off + sizeof(la::SegEntry) * (size_t)nseq);
+    L->off_chunks = off;
+    off = align_up(off + sizeof(la::ChunkEntry) * (size_t)maxc);
+    L->off_states = off;
+    off = align_up(off + sizeof(float) * (size_t)maxc * heads * head_dim * head_dim);
+    L->bytes = off;
+    return true;
+}
+
+la_status check_dtype(la_dtype dtype) {
+    return (dtype == LA_DTYPE_F32 || dtype == LA_DTYPE_BF16) ? LA_OK : LA_ERR_UNSUPPORTED;
+}
+
+la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    a.chunk = L.chunk;
+    a.max_chunks = L.max_chunks;
+    a.hdr = reinterpret_cast<la::PlanHeader*>(ws);
+    a.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
+    a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
+    a.states = reinterpret_cast<float*>(ws + L.off_states);
+    const bool mfma = la::mfma_supported(a);
+    hipError_t e = la::launch_plan(a, stream);
+    if (e == hipSuccess)
+        e = mfma ? la::launch_chunk_state_mfma(a, stream) : la::launch_chunk_state_valu(a, stream);
+    if (e == hipSuccess) e = la::launch_state_scan(a, stream);
+    if (e == hipSuccess) e = mfma ? la::launch_walk_mfma(a, stream) : la::launch_walk_valu(a, stream);
+    if (e == hipSuccess) e = la::launch_norm_gate(a, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status check_ptrs(const void* q, const void* k, const void* v, const void* g, const void* w,
+                     const void* out) {
+    if (!q || !k || !v || !g || !w || !out) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(w) ||
+        !aligned16(out))
+        return LA_ERR_MISALIGNED;
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lightning_attn_status_string(la_status s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case LA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
+        case LA_ERR_UNSUPPORTED: return "unsupported head_dim, block, chunk or dtype";
+        case LA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+        case LA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the required size";
+        case LA_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
+    }
+    return "unknown status";
+}
+
+size_t lightning_attn_prefill_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                             int head_dim, int block, int chunk_tokens,
+                                             la_dtype dtype) {
+    if (check_dtype(dtype) != LA_OK) return 0;
+    Layout L;
+    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, &L)) return 0;
+    return L.bytes;
+}
+
+la_status lightning_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
+                                 const void* norm_weight, void* out, const float* initial_state,
+                                 float* final_state, int batch, int64_t seqlen, int heads,
+                                 int head_dim, int block, int chunk_tokens, float eps,
+                                 la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    if (batch < 0 || seqlen < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
+    if (chunk_tokens < 0) return LA_ERR_BAD_SHAPE;
+    if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
+        return LA_ERR_UNSUPPORTED;
+    if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
+    const int64_t total = (int64_t)batch * seqlen;
+    if (total > 0) {
+        la_status s = check_ptrs(q, k, v, gate, norm_weight, out);
+        if (s != LA_OK) return s;
+    }
+    if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
+    if (final_state && !aligned16(final_state)) return LA_ERR_MISALIGNED;
+    Layout L;
+    if (!plan_layout(total, batch, heads, head_dim, block, chunk_tokens, &L))
+        return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (batch == 0) return LA_OK;
+    la::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = gate; a.w = norm_weight; a.out = out;
+    a.init_state = initial_state;
+    a.final_state = final_state;
+    a.cu = nullptr;
+    a.nseq = batch;
+    a.seqlen = seqlen;
+    a.total = total;
+    a.H = heads; a.D = head_dim; a.block = block;
+    a.eps = eps;
+    a.bf16 = dtype == LA_DTYPE_BF16;
+    return run_prefill(a, L, workspace, stream);
+}
+
+la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void* v,
+                                        const void* gate, const void* norm_weight, void* out,
+                                        const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+                                        const float* initial_state, float* final_state, int heads,
+                                        int head_dim, int block, int chunk_tokens, float eps,
+                                        la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    if (nseq < 0 || total_tokens < 0 || total_tokens > 0x7fffffffLL || heads < 1 ||
+        !(eps >= 0.0f) || chunk_tokens < 0)
+        return LA_ERR_BAD_SHAPE;
+    if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
+        return LA_ERR_UNSUPPORTED;
+    if (nseq == 0 && total_tokens != 0) return LA_ERR_BAD_SHAPE;
+    if (total_tokens > 0) {
+        la_status s = check_ptrs(q, k, v, gate, norm_weight, out);
+        if (s != LA_OK) return s;
+    }
+    if (nseq > 0 && !cu_seqlens) return LA_ERR_NULL_POINTER;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return LA_ERR_MISALIGNED;
+    if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
+    if (final_state && !aligned16(final_state)) return LA_ERR_MISALIGNED;
+    Layout L;
+    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, &L))
+        return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (nseq == 0) return LA_OK;
+    la::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = gate; a.w = norm_weight; a.out = out;
+    a.init_state = initial_state;
+    a.final_state = final_state;
+    a.cu = cu_seqlens;
+    a.nseq = nseq;
+    a.seqlen = 0;
+    a.total = total_tokens;
+    a.H = heads; a.D = head_dim; a.block = block;
+    a.eps = eps;
+    a.bf16 = dtype == LA_DTYPE_BF16;
+    return run_prefill(a, L, workspace, stream);
+}
+
+size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {
+    if (nseq < 0 || heads < 1 || !supported_dim(head_dim)) return 0;
+    return align_up(sizeof(float) * (size_t)nseq * heads * head_dim) +
+           align_up(sizeof(float) * (size_t)nseq * heads);
+}
+
+la_status lightning_attn_decode(const void* q, const void* k, const void* v, const void* gate,
+                                const void* norm_weight, void* out, float* state, int nseq,
+                                int heads, int head_dim, float eps, la_dtype dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (nseq < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
+    if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim)) return LA_ERR_UNSUPPORTED;
+    if ((int64_t)nseq * heads > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
+    if (nseq > 0) {
+        la_status s = check_ptrs(q, k, v, gate, norm_weight, out);
+        if (s != LA_OK) return s;
+        if (!state) return LA_ERR_NULL_POINTER;
+        if (!aligned16(state)) return LA_ERR_MISALIGNED;
+    }
+    const size_t need = lightning_attn_decode_workspace_size(nseq, heads, head_dim);
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < need) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (nseq == 0) return LA_OK;
+    la::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = gate; a.w = norm_weight; a.out = out;
+    a.state = state;
+    a.nseq = nseq; a.H = heads; a.D = head_dim;
+    a.eps = eps;
+    a.bf16 = dtype == LA_DTYPE_BF16;
+    a.ybuf = static_cast<float*>(workspace);
+    a.ssbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align_up(sizeof(float) * (size_t)nseq * heads * head_dim));
+    return la::launch_decode(a, stream) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

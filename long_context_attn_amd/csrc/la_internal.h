@@ -1,0 +1,93 @@
+// Internal declarations of the Lightning Attention library (device helpers,
+// workspace records and kernel launchers).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// ---------------------------------------------------------------- workspace
+// Chunk plan: every sequence is cut into chunks of at most `chunk` tokens;
+// chunks of one sequence are consecutive in the table.
+struct PlanHeader {
+    int32_t n_chunks;  // chunks in the table (0 if cu_seqlens was invalid)
+    int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow
+    int32_t pad[14];
+};
+struct SegEntry {
+    int32_t first;  // index of the sequence's first chunk
+    int32_t count;  // number of chunks (0 for an empty sequence)
+};
+struct ChunkEntry {
+    int64_t start;  // first token (packed index)
+    int32_t len;    // tokens in the chunk, 1..chunk
+    int32_t seg;    // owning sequence
+};
+
+// --------------------------------------------------------- element helpers
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+template <class TT> __device__ __forceinline__ TT from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// logistic function 1 / (1 + e^-x) from its definition, on the hardware
+// base-2 exponential and reciprocal (each ~1 ulp); saturates to 0 / 1.
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+// SiLU(x) = x * sigmoid(x)
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `st` and return hipGetLastError().
+struct PrefillArgs {
+    const void *q, *k, *v, *g, *w;
+    void* out;
+    const float* init_state;  // [nseq][H][D][D] or null
+    float* final_state;       // [nseq][H][D][D] or null
+    const int32_t* cu;        // device cu_seqlens or null (uniform rows)
+    int nseq;
+    int64_t seqlen;           // rows' length when cu == null
+    int64_t total;            // total tokens
+    int H, D, block, chunk;
+    float eps;
+    bool bf16;
+    int max_chunks;
+    PlanHeader* hdr;
+    SegEntry* segs;
+    ChunkEntry* chunks;
+    float* states;            // [max_chunks][H][D][D]
+};
+
+hipError_t launch_plan(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_state_scan(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_norm_gate(const PrefillArgs& a, hipStream_t st);
+// portable fp32 vector-ALU kernels (any supported shape)
+hipError_t launch_chunk_state_valu(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_walk_valu(const PrefillArgs& a, hipStream_t st);
+// bf16 MFMA kernels (D = 128, block = 64)
+bool mfma_supported(const PrefillArgs& a);
+hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_walk_mfma(const PrefillArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *w;
+    void* out;
+    float* state;
+    int nseq, H, D;
+    float eps;
+    bool bf16;
+    float* ybuf;   // [nseq][H*D]
+    float* ssbuf;  // [nseq][H]
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace la

@@ -1,0 +1,214 @@
+// Chunk plan, per-sequence state scan and the RMSNorm * sigmoid(gate)
+// epilogue of the Lightning Attention layer.
+//
+// The running state of Mechanism step 3 ("Diving into MiniMax01 405B MoE",
+// section "Hybrid Modeling") is a sum over past tokens, so a sequence can be
+// cut into chunks: the state entering chunk c is the exclusive prefix sum of
+// the per-chunk sums K~_c^T V~_c (plus the initial state).  The epilogue is
+// Mechanism step 4, RMSNorm over all heads*head_dim values of a token.
+#include "la_internal.h"
+
+namespace la {
+
+// ------------------------------------------------------------------- plan
+// One workgroup of 1024 threads: chunk counts per sequence, exclusive scan,
+// then each thread writes the chunk records of its sequences.
+constexpr int PLAN_THREADS = 1024;
+
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
+    const int32_t* __restrict__ cu, int nseq, int64_t seqlen, int64_t total, int chunk,
+    int max_chunks, PlanHeader* __restrict__ hdr, SegEntry* __restrict__ segs,
+    ChunkEntry* __restrict__ chunks) {
+    __shared__ int32_t scan[PLAN_THREADS];
+    __shared__ int32_t bad;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        bad = 0;
+        if (cu != nullptr && (cu[0] != 0 || (int64_t)cu[nseq] != total)) bad = 1;
+    }
+    __syncthreads();
+    int32_t carry = 0;
+    for (int base = 0; base < nseq; base += PLAN_THREADS) {
+        const int s = base + tid;
+        int64_t start = 0, len = 0;
+        if (s < nseq) {
+            if (cu != nullptr) {
+                start = cu[s];
+                len = (int64_t)cu[s + 1] - start;
+                if (len < 0) bad = 1;
+            } else {
+                start = (int64_t)s * seqlen;
+                len = seqlen;
+            }
+        }
+        const int32_t cnt = len > 0 ? (int32_t)((len + chunk - 1) / chunk) : 0;
+        scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < PLAN_THREADS; off <<= 1) {  // inclusive Hillis-Steele
+            const int32_t add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        const int32_t first = carry + scan[tid] - cnt;
+        if (s < nseq) {
+            segs[s].first = first;
+            segs[s].count = cnt;
+            if (first + cnt <= max_chunks) {
+                for (int32_t c = 0; c < cnt; ++c) {
+                    ChunkEntry e;
+                    e.start = start + (int64_t)c * chunk;
+                    const int64_t rem = len - (int64_t)c * chunk;
+                    e.len = (int32_t)(rem < chunk ? rem : chunk);
+                    e.seg = s;
+                    chunks[first + c] = e;
+                }
+            }
+        }
+        carry += scan[PLAN_THREADS - 1];
+        __syncthreads();
+    }
+    __shared__ int32_t err;
+    if (tid == 0) {
+        err = bad ? 1 : (carry > max_chunks ? 2 : 0);
+        hdr->error = err;
+        hdr->n_chunks = err ? 0 : carry;
+    }
+    __syncthreads();
+    // an invalid plan leaves no chunk to process and every sequence empty
+    if (err != 0)
+        for (int s = tid; s < nseq; s += PLAN_THREADS) segs[s].count = 0;
+}
+
+hipError_t launch_plan(const PrefillArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a.cu, a.nseq, a.seqlen,
+                       a.total, a.chunk, a.max_chunks, a.hdr, a.segs, a.chunks);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- state scan
+// One thread per 4 state entries of one (sequence, head): walks the
+// sequence's chunks in order, replacing each chunk sum by the state that
+// enters the chunk, and stores the state after the last chunk.
+constexpr int SCAN_THREADS = 256;
+
+__global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(
+    float* __restrict__ states, const SegEntry* __restrict__ segs, const float* init,
+    float* fin, int H, int DD, int tiles) {
+    const int pair = blockIdx.x / tiles;  // sequence * H + head
+    const int tile = blockIdx.x - pair * tiles;
+    const int e = (tile * SCAN_THREADS + threadIdx.x) * 4;
+    if (e >= DD) return;
+    const int s = pair / H, h = pair - s * H;
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    if (init != nullptr) run = *reinterpret_cast<const f32x4*>(init + (int64_t)pair * DD + e);
+    const SegEntry se = segs[s];
+    for (int c = se.first; c < se.first + se.count; ++c) {
+        f32x4* p = reinterpret_cast<f32x4*>(states + ((int64_t)c * H + h) * DD + e);
+        const f32x4 sum = *p;
+        *p = run;
+        run += sum;
+    }
+    if (fin != nullptr) *reinterpret_cast<f32x4*>(fin + (int64_t)pair * DD + e) = run;
+}
+
+hipError_t launch_state_scan(const PrefillArgs& a, hipStream_t st) {
+    const int DD = a.D * a.D;
+    const int tiles = (DD / 4 + SCAN_THREADS - 1) / SCAN_THREADS;
+    const int64_t grid = (int64_t)a.nseq * a.H * tiles;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(state_scan_kernel, dim3((unsigned)grid), dim3(SCAN_THREADS), 0, st,
+                       a.states, a.segs, a.init_state, a.final_state, a.H, DD, tiles);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ norm * gate epilogue
+// One workgroup per token.  `out` holds the raw attention output y of the
+// token on entry; it is overwritten with y * r * w * sigmoid(g), r =
+// 1/sqrt(mean(y^2) + eps) over the token's H*D values.
+constexpr int NORM_THREADS = 256;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NORM_THREADS / 64; ++i) tot += red[i];
+    return tot;
+}
+
+// any dtype and H*D: one element per thread per step, y re-read from `out`
+template <class TT>
+__global__ __launch_bounds__(NORM_THREADS) void norm_gate_kernel(
+    TT* __restrict__ out, const TT* __restrict__ g, const TT* __restrict__ w, int HD, float eps) {
+    __shared__ float red[NORM_THREADS / 64];
+    const int64_t base = (int64_t)blockIdx.x * HD;
+    TT* y = out + base;
+    const TT* gt = g + base;
+    float ss = 0.f;
+    for (int e = threadIdx.x; e < HD; e += NORM_THREADS) {
+        const float t = to_f32(y[e]);
+        ss += t * t;
+    }
+    const float r = 1.0f / __builtin_sqrtf(block_sum(ss, red) / (float)HD + eps);
+    for (int e = threadIdx.x; e < HD; e += NORM_THREADS)
+        y[e] = from_f32<TT>(to_f32(y[e]) * r * to_f32(w[e]) * sigmoid_f(to_f32(gt[e])));
+}
+
+// bf16 with H*D a multiple of 8 * NORM_THREADS and at most NV such vectors
+// per thread: y stays in registers between the reduction and the epilogue.
+template <int NV>
+__global__ __launch_bounds__(NORM_THREADS) void norm_gate_bf16_kernel(
+    __bf16* __restrict__ out, const __bf16* __restrict__ g, const __bf16* __restrict__ w, int HD,
+    float eps) {
+    __shared__ float red[NORM_THREADS / 64];
+    const int64_t base = (int64_t)blockIdx.x * HD;
+    bf16x8* y = reinterpret_cast<bf16x8*>(out + base);
+    const bf16x8* gt = reinterpret_cast<const bf16x8*>(g + base);
+    const bf16x8* wv = reinterpret_cast<const bf16x8*>(w);
+    const int nvec = HD / (8 * NORM_THREADS);
+    bf16x8 yv[NV], gv[NV];
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+        if (r < nvec) {
+            yv[r] = y[r * NORM_THREADS + threadIdx.x];
+            gv[r] = gt[r * NORM_THREADS + threadIdx.x];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ss += (float)yv[r][u] * (float)yv[r][u];
+        }
+    }
+    const float rr = 1.0f / __builtin_sqrtf(block_sum(ss, red) / (float)HD + eps);
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+        if (r < nvec) {
+            const bf16x8 ww = wv[r * NORM_THREADS + threadIdx.x];
+            bf16x8 o;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                o[u] = (__bf16)((float)yv[r][u] * rr * (float)ww[u] * sigmoid_f((float)gv[r][u]));
+            y[r * NORM_THREADS + threadIdx.x] = o;
+        }
+    }
+}
+
+hipError_t launch_norm_gate(const PrefillArgs& a, hipStream_t st) {
+    const int HD = a.H * a.D;
+    if (a.total == 0) return hipSuccess;
+    const dim3 grid((unsigned)a.total);
+    if (a.bf16 && HD % (8 * NORM_THREADS) == 0 && HD <= 4 * 8 * NORM_THREADS) {
+        hipLaunchKernelGGL((norm_gate_bf16_kernel<4>), grid, dim3(NORM_THREADS), 0, st,
+                           (__bf16*)a.out, (const __bf16*)a.g, (const __bf16*)a.w, HD, a.eps);
+    } else if (a.bf16) {
+        hipLaunchKernelGGL((norm_gate_kernel<__bf16>), grid, dim3(NORM_THREADS), 0, st,
+                           (__bf16*)a.out, (const __bf16*)a.g, (const __bf16*)a.w, HD, a.eps);
+    } else {
+        hipLaunchKernelGGL((norm_gate_kernel<float>), grid, dim3(NORM_THREADS), 0, st,
+                           (float*)a.out, (const float*)a.g, (const float*)a.w, HD, a.eps);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,220 @@
+"""Python binding of liblightning_attn.so (ctypes; argument marshalling only).
+
+Every step of the layer runs in the library's HIP kernels; torch is used for
+device memory and the current stream.  The calls mirror the C ABI declared in
+include/lightning_attn.h:
+
+    prefill(q, k, v, gate, weight, ...)            q: [B, N, H, D]
+    prefill_varlen(q, k, v, gate, weight, cu, ...) q: [T, H, D], cu: int32 [nseq+1]
+    decode(q, k, v, gate, weight, state, ...)      q: [S, H, D], state updated in place
+
+The layer is the Lightning Attention Mechanism of "Diving into MiniMax01 405B
+MoE" (section "Hybrid Modeling"): SiLU on q/k/v, causal Y = Q (K^T V) against
+a running fp32 state, then RMSNorm(Y) * sigmoid(gate).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblightning_attn.so")
+
+LA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+class LightningAttnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__("lightning_attn: %s (status %d)" % (text, status))
+        self.status = status
+
+
+def library():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("%s is missing: build it with `python -m long_context_attn_amd.build`"
+                               % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.lightning_attn_status_string.argtypes = [_I]
+        lib.lightning_attn_status_string.restype = ctypes.c_char_p
+        lib.lightning_attn_prefill_workspace_size.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        lib.lightning_attn_prefill_workspace_size.restype = _SZ
+        lib.lightning_attn_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I, _I,
+                                               _I, _I, _F, _I, _P, _SZ, _P]
+        lib.lightning_attn_prefill.restype = _I
+        lib.lightning_attn_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _P,
+                                                      _P, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]
+        lib.lightning_attn_prefill_varlen.restype = _I
+        lib.lightning_attn_decode_workspace_size.argtypes = [_I, _I, _I]
+        lib.lightning_attn_decode_workspace_size.restype = _SZ
+        lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
+                                              _SZ, _P]
+        lib.lightning_attn_decode.restype = _I
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().lightning_attn_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise LightningAttnError(status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in LA_DTYPE:
+        raise TypeError("lightning_attn supports float32 and bfloat16 activations, got %s" % t.dtype)
+    return LA_DTYPE[t.dtype]
+
+
+def _same(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise TypeError("all activations and the norm weight must share dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _state(t, shape, device, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s"
+                         % (name, tuple(shape), device))
+    return t
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def prefill_workspace_size(total_tokens, nseq, heads, head_dim, block=64, chunk_tokens=0,
+                           dtype=torch.bfloat16) -> int:
+    return int(library().lightning_attn_prefill_workspace_size(
+        int(total_tokens), int(nseq), int(heads), int(head_dim), int(block), int(chunk_tokens),
+        LA_DTYPE[dtype]))
+
+
+def decode_workspace_size(nseq, heads, head_dim) -> int:
+    return int(library().lightning_attn_decode_workspace_size(int(nseq), int(heads), int(head_dim)))
+
+
+def _workspace(nbytes, device, given):
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
+        return given
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def prefill(q, k, v, gate, weight, *, block=64, eps=1e-6, initial_state=None,
+            return_final_state=False, chunk_tokens=0, out=None, final_state=None,
+            workspace=None):
+    """Causal Lightning Attention prefill of B rows of N tokens.
+
+    q, k, v, gate: [B, N, H, D] (float32 or bfloat16, contiguous, one device);
+    weight: [H*D]; initial_state: [B, H, D, D] float32 or None (zeros).
+    Returns out [B, N, H, D] (and the final state [B, H, D, D] if requested).
+    """
+    _same(q, k, v, gate, weight)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or gate.shape != q.shape:
+        raise ValueError("q, k, v, gate must share one [B, N, H, D] shape")
+    B, N, H, D = q.shape
+    if weight.numel() != H * D:
+        raise ValueError("weight must have H*D elements")
+    dev = q.device
+    init = _state(initial_state, (B, H, D, D), dev, "initial_state")
+    if out is None:
+        out = torch.empty_like(q)
+    fs = None
+    if return_final_state:
+        fs = final_state if final_state is not None else torch.empty(B, H, D, D, dtype=torch.float32,
+                                                                    device=dev)
+        _state(fs, (B, H, D, D), dev, "final_state")
+    ws_bytes = prefill_workspace_size(B * N, B, H, D, block, chunk_tokens, q.dtype)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(init), _ptr(fs),
+        B, N, H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes,
+        _stream(dev)))
+    return (out, fs) if return_final_state else out
+
+
+def prefill_varlen(q, k, v, gate, weight, cu_seqlens, *, block=64, eps=1e-6, initial_state=None,
+                   return_final_state=False, chunk_tokens=0, out=None, final_state=None,
+                   workspace=None):
+    """Causal prefill of sequences packed back to back.
+
+    q, k, v, gate: [T, H, D]; cu_seqlens: int32 [nseq+1] on the same device
+    (0 = cu[0] <= ... <= cu[nseq] = T); initial_state: [nseq, H, D, D] or None.
+    """
+    _same(q, k, v, gate, weight)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or gate.shape != q.shape:
+        raise ValueError("q, k, v, gate must share one [T, H, D] shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector on the activations' device")
+    T, H, D = q.shape
+    nseq = cu_seqlens.numel() - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if weight.numel() != H * D:
+        raise ValueError("weight must have H*D elements")
+    dev = q.device
+    init = _state(initial_state, (nseq, H, D, D), dev, "initial_state")
+    if out is None:
+        out = torch.empty_like(q)
+    fs = None
+    if return_final_state:
+        fs = final_state if final_state is not None else torch.empty(nseq, H, D, D,
+                                                                    dtype=torch.float32, device=dev)
+        _state(fs, (nseq, H, D, D), dev, "final_state")
+    ws_bytes = prefill_workspace_size(T, nseq, H, D, block, chunk_tokens, q.dtype)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(cu_seqlens), nseq,
+        T, _ptr(init), _ptr(fs), H, D, int(block), int(chunk_tokens), float(eps), _dtype(q),
+        _ptr(ws), ws_bytes, _stream(dev)))
+    return (out, fs) if return_final_state else out
+
+
+def decode(q, k, v, gate, weight, state, *, eps=1e-6, out=None, workspace=None):
+    """One decode step for S sequences; `state` [S, H, D, D] fp32 is updated in place."""
+    _same(q, k, v, gate, weight)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or gate.shape != q.shape:
+        raise ValueError("q, k, v, gate must share one [S, H, D] shape")
+    S, H, D = q.shape
+    if weight.numel() != H * D:
+        raise ValueError("weight must have H*D elements")
+    dev = q.device
+    _state(state, (S, H, D, D), dev, "state")
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = decode_workspace_size(S, H, D)
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(state), S, H, D,
+        float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    return out

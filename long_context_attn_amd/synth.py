@@ -35,9 +35,10 @@ TINY_FP32, PREFILL_8K, DECODE, VARLEN_1M, PREFILL_1M = 1, 2, 3, 4, 5
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    # finite values never wrap in uint32: the largest finite pattern plus 0x8000 stays below 2^32
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def stream(key, n: int) -> np.ndarray:

@@ -1,0 +1,148 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+include/lightning_attn.h declares, and rejects bad arguments on the host
+before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_attn_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning_attn.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, WS, HIPERR = range(7)
+F32, BF16 = 0, 1
+A = 0x10000  # a fake 16-byte aligned "device" address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from long_context_attn_amd import build
+        build.build()
+    return ops.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LA_API\s+[\w\s\*]+?\b(lightning_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("lightning_attn_prefill", "lightning_attn_prefill_varlen", "lightning_attn_decode"):
+        assert n in names
+    assert len(names) == 6
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    # nothing else leaks out of the library under the API's prefix
+    assert {e for e in exported if e.startswith("lightning_attn")} == set(declared_functions())
+
+
+def test_status_strings(lib):
+    assert ops.status_string(0) == "ok"
+    for s in range(1, 7):
+        assert len(ops.status_string(s)) > 10
+    assert ops.status_string(99) == "unknown status"
+
+
+def test_prefill_workspace_size(lib):
+    ws = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024)
+    # 8 chunks of 1024 tokens (+ one spare per sequence) x 64 heads x 128 x 128 fp32
+    assert ws >= 9 * 64 * 128 * 128 * 4
+    assert ws < 9 * 64 * 128 * 128 * 4 + 65536
+    assert ops.prefill_workspace_size(8192, 1, 64, 96, 64, 0) == 0      # head_dim
+    assert ops.prefill_workspace_size(8192, 1, 64, 128, 48, 0) == 0     # block
+    assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, 100) == 0   # chunk % block
+    assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, 32) == 0    # chunk < block
+    assert ops.prefill_workspace_size(0, 0, 64, 128, 64, 0) > 0
+    # varlen: one extra chunk per sequence at most
+    assert ops.prefill_workspace_size(1000, 3, 2, 64, 32, 64) >= (1000 // 64 + 3) * 2 * 64 * 64 * 4
+    assert ops.decode_workspace_size(256, 64, 128) >= 256 * 64 * 128 * 4 + 256 * 64 * 4
+
+
+def _prefill(lib, q=A, k=A, v=A, g=A, w=A, out=A, init=None, fin=None, batch=1, seqlen=128,
+             heads=2, d=64, block=32, chunk=0, eps=1e-6, dtype=F32, ws=A, ws_bytes=1 << 40):
+    return lib.lightning_attn_prefill(q, k, v, g, w, out, init, fin, batch, seqlen, heads, d,
+                                      block, chunk, eps, dtype, ws, ws_bytes, None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, q=None) == NULLP
+    assert _prefill(lib, out=None) == NULLP
+    assert _prefill(lib, ws=None) == NULLP
+    assert _prefill(lib, k=A + 8) == MISAL
+    assert _prefill(lib, init=A + 4) == MISAL
+    assert _prefill(lib, fin=A + 4) == MISAL
+    assert _prefill(lib, ws=A + 8) == MISAL
+    assert _prefill(lib, d=96) == UNSUP
+    assert _prefill(lib, block=48) == UNSUP
+    assert _prefill(lib, chunk=48) == UNSUP
+    assert _prefill(lib, dtype=7) == UNSUP
+    assert _prefill(lib, batch=-1) == SHAPE
+    assert _prefill(lib, seqlen=-5) == SHAPE
+    assert _prefill(lib, heads=0) == SHAPE
+    assert _prefill(lib, eps=-1.0) == SHAPE
+    assert _prefill(lib, eps=float("nan")) == SHAPE
+    assert _prefill(lib, chunk=-64) == SHAPE
+    assert _prefill(lib, ws_bytes=100) == WS
+    # empty batch: valid, nothing to enqueue
+    assert _prefill(lib, batch=0, q=None, k=None, v=None, g=None, w=None, out=None) == OK
+
+
+def test_varlen_validation(lib):
+    def call(q=A, cu=A, nseq=2, total=100, d=64, block=32, ws=A, ws_bytes=1 << 40, eps=1e-6):
+        return lib.lightning_attn_prefill_varlen(q, A, A, A, A, A, cu, nseq, total, None, None, 2,
+                                                 d, block, 0, eps, F32, ws, ws_bytes, None)
+    assert call(q=None) == NULLP
+    assert call(cu=None) == NULLP
+    assert call(cu=A + 2) == MISAL
+    assert call(nseq=-1) == SHAPE
+    assert call(total=-1) == SHAPE
+    assert call(total=1 << 31) == SHAPE
+    assert call(nseq=0, total=10) == SHAPE
+    assert call(d=48) == UNSUP
+    assert call(ws_bytes=64) == WS
+    assert call(nseq=0, total=0, q=None, cu=None) == OK
+
+
+def test_decode_validation(lib):
+    def call(q=A, state=A, nseq=4, heads=2, d=64, ws=A, ws_bytes=1 << 30, dtype=BF16):
+        return lib.lightning_attn_decode(q, A, A, A, A, A, state, nseq, heads, d, 1e-6, dtype, ws,
+                                         ws_bytes, None)
+    assert call(q=None) == NULLP
+    assert call(state=None) == NULLP
+    assert call(state=A + 4) == MISAL
+    assert call(ws=None) == NULLP
+    assert call(nseq=-1) == SHAPE
+    assert call(heads=0) == SHAPE
+    assert call(d=100) == UNSUP
+    assert call(dtype=5) == UNSUP
+    assert call(ws_bytes=16) == WS
+    assert call(nseq=0, q=None, state=None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.library()
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "long_context_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("CPU oracle", ""), os.path.join(dirpath, f)
