@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lightning Attention layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+
+Prints ONE JSON line.  A step is one call of the library's prefill on the
+MiniMax-shaped workload: batch 1, 8192 tokens, 64 heads x head_dim 128
+(attention width 8192), block 64, bf16 inputs with q/k/v ~ N(0,1)/sqrt(128),
+gate ~ N(0,1), norm weight ~ N(1, 0.02), eps 1e-6 -- the whole layer: SiLU on
+q/k/v, causal Y = Q(K^T V) against the running fp32 state, RMSNorm(Y) *
+sigmoid(gate).  Inputs are synthetic (seeded), resident in HBM before timing.
+
+value = prefill tokens/s.  Also reported: TFLOP/s on the block-tiled FLOP
+count, the per-kernel split (HIP events recorded between the library's
+kernels on the stream they run on), the roofline of the dominant kernel, the
+decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
+as state GB/s, and the CPU oracle timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + TFLOP/s (64h×d128, bf16) and decode state GB/s, 1×MI355X"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+PREFILL_8K = dict(workload="prefill_8k_64h_d128_bf16", batch=1, seqlen=8192, heads=64,
+                  head_dim=128, block=64, eps=1e-6, dist="minimax")
+DECODE_256 = dict(workload="decode_256seq_64h_d128_fp32state", nseq=256, heads=64, head_dim=128,
+                  steps=64, prefix_lo=1024, prefix_hi=32768, eps=1e-6, dist="unit")
+# parity-only workloads (tests/test_gpu_workloads.py), listed for reference
+PREFILL_1M = dict(workload="prefill_1m_64h_d128_bf16", batch=1, seqlen=1 << 20, heads=64,
+                  head_dim=128, block=64)
+VARLEN_1M = dict(workload="varlen_1m_64h_d128_bf16", total=1 << 20, heads=64, head_dim=128,
+                 block=64)
+
+
+def layer_bytes_per_token(H, D, elem=2):
+    """Algorithmic HBM bytes of the layer per token: read q, k, v, gate; write out."""
+    return 5 * H * D * elem
+
+
+def walk_bytes_per_token(H, D, elem=2):
+    """Algorithmic bytes of the chunk-walk kernel per token: read q, k, v; write y."""
+    return 4 * H * D * elem
+
+
+def flops_per_token(H, D, block):
+    """Block-tiled FLOPs per token: 4 H D^2 (state update + q S) plus the causal
+    half of the intra-block product, H (block + 1) 2 D."""
+    return 4 * H * D * D + H * (block + 1) * 2 * D
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls needed for raw events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, arr):
+        for e in arr:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def stage_names(lib, prefix):
+    cnt = getattr(lib, "lightning_attn_%s_stage_count" % prefix)()
+    f = getattr(lib, "lightning_attn_%s_stage_name" % prefix)
+    f.restype = ctypes.c_char_p
+    return [f(i).decode() for i in range(cnt)]
+
+
+def source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_attn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    ent = doc.get("%s@%s" % (kernel, workload))
+    if not ent or ent.get("source_sha") != source_sha():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def bench_prefill(args, la, torch, hip):
+    from long_context_attn_amd import synth
+    cfg = PREFILL_8K
+    B, N, H, D, blk = cfg["batch"], cfg["seqlen"], cfg["heads"], cfg["head_dim"], cfg["block"]
+    t0 = time.time()
+    q, k, v, g, w = synth.layer_inputs(synth.PREFILL_8K, B * N, H, D, cfg["dist"], threads=16)
+    log("generated prefill inputs in %.1fs" % (time.time() - t0))
+    dev = "cuda"
+    dt = torch.bfloat16
+    to = lambda a, shape: torch.from_numpy(a).to(dev).to(dt).view(*shape).contiguous()
+    qd, kd, vd, gd = (to(a, (B, N, H, D)) for a in (q, k, v, g))
+    wd = to(w, (H * D,))
+    out = torch.empty_like(qd)
+    ws_bytes = la.prefill_workspace_size(B * N, B, H, D, blk, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    call = lambda: la.prefill(qd, kd, vd, gd, wd, block=blk, eps=cfg["eps"], out=out, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel split with HIP events between the library's kernels
+    lib = la.library()
+    names = stage_names(lib, "prefill")
+    nst = len(names)
+    f = lib.lightning_attn_prefill_profiled
+    P = ctypes.c_void_p
+    f.argtypes = [P] * 8 + [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                            ctypes.c_int, ctypes.c_float, ctypes.c_int, P, ctypes.c_size_t, P, P,
+                            ctypes.c_int]
+    f.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [hip.events(nst + 1) for _ in range(args.steps)]
+    for i in range(args.steps):
+        st = f(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), gd.data_ptr(), wd.data_ptr(),
+               out.data_ptr(), None, None, B, N, H, D, blk, 0, cfg["eps"], 1, ws.data_ptr(),
+               ws_bytes, stream, evs[i], nst + 1)
+        assert st == 0, st
+    torch.cuda.synchronize()
+    per = {n: 0.0 for n in names}
+    for i in range(args.steps):
+        for j, n in enumerate(names):
+            per[n] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / args.steps
+    for e in evs:
+        hip.destroy(e)
+    tokens = B * N
+    tok_s = tokens / (ms * 1e-3)
+    fl = flops_per_token(H, D, blk) * tokens
+    walk_us = per["walk"] * 1e3
+    walk_bytes = walk_bytes_per_token(H, D) * tokens
+    achieved = walk_bytes / (walk_us * 1e-6) / 1e9
+    traffic = measured_traffic("walk_mfma_kernel", cfg["workload"])
+    res = dict(
+        ms_per_step=ms, tokens_per_s=tok_s, tflops=fl / (ms * 1e-3) / 1e12,
+        layer_hbm_frac=layer_bytes_per_token(H, D) * tokens / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        kernels_us={n: round(per[n] * 1e3, 2) for n in names},
+        roofline=dict(kernel="walk_mfma_kernel", bound="hbm", achieved=round(achieved, 1),
+                      peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=traffic, algorithmic_bytes_per_launch=walk_bytes,
+                      avg_launch_us=round(walk_us, 2)),
+        inputs=(q, k, v, g, w))
+    log("prefill: %.1f us/step, %.2f M tok/s, %.1f TFLOP/s, kernels %s" %
+        (ms * 1e3, tok_s / 1e6, res["tflops"], res["kernels_us"]))
+    del qd, kd, vd, gd, out, ws
+    return res
+
+
+def bench_decode(args, la, torch, hip):
+    from long_context_attn_amd import synth
+    cfg = DECODE_256
+    S, H, D = cfg["nseq"], cfg["heads"], cfg["head_dim"]
+    dev = "cuda"
+    dt = torch.bfloat16
+    # initial state of every sequence = K~^T V~ of a seeded prefill whose length is
+    # uniform in [1024, 32768]; built here with the library's own varlen prefill
+    lens = synth.decode_prefix_lengths(S, cfg["prefix_lo"], cfg["prefix_hi"])
+    state = torch.empty(S, H, D, D, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    t0 = time.time()
+    group = 8
+    w = torch.ones(H * D, dtype=dt, device=dev)
+    for s0 in range(0, S, group):
+        gl = lens[s0:s0 + group]
+        T = sum(gl)
+        gen.manual_seed(2025 * 1000 + s0)
+        kk = torch.randn(T, H, D, device=dev, dtype=torch.float32, generator=gen).to(dt)
+        vv = torch.randn(T, H, D, device=dev, dtype=torch.float32, generator=gen).to(dt)
+        cu = torch.tensor([0] + list(torch.tensor(gl).cumsum(0).tolist()), dtype=torch.int32,
+                          device=dev)
+        _, fs = la.prefill_varlen(kk, kk, vv, kk, w, cu, return_final_state=True,
+                                  final_state=state[s0:s0 + len(gl)])
+        del kk, vv
+    torch.cuda.synchronize()
+    log("decode initial states (%d prefill tokens) built in %.1fs" % (sum(lens), time.time() - t0))
+    steps = cfg["steps"]
+    gen.manual_seed(2025 * 1000 + 999)
+    inp = [torch.randn(4, S, H, D, device=dev, dtype=torch.float32, generator=gen).to(dt)
+           for _ in range(steps)]
+    wd = torch.ones(H * D, dtype=dt, device=dev)
+    out = torch.empty(S, H, D, dtype=dt, device=dev)
+    ws = torch.empty(la.decode_workspace_size(S, H, D), dtype=torch.uint8, device=dev)
+    step = lambda x: la.decode(x[0], x[1], x[2], x[3], wd, state, eps=cfg["eps"], out=out,
+                               workspace=ws)
+    for i in range(3):
+        step(inp[i])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(inp[i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # per-kernel split
+    lib = la.library()
+    names = stage_names(lib, "decode")
+    f = lib.lightning_attn_decode_profiled
+    P = ctypes.c_void_p
+    f.argtypes = [P] * 7 + [ctypes.c_int] * 3 + [ctypes.c_float, ctypes.c_int, P, ctypes.c_size_t,
+                                                 P, P, ctypes.c_int]
+    f.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+    nprof = 16
+    evs = [hip.events(len(names) + 1) for _ in range(nprof)]
+    for i in range(nprof):
+        x = inp[i]
+        st = f(x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(), x[3].data_ptr(), wd.data_ptr(),
+               out.data_ptr(), state.data_ptr(), S, H, D, cfg["eps"], 1, ws.data_ptr(),
+               ws.numel(), stream, evs[i], len(names) + 1)
+        assert st == 0, st
+    torch.cuda.synchronize()
+    per = {n: 0.0 for n in names}
+    for i in range(nprof):
+        for j, n in enumerate(names):
+            per[n] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / nprof
+    for e in evs:
+        hip.destroy(e)
+    state_bytes = 2 * S * H * D * D * 4  # read + write of the fp32 state
+    k_us = per["decode_state"] * 1e3
+    res = dict(workload=cfg["workload"], steps=steps, ms_per_step=round(ms, 4),
+               tokens_per_s=round(S / (ms * 1e-3), 1),
+               state_GBps=round(state_bytes / (ms * 1e-3) / 1e9, 1),
+               state_hbm_frac=round(state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               kernels_us={n: round(per[n] * 1e3, 2) for n in names},
+               state_kernel_GBps=round(state_bytes / (k_us * 1e-6) / 1e9, 1),
+               initial_state="K~^T V~ of a prefill of length U{1024..32768} per sequence, "
+                             "N(0,1) k/v (torch generator), built with the library's varlen prefill")
+    log("decode: %.1f us/step, state %.0f GB/s (%.1f%% of HBM peak), kernels %s" %
+        (ms * 1e3, res["state_GBps"], 100 * res["state_hbm_frac"], res["kernels_us"]))
+    del state, inp, out, ws
+    return res
+
+
+def cpu_baseline(inputs, budget_s):
+    """The CPU oracle (fp64, OpenMP over heads) on the same 8192-token workload,
+    repeated until about `budget_s` seconds of host work."""
+    import oracle
+    q, k, v, g, w = inputs
+    cores = oracle.max_threads()
+    passes, t_total = 0, 0.0
+    while passes == 0 or (t_total < budget_s and passes < 10):
+        t0 = time.time()
+        oracle.prefill(q, k, v, g, w, eps=PREFILL_8K["eps"])
+        t_total += time.time() - t0
+        passes += 1
+    T = q.shape[0]
+    return dict(value=round(T * passes / t_total, 1), unit="tokens/s", cores=cores, kind="oracle",
+                sample="the full 8192-token x 64-head prefill workload, %d pass(es), %.1f s"
+                       % (passes, t_total))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the layer's multi-GPU sharding is a design "
+              "(see the package documentation), not a path this build runs; use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_attn_amd as la
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    la.library()  # fail loudly if the HIP library is missing
+    hip = Hip()
+    pre = bench_prefill(args, la, torch, hip)
+    dec = None if args.no_decode else bench_decode(args, la, torch, hip)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(pre["inputs"], args.cpu_seconds)
+        log("cpu oracle: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+    c = PREFILL_8K
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c["workload"], "batch": c["batch"], "seq_len": c["seqlen"],
+                   "heads": c["heads"], "head_dim": c["head_dim"], "block": c["block"],
+                   "inputs": "q,k,v ~ N(0,1)/sqrt(128), gate ~ N(0,1), w ~ N(1,0.02), bf16"},
+        "tflops": round(pre["tflops"], 2),
+        "mfma_frac": round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "layer_hbm_frac": round(pre["layer_hbm_frac"], 4),
+        "kernels_us": pre["kernels_us"],
+        "roofline": pre["roofline"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -127,6 +127,33 @@ LA_API la_status lightning_attn_decode(const void* q, const void* k, const void*
                                 int heads, int head_dim, float eps, la_dtype dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Instrumented variants, for attributing time to the kernels of one call.
+ * They behave exactly like lightning_attn_prefill / lightning_attn_decode and
+ * additionally record events[0] on `stream` before the first kernel and
+ * events[i] after the i-th kernel; the kernels of a call are named by
+ * lightning_attn_prefill_stage_name / lightning_attn_decode_stage_name.
+ * events: caller-created hipEvent_t handles, n_events >= stage count + 1
+ * (LA_ERR_BAD_SHAPE otherwise; NULL events with n_events = 0 records none).
+ */
+LA_API int lightning_attn_prefill_stage_count(void);
+LA_API const char* lightning_attn_prefill_stage_name(int stage); /* NULL if out of range */
+LA_API int lightning_attn_decode_stage_count(void);
+LA_API const char* lightning_attn_decode_stage_name(int stage);  /* NULL if out of range */
+
+LA_API la_status lightning_attn_prefill_profiled(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    void* out, const float* initial_state, float* final_state, int batch, int64_t seqlen,
+    int heads, int head_dim, int block, int chunk_tokens, float eps, la_dtype dtype,
+    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+    int n_events);
+
+LA_API la_status lightning_attn_decode_profiled(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    void* out, float* state, int nseq, int heads, int head_dim, float eps, la_dtype dtype,
+    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+    int n_events);
+
 #ifdef __cplusplus
 }
 #endif

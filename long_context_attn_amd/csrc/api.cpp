@@ -60,7 +60,24 @@ la_status check_dtype(la_dtype dtype) {
     return (dtype == LA_DTYPE_F32 || dtype == LA_DTYPE_BF16) ? LA_OK : LA_ERR_UNSUPPORTED;
 }
 
-la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipStream_t stream) {
+const char* const kPrefillStages[] = {"plan", "chunk_state", "state_scan", "walk", "norm_gate"};
+constexpr int kPrefillStageCount = 5;
+const char* const kDecodeStages[] = {"decode_state", "decode_norm"};
+constexpr int kDecodeStageCount = 2;
+
+// Records events[i] (if any) on the stream; returns false on a HIP error.
+struct Marks {
+    hipEvent_t* ev = nullptr;
+    int n = 0;
+    int next = 0;
+    hipError_t mark(hipStream_t st) {
+        if (ev == nullptr) return hipSuccess;
+        return hipEventRecord(ev[next++], st);
+    }
+};
+
+la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipStream_t stream,
+                      Marks marks = Marks()) {
     char* ws = static_cast<char*>(workspace);
     a.chunk = L.chunk;
     a.max_chunks = L.max_chunks;
@@ -69,12 +86,18 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
     a.states = reinterpret_cast<float*>(ws + L.off_states);
     const bool mfma = la::mfma_supported(a);
-    hipError_t e = la::launch_plan(a, stream);
+    hipError_t e = marks.mark(stream);
+    if (e == hipSuccess) e = la::launch_plan(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
     if (e == hipSuccess)
         e = mfma ? la::launch_chunk_state_mfma(a, stream) : la::launch_chunk_state_valu(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
     if (e == hipSuccess) e = la::launch_state_scan(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
     if (e == hipSuccess) e = mfma ? la::launch_walk_mfma(a, stream) : la::launch_walk_valu(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
     if (e == hipSuccess) e = la::launch_norm_gate(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
@@ -113,12 +136,12 @@ size_t lightning_attn_prefill_workspace_size(int64_t total_tokens, int nseq, int
     return L.bytes;
 }
 
-la_status lightning_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
-                                 const void* norm_weight, void* out, const float* initial_state,
-                                 float* final_state, int batch, int64_t seqlen, int heads,
-                                 int head_dim, int block, int chunk_tokens, float eps,
-                                 la_dtype dtype, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
+static la_status prefill_impl(const void* q, const void* k, const void* v, const void* gate,
+                              const void* norm_weight, void* out, const float* initial_state,
+                              float* final_state, int batch, int64_t seqlen, int heads,
+                              int head_dim, int block, int chunk_tokens, float eps,
+                              la_dtype dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, Marks marks) {
     if (batch < 0 || seqlen < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
     if (chunk_tokens < 0) return LA_ERR_BAD_SHAPE;
     if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
@@ -149,7 +172,45 @@ la_status lightning_attn_prefill(const void* q, const void* k, const void* v, co
     a.H = heads; a.D = head_dim; a.block = block;
     a.eps = eps;
     a.bf16 = dtype == LA_DTYPE_BF16;
-    return run_prefill(a, L, workspace, stream);
+    return run_prefill(a, L, workspace, stream, marks);
+}
+
+la_status lightning_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
+                                 const void* norm_weight, void* out, const float* initial_state,
+                                 float* final_state, int batch, int64_t seqlen, int heads,
+                                 int head_dim, int block, int chunk_tokens, float eps,
+                                 la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    return prefill_impl(q, k, v, gate, norm_weight, out, initial_state, final_state, batch, seqlen,
+                        heads, head_dim, block, chunk_tokens, eps, dtype, workspace,
+                        workspace_bytes, stream, Marks());
+}
+
+la_status lightning_attn_prefill_profiled(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    void* out, const float* initial_state, float* final_state, int batch, int64_t seqlen,
+    int heads, int head_dim, int block, int chunk_tokens, float eps, la_dtype dtype,
+    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+    int n_events) {
+    Marks m;
+    if (n_events != 0) {
+        if (events == nullptr) return LA_ERR_NULL_POINTER;
+        if (n_events < kPrefillStageCount + 1) return LA_ERR_BAD_SHAPE;
+        m.ev = events;
+        m.n = n_events;
+    }
+    return prefill_impl(q, k, v, gate, norm_weight, out, initial_state, final_state, batch, seqlen,
+                        heads, head_dim, block, chunk_tokens, eps, dtype, workspace,
+                        workspace_bytes, stream, m);
+}
+
+int lightning_attn_prefill_stage_count(void) { return kPrefillStageCount; }
+const char* lightning_attn_prefill_stage_name(int stage) {
+    return (stage >= 0 && stage < kPrefillStageCount) ? kPrefillStages[stage] : nullptr;
+}
+int lightning_attn_decode_stage_count(void) { return kDecodeStageCount; }
+const char* lightning_attn_decode_stage_name(int stage) {
+    return (stage >= 0 && stage < kDecodeStageCount) ? kDecodeStages[stage] : nullptr;
 }
 
 la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void* v,
@@ -200,10 +261,10 @@ size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {
            align_up(sizeof(float) * (size_t)nseq * heads);
 }
 
-la_status lightning_attn_decode(const void* q, const void* k, const void* v, const void* gate,
-                                const void* norm_weight, void* out, float* state, int nseq,
-                                int heads, int head_dim, float eps, la_dtype dtype,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static la_status decode_impl(const void* q, const void* k, const void* v, const void* gate,
+                             const void* norm_weight, void* out, float* state, int nseq, int heads,
+                             int head_dim, float eps, la_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, Marks marks) {
     if (nseq < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
     if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim)) return LA_ERR_UNSUPPORTED;
     if ((int64_t)nseq * heads > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
@@ -227,7 +288,36 @@ la_status lightning_attn_decode(const void* q, const void* k, const void* v, con
     a.ybuf = static_cast<float*>(workspace);
     a.ssbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align_up(sizeof(float) * (size_t)nseq * heads * head_dim));
-    return la::launch_decode(a, stream) == hipSuccess ? LA_OK : LA_ERR_HIP;
+    hipError_t e = marks.mark(stream);
+    if (e == hipSuccess) e = la::launch_decode_state(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
+    if (e == hipSuccess) e = la::launch_decode_norm(a, stream);
+    if (e == hipSuccess) e = marks.mark(stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status lightning_attn_decode(const void* q, const void* k, const void* v, const void* gate,
+                                const void* norm_weight, void* out, float* state, int nseq,
+                                int heads, int head_dim, float eps, la_dtype dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(q, k, v, gate, norm_weight, out, state, nseq, heads, head_dim, eps, dtype,
+                       workspace, workspace_bytes, stream, Marks());
+}
+
+la_status lightning_attn_decode_profiled(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    void* out, float* state, int nseq, int heads, int head_dim, float eps, la_dtype dtype,
+    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+    int n_events) {
+    Marks m;
+    if (n_events != 0) {
+        if (events == nullptr) return LA_ERR_NULL_POINTER;
+        if (n_events < kDecodeStageCount + 1) return LA_ERR_BAD_SHAPE;
+        m.ev = events;
+        m.n = n_events;
+    }
+    return decode_impl(q, k, v, gate, norm_weight, out, state, nseq, heads, head_dim, eps, dtype,
+                       workspace, workspace_bytes, stream, m);
 }
 
 }  // extern "C"

@@ -97,33 +97,41 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_norm_kernel(
 }
 
 template <class TT, int D>
-static hipError_t decode_d(const DecodeArgs& a, hipStream_t st) {
+static hipError_t decode_state_d(const DecodeArgs& a, hipStream_t st) {
     const int64_t pairs = (int64_t)a.nseq * a.H;
     hipLaunchKernelGGL((decode_state_kernel<TT, D>), dim3((unsigned)pairs), dim3(DEC_THREADS), 0,
                        st, (const TT*)a.q, (const TT*)a.k, (const TT*)a.v, a.state, a.ybuf,
                        a.ssbuf);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_norm_kernel<TT>), dim3((unsigned)a.nseq), dim3(DEC_THREADS), 0, st,
-                       (const TT*)a.g, (const TT*)a.w, (TT*)a.out, a.ybuf, a.ssbuf, a.H,
-                       a.H * a.D, a.eps);
     return hipGetLastError();
 }
 
 template <class TT>
-static hipError_t decode_t(const DecodeArgs& a, hipStream_t st) {
+static hipError_t decode_state_t(const DecodeArgs& a, hipStream_t st) {
     switch (a.D) {
-        case 16: return decode_d<TT, 16>(a, st);
-        case 32: return decode_d<TT, 32>(a, st);
-        case 64: return decode_d<TT, 64>(a, st);
-        case 128: return decode_d<TT, 128>(a, st);
+        case 16: return decode_state_d<TT, 16>(a, st);
+        case 32: return decode_state_d<TT, 32>(a, st);
+        case 64: return decode_state_d<TT, 64>(a, st);
+        case 128: return decode_state_d<TT, 128>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_state(const DecodeArgs& a, hipStream_t st) {
     if (a.nseq == 0) return hipSuccess;
-    return a.bf16 ? decode_t<__bf16>(a, st) : decode_t<float>(a, st);
+    return a.bf16 ? decode_state_t<__bf16>(a, st) : decode_state_t<float>(a, st);
+}
+
+hipError_t launch_decode_norm(const DecodeArgs& a, hipStream_t st) {
+    if (a.nseq == 0) return hipSuccess;
+    if (a.bf16)
+        hipLaunchKernelGGL((decode_norm_kernel<__bf16>), dim3((unsigned)a.nseq), dim3(DEC_THREADS),
+                           0, st, (const __bf16*)a.g, (const __bf16*)a.w, (__bf16*)a.out, a.ybuf,
+                           a.ssbuf, a.H, a.H * a.D, a.eps);
+    else
+        hipLaunchKernelGGL((decode_norm_kernel<float>), dim3((unsigned)a.nseq), dim3(DEC_THREADS),
+                           0, st, (const float*)a.g, (const float*)a.w, (float*)a.out, a.ybuf,
+                           a.ssbuf, a.H, a.H * a.D, a.eps);
+    return hipGetLastError();
 }
 
 }  // namespace la

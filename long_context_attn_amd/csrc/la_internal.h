@@ -88,6 +88,7 @@ struct DecodeArgs {
     float* ybuf;   // [nseq][H*D]
     float* ssbuf;  // [nseq][H]
 };
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_state(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_norm(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace la

@@ -35,7 +35,9 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("lightning_attn_prefill", "lightning_attn_prefill_varlen", "lightning_attn_decode"):
         assert n in names
-    assert len(names) == 6
+    for n in ("lightning_attn_prefill_profiled", "lightning_attn_decode_profiled"):
+        assert n in names
+    assert len(names) == 12
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -130,6 +132,36 @@ def test_decode_validation(lib):
     assert call(dtype=5) == UNSUP
     assert call(ws_bytes=16) == WS
     assert call(nseq=0, q=None, state=None) == OK
+
+
+def test_stage_names_and_profiled_validation(lib):
+    assert lib.lightning_attn_prefill_stage_count() == 5
+    lib.lightning_attn_prefill_stage_name.restype = ctypes.c_char_p
+    lib.lightning_attn_decode_stage_name.restype = ctypes.c_char_p
+    names = [lib.lightning_attn_prefill_stage_name(i) for i in range(5)]
+    assert names == [b"plan", b"chunk_state", b"state_scan", b"walk", b"norm_gate"]
+    assert lib.lightning_attn_prefill_stage_name(5) is None
+    assert lib.lightning_attn_decode_stage_count() == 2
+    assert lib.lightning_attn_decode_stage_name(0) == b"decode_state"
+    assert lib.lightning_attn_decode_stage_name(-1) is None
+    f = lib.lightning_attn_prefill_profiled
+    f.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int]
+    ev = (ctypes.c_void_p * 8)()
+    args = [A] * 6 + [None, None, 1, 128, 2, 64, 32, 0, 1e-6, F32, A, 1 << 40, None]
+    assert f(*args, None, 6) == NULLP          # events missing
+    assert f(*args, ev, 3) == SHAPE            # too few events
+    assert f(*(args[:9] + [-1] + args[10:]), ev, 6) == SHAPE  # validation still applies
+    d = lib.lightning_attn_decode_profiled
+    d.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 3 + [ctypes.c_float, ctypes.c_int,
+                                                                ctypes.c_void_p, ctypes.c_size_t,
+                                                                ctypes.c_void_p, ctypes.c_void_p,
+                                                                ctypes.c_int]
+    dargs = [A] * 7 + [4, 2, 64, 1e-6, F32, A, 1 << 30, None]
+    assert d(*dargs, ev, 2) == SHAPE
+    assert d(*dargs, None, 3) == NULLP
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -14,6 +14,12 @@ import long_context_attn_amd as la
 
 pytestmark = pytest.mark.gpu
 
+# Final-state bound, relative to max|state|.  bf16 inputs: the MFMA path
+# multiplies bf16-rounded SiLU(k) and SiLU(v), each product off by at most
+# 2 * 2^-9 relative, so a sum of such products is within 2^-8 ~ 3.9e-3 of the
+# exact state.  fp32 inputs: fp32 arithmetic throughout.
+STATE_TOL = {torch.float32: 1e-5, torch.bfloat16: 4e-3}
+
 
 def run_prefill(q, k, v, g, w, B, dtype, block, chunk=0, init=None, eps=1e-6):
     T, H, D = q.shape
@@ -43,7 +49,7 @@ def test_tiny_fp32_workload():
         say("tiny fp32 chunk", chunk)
         out, fs = run_prefill(q, k, v, g, w, 1, torch.float32, 32, chunk)
         check(out, ref, torch.float32, "tiny fp32 chunk=%d" % chunk)
-        assert rel_state(host(fs), st) < 1e-5
+        assert rel_state(host(fs), st) < STATE_TOL[torch.float32]
 
 
 @pytest.mark.parametrize("D,block", [(16, 16), (32, 32), (64, 64), (128, 32), (128, 64)])
@@ -55,7 +61,7 @@ def test_fp32_shapes_ragged_with_state(D, block):
     say("fp32 D", D, "block", block)
     out, fs = run_prefill(q, k, v, g, w, B, torch.float32, block, 2 * block, init=init)
     check(out, ref, torch.float32, "fp32 D=%d block=%d" % (D, block))
-    assert rel_state(host(fs), st) < 1e-5
+    assert rel_state(host(fs), st) < STATE_TOL[torch.float32]
 
 
 @pytest.mark.parametrize("D,block,dist", [(64, 32, "unit"), (64, 64, "minimax"),
@@ -69,7 +75,7 @@ def test_bf16_ragged(D, block, dist):
         say("bf16 D", D, "block", block, dist, "chunk", chunk)
         out, fs = run_prefill(q, k, v, g, w, B, torch.bfloat16, block, chunk)
         check(out, ref, torch.bfloat16, "bf16 D=%d block=%d %s chunk=%d" % (D, block, dist, chunk))
-        assert rel_state(host(fs), st) < 1e-4
+        assert rel_state(host(fs), st) < STATE_TOL[torch.bfloat16]
 
 
 @pytest.mark.parametrize("dtype,D,block", [(torch.float32, 64, 32), (torch.bfloat16, 128, 64)])
@@ -89,7 +95,7 @@ def test_varlen_packed(dtype, D, block):
                                     return_final_state=True, chunk_tokens=chunk)
         torch.cuda.synchronize()
         check(out, ref, dtype, "varlen chunk=%d" % chunk)
-        assert rel_state(host(fs), st) < (1e-5 if dtype == torch.float32 else 1e-4)
+        assert rel_state(host(fs), st) < STATE_TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128), (torch.bfloat16, 32)])
