@@ -288,6 +288,30 @@ def bench_decode(args, la, torch, hip):
     return res
 
 
+def pmc_pass(args, la, torch):
+    """Kernels for one rocprofv3 --pmc pass: a copy of exactly 1 GiB (the
+    calibration reference for the traffic counters) and the prefill workload."""
+    from long_context_attn_amd import synth
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    cfg = PREFILL_8K
+    B, N, H, D, blk = cfg["batch"], cfg["seqlen"], cfg["heads"], cfg["head_dim"], cfg["block"]
+    q, k, v, g, w = synth.layer_inputs(synth.PREFILL_8K, B * N, H, D, cfg["dist"], threads=16)
+    to = lambda a, shape: torch.from_numpy(a).cuda().to(torch.bfloat16).view(*shape).contiguous()
+    qd, kd, vd, gd = (to(a, (B, N, H, D)) for a in (q, k, v, g))
+    wd = to(w, (H * D,))
+    out = torch.empty_like(qd)
+    ws = torch.empty(la.prefill_workspace_size(B * N, B, H, D, blk, 0), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.steps):
+        la.prefill(qd, kd, vd, gd, wd, block=blk, eps=cfg["eps"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    log("pmc pass done: copy 1 GiB + %d prefill calls" % args.steps)
+
+
 def cpu_baseline(inputs, budget_s):
     """The CPU oracle (fp64, OpenMP over heads) on the same 8192-token workload,
     repeated until about `budget_s` seconds of host work."""
@@ -314,6 +338,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="counter-collection run: a 1 GiB device copy (calibrates FETCH_SIZE / "
+                         "WRITE_SIZE against a known byte count), then --steps prefill calls; "
+                         "prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the layer's multi-GPU sharding is a design "
@@ -326,6 +354,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     la.library()  # fail loudly if the HIP library is missing
+    if args.pmc_pass:
+        pmc_pass(args, la, torch)
+        return
     hip = Hip()
     pre = bench_prefill(args, la, torch, hip)
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)

@@ -30,12 +30,20 @@ int auto_chunk(int64_t total, int nseq, int heads, int block) {
 struct Layout {
     int chunk = 0;
     int max_chunks = 0;
-    size_t off_segs = 0, off_chunks = 0, off_states = 0, bytes = 0;
+    int n_slots = 0;
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rnorm = 0,
+           off_arrivals = 0, off_ready = 0, bytes = 0;
 };
 
+// the fused bf16 MFMA path (walk + RMSNorm in one kernel)
+bool fused_path(int head_dim, int block, la_dtype dtype) {
+    return dtype == LA_DTYPE_BF16 && head_dim == 128 && block == 64;
+}
+
 // Workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks][states]
+// and, for the fused path, the per-(chunk, block) RMSNorm exchange buffers.
 bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
-                 Layout* L) {
+                 bool fused, Layout* L) {
     if (total < 0 || nseq < 0 || heads < 1 || !supported_dim(head_dim) || !supported_block(block))
         return false;
     int chunk = chunk_tokens;
@@ -52,6 +60,17 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     off = align_up(off + sizeof(la::ChunkEntry) * (size_t)maxc);
     L->off_states = off;
     off = align_up(off + sizeof(float) * (size_t)maxc * heads * head_dim * head_dim);
+    const int64_t slots = fused ? maxc * (chunk / block) : 0;
+    if (slots > (int64_t)0x7fffffff) return false;
+    L->n_slots = (int)slots;
+    L->off_part = off;
+    off = align_up(off + sizeof(float) * (size_t)slots * heads * block);
+    L->off_rnorm = off;
+    off = align_up(off + sizeof(float) * (size_t)slots * block);
+    L->off_arrivals = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)slots);
+    L->off_ready = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)slots);
     L->bytes = off;
     return true;
 }
@@ -85,6 +104,11 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     a.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
     a.states = reinterpret_cast<float*>(ws + L.off_states);
+    a.n_slots = L.n_slots;
+    a.part = reinterpret_cast<float*>(ws + L.off_part);
+    a.rnorm = reinterpret_cast<float*>(ws + L.off_rnorm);
+    a.arrivals = reinterpret_cast<int32_t*>(ws + L.off_arrivals);
+    a.ready = reinterpret_cast<int32_t*>(ws + L.off_ready);
     const bool mfma = la::mfma_supported(a);
     hipError_t e = marks.mark(stream);
     if (e == hipSuccess) e = la::launch_plan(a, stream);
@@ -96,7 +120,8 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     if (e == hipSuccess) e = marks.mark(stream);
     if (e == hipSuccess) e = mfma ? la::launch_walk_mfma(a, stream) : la::launch_walk_valu(a, stream);
     if (e == hipSuccess) e = marks.mark(stream);
-    if (e == hipSuccess) e = la::launch_norm_gate(a, stream);
+    // the MFMA walk applies the RMSNorm * gate epilogue itself
+    if (e == hipSuccess && !mfma) e = la::launch_norm_gate(a, stream);
     if (e == hipSuccess) e = marks.mark(stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -132,7 +157,9 @@ size_t lightning_attn_prefill_workspace_size(int64_t total_tokens, int nseq, int
                                              la_dtype dtype) {
     if (check_dtype(dtype) != LA_OK) return 0;
     Layout L;
-    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, &L)) return 0;
+    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens,
+                     fused_path(head_dim, block, dtype), &L))
+        return 0;
     return L.bytes;
 }
 
@@ -155,7 +182,8 @@ static la_status prefill_impl(const void* q, const void* k, const void* v, const
     if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
     if (final_state && !aligned16(final_state)) return LA_ERR_MISALIGNED;
     Layout L;
-    if (!plan_layout(total, batch, heads, head_dim, block, chunk_tokens, &L))
+    if (!plan_layout(total, batch, heads, head_dim, block, chunk_tokens,
+                     fused_path(head_dim, block, dtype), &L))
         return LA_ERR_UNSUPPORTED;
     if (!workspace) return LA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
@@ -235,7 +263,8 @@ la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void
     if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
     if (final_state && !aligned16(final_state)) return LA_ERR_MISALIGNED;
     Layout L;
-    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, &L))
+    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens,
+                     fused_path(head_dim, block, dtype), &L))
         return LA_ERR_UNSUPPORTED;
     if (!workspace) return LA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return LA_ERR_MISALIGNED;

@@ -18,8 +18,10 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 // chunks of one sequence are consecutive in the table.
 struct PlanHeader {
     int32_t n_chunks;  // chunks in the table (0 if cu_seqlens was invalid)
-    int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow
-    int32_t pad[14];
+    int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow,
+                       // 3 = a cross-head wait of the fused walk timed out
+    int32_t ticket;    // start-order ticket of the fused walk's workgroups
+    int32_t pad[13];
 };
 struct SegEntry {
     int32_t first;  // index of the sequence's first chunk
@@ -65,6 +67,13 @@ struct PrefillArgs {
     SegEntry* segs;
     ChunkEntry* chunks;
     float* states;            // [max_chunks][H][D][D]
+    // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
+    // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block
+    int n_slots;
+    float* part;              // [n_slots][H][64] per-head sums of y^2 per token
+    float* rnorm;             // [n_slots][64] 1 / sqrt(mean y^2 + eps) per token
+    int32_t* arrivals;        // [n_slots] heads that published their sums
+    int32_t* ready;           // [n_slots] 1 once rnorm is written
 };
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st);

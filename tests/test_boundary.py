@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from long_context_attn_amd import ops
 
@@ -60,9 +61,14 @@ def test_status_strings(lib):
 
 def test_prefill_workspace_size(lib):
     ws = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024)
-    # 8 chunks of 1024 tokens (+ one spare per sequence) x 64 heads x 128 x 128 fp32
-    assert ws >= 9 * 64 * 128 * 128 * 4
-    assert ws < 9 * 64 * 128 * 128 * 4 + 65536
+    # 8 chunks of 1024 tokens (+ one spare per sequence) x 64 heads x 128 x 128 fp32 states,
+    # plus the fused path's per-(chunk, 64-token block) exchange: 64 heads x 64 tokens of
+    # partial sums, 64 norm factors and two counters per slot
+    slots = 9 * (1024 // 64)
+    need = 9 * 64 * 128 * 128 * 4 + slots * (64 * 64 * 4 + 64 * 4 + 8)
+    assert need <= ws < need + 65536
+    ws32 = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024, dtype=torch.float32)
+    assert 9 * 64 * 128 * 128 * 4 <= ws32 < 9 * 64 * 128 * 128 * 4 + 65536
     assert ops.prefill_workspace_size(8192, 1, 64, 96, 64, 0) == 0      # head_dim
     assert ops.prefill_workspace_size(8192, 1, 64, 128, 48, 0) == 0     # block
     assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, 100) == 0   # chunk % block

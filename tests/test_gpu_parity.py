@@ -21,15 +21,23 @@ pytestmark = pytest.mark.gpu
 STATE_TOL = {torch.float32: 1e-5, torch.bfloat16: 4e-3}
 
 
+def plan_error(ws):
+    """Error code the kernels leave in the workspace's plan header (0 = ok)."""
+    return int(ws[4:8].cpu().view(torch.int32)[0])
+
+
 def run_prefill(q, k, v, g, w, B, dtype, block, chunk=0, init=None, eps=1e-6):
     T, H, D = q.shape
     N = T // B
     qd, kd, vd, gd = (dev(a, dtype).view(B, N, H, D) for a in (q, k, v, g))
     wd = dev(w, dtype)
     initd = None if init is None else torch.from_numpy(init.astype(np.float32)).cuda()
+    ws = torch.empty(la.prefill_workspace_size(T, B, H, D, block, chunk, dtype), dtype=torch.uint8,
+                     device="cuda")
     out, fs = la.prefill(qd, kd, vd, gd, wd, block=block, eps=eps, initial_state=initd,
-                         return_final_state=True, chunk_tokens=chunk)
+                         return_final_state=True, chunk_tokens=chunk, workspace=ws)
     torch.cuda.synchronize()
+    assert plan_error(ws) == 0
     return out.view(T, H, D), fs
 
 
@@ -89,11 +97,14 @@ def test_varlen_packed(dtype, D, block):
     cu = torch.from_numpy(seg.astype(np.int32)).cuda()
     for chunk in (0, block, 2 * block):
         say("varlen", dtype, "chunk", chunk)
+        ws = torch.empty(la.prefill_workspace_size(T, len(lens), H, D, block, chunk, dtype),
+                         dtype=torch.uint8, device="cuda")
         out, fs = la.prefill_varlen(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(g, dtype),
                                     dev(w, dtype), cu, block=block,
                                     initial_state=torch.from_numpy(init).cuda(),
-                                    return_final_state=True, chunk_tokens=chunk)
+                                    return_final_state=True, chunk_tokens=chunk, workspace=ws)
         torch.cuda.synchronize()
+        assert plan_error(ws) == 0
         check(out, ref, dtype, "varlen chunk=%d" % chunk)
         assert rel_state(host(fs), st) < STATE_TOL[dtype]
 
