@@ -15,11 +15,13 @@ bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool supported_block(int b) { return b == 16 || b == 32 || b == 64; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Chunk length when the caller leaves it to the library: aim for about
-// 1024 (chunk, head) work items so every one of the 256 CUs gets several,
-// while keeping chunks long (the per-chunk state is D*D*4 bytes per head).
+// Chunk length when the caller leaves it to the library: the longest power
+// of two (up to 8192 tokens) that still gives about 256 (chunk, head) work
+// items, one per CU.  The walk holds one workgroup per CU, and every chunk
+// costs a D*D*4-byte state per head that is written, scanned and read back,
+// so fewer, longer chunks are cheaper as long as the CUs stay busy.
 int auto_chunk(int64_t total, int nseq, int heads, int block) {
-    const int64_t target_items = 1024;
+    const int64_t target_items = 256;
     int64_t per = total * heads / target_items;
     int64_t c = block;
     while (c * 2 <= per && c < 8192) c *= 2;
@@ -31,8 +33,7 @@ struct Layout {
     int chunk = 0;
     int max_chunks = 0;
     int n_slots = 0;
-    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rnorm = 0,
-           off_arrivals = 0, off_ready = 0, bytes = 0;
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rsub = 0, bytes = 0;
 };
 
 // the fused bf16 MFMA path (walk + RMSNorm in one kernel)
@@ -64,13 +65,9 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     if (slots > (int64_t)0x7fffffff) return false;
     L->n_slots = (int)slots;
     L->off_part = off;
-    off = align_up(off + sizeof(float) * (size_t)slots * heads * block);
-    L->off_rnorm = off;
-    off = align_up(off + sizeof(float) * (size_t)slots * block);
-    L->off_arrivals = off;
-    off = align_up(off + sizeof(int32_t) * (size_t)slots);
-    L->off_ready = off;
-    off = align_up(off + sizeof(int32_t) * (size_t)slots);
+    off = align_up(off + sizeof(uint64_t) * (size_t)slots * heads * block);
+    L->off_rsub = off;
+    off = align_up(off + sizeof(uint64_t) * (size_t)slots * ((heads + 15) / 16) * block);
     L->bytes = off;
     return true;
 }
@@ -105,10 +102,8 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
     a.states = reinterpret_cast<float*>(ws + L.off_states);
     a.n_slots = L.n_slots;
-    a.part = reinterpret_cast<float*>(ws + L.off_part);
-    a.rnorm = reinterpret_cast<float*>(ws + L.off_rnorm);
-    a.arrivals = reinterpret_cast<int32_t*>(ws + L.off_arrivals);
-    a.ready = reinterpret_cast<int32_t*>(ws + L.off_ready);
+    a.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
+    a.rsub = reinterpret_cast<uint64_t*>(ws + L.off_rsub);
     const bool mfma = la::mfma_supported(a);
     hipError_t e = marks.mark(stream);
     if (e == hipSuccess) e = la::launch_plan(a, stream);

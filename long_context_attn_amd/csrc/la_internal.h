@@ -68,12 +68,12 @@ struct PrefillArgs {
     ChunkEntry* chunks;
     float* states;            // [max_chunks][H][D][D]
     // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
-    // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block
+    // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block.
+    // Each word holds a float in its low half and 1 in its high half once
+    // written (0 = not yet written); the chunk-state kernel clears them.
     int n_slots;
-    float* part;              // [n_slots][H][64] per-head sums of y^2 per token
-    float* rnorm;             // [n_slots][64] 1 / sqrt(mean y^2 + eps) per token
-    int32_t* arrivals;        // [n_slots] heads that published their sums
-    int32_t* ready;           // [n_slots] 1 once rnorm is written
+    uint64_t* part;           // [n_slots][H][64] per-head sums of y^2 per token
+    uint64_t* rsub;           // [n_slots][ceil(H / 16)][64] sums over groups of 16 heads
 };
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st);

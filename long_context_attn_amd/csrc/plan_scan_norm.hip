@@ -18,17 +18,11 @@ constexpr int PLAN_THREADS = 1024;
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu, int nseq, int64_t seqlen, int64_t total, int chunk,
     int max_chunks, PlanHeader* __restrict__ hdr, SegEntry* __restrict__ segs,
-    ChunkEntry* __restrict__ chunks, int n_slots, int32_t* __restrict__ arrivals,
-    int32_t* __restrict__ ready) {
+    ChunkEntry* __restrict__ chunks) {
     __shared__ int32_t scan[PLAN_THREADS];
     __shared__ int32_t bad;
     const int tid = threadIdx.x;
-    // the fused walk's exchange counters start from zero on every call
-    for (int i = tid; i < n_slots; i += PLAN_THREADS) {
-        arrivals[i] = 0;
-        ready[i] = 0;
-    }
-    if (tid == 0) hdr->ticket = 0;
+    if (tid == 0) hdr->ticket = 0;  // start-order ticket of the fused walk
     if (tid == 0) {
         bad = 0;
         if (cu != nullptr && (cu[0] != 0 || (int64_t)cu[nseq] != total)) bad = 1;
@@ -89,8 +83,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a.cu, a.nseq, a.seqlen,
-                       a.total, a.chunk, a.max_chunks, a.hdr, a.segs, a.chunks, a.n_slots,
-                       a.arrivals, a.ready);
+                       a.total, a.chunk, a.max_chunks, a.hdr, a.segs, a.chunks);
     return hipGetLastError();
 }
 

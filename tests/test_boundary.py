@@ -63,9 +63,10 @@ def test_prefill_workspace_size(lib):
     ws = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024)
     # 8 chunks of 1024 tokens (+ one spare per sequence) x 64 heads x 128 x 128 fp32 states,
     # plus the fused path's per-(chunk, 64-token block) exchange: 64 heads x 64 tokens of
-    # partial sums, 64 norm factors and two counters per slot
+    # partial sums and 64 sums for each group of 16 heads per slot, each an 8-byte
+    # {value, written} word
     slots = 9 * (1024 // 64)
-    need = 9 * 64 * 128 * 128 * 4 + slots * (64 * 64 * 4 + 64 * 4 + 8)
+    need = 9 * 64 * 128 * 128 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ws < need + 65536
     ws32 = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024, dtype=torch.float32)
     assert 9 * 64 * 128 * 128 * 4 <= ws32 < 9 * 64 * 128 * 128 * 4 + 65536
