@@ -153,66 +153,68 @@ __global__ __launch_bounds__(NTHREADS) void chunk_state_mfma_kernel(
     const int HD = H * MD;
     const int64_t off0 = ce.start * (int64_t)HD + (int64_t)h * MD;
     const int nblk = (ce.len + MB - 1) / MB;
-
-    if (w >= 4) {
-        // two register sets: block b is loaded into set b & 1 two blocks ahead
-        const int ptid = tid - 256;
-        const int cc = ptid & 15, rg = ptid >> 4;
-        const int voff = (4 * rg * HD + 8 * cc) * 2, rstride = HD * 2;
-        // Loads are issued unconditionally (blocks past the chunk's end get an
-        // empty range and return zeros): a conditional load would make the
-        // compiler copy registers that still have a load in flight.
-        Tile k0, v0, k1, v1;
-        auto load_kv = [&](int b, Tile& tk, Tile& tv) {
-            const int t0 = b * MB, n = max(0, min(MB, ce.len - t0));
-            load_tile(tk, tile_rsrc(k + off0 + (int64_t)t0 * HD, n, HD), voff, rstride);
-            load_tile(tv, tile_rsrc(v + off0 + (int64_t)t0 * HD, n, HD), voff, rstride);
-        };
-        load_kv(0, k0, v0);
-        load_kv(1, k1, v1);
-        auto step = [&](int b, Tile& tk, Tile& tv) {  // block b goes to LDS buffer b & 1
-            if (b < nblk) {
-                bf16x8 ks[4], vs[4];
+    // Every wave loads, applies SiLU and multiplies: the SiLU work is a chain
+    // of dependent transcendental operations, and two waves per SIMD hide its
+    // latency where one could not.  Thread t loads rows t / 16 and t / 16 + 32
+    // of a block, features 8 (t % 16) .. + 7; wave w accumulates the state
+    // tiles dk in [64 (w / 4), +64), dv in [32 (w % 4), +32).
+    const int cc = tid & 15, rg = tid >> 4;
+    const int voff = (rg * HD + 8 * cc) * 2, rstride = 32 * HD * 2;
+    // SPF register sets: block b is loaded into set b % SPF, SPF blocks
+    // ahead.  Loads are issued unconditionally (blocks past the chunk's end
+    // get an empty range and return zeros): a conditional load would make the
+    // compiler copy registers that still have a load in flight.
+    constexpr int SPF = 4;
+    struct Rows {
+        bf16x8 r[2];
+    };
+    Rows tk[SPF], tv[SPF];
+    auto load_rows = [&](const __bf16* base, int b, Rows& t) {
+        const int t0 = b * MB, n = max(0, min(MB, ce.len - t0));
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base + off0 + (int64_t)t0 * HD, n, HD);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ks[r] = silu8(tk.r[r]);
-                    vs[r] = silu8(tv.r[r]);
-                }
-                store_rows(ks, L.k[b & 1], cc, rg);
-                store_rows(vs, L.v[b & 1], cc, rg);
-            }
-            load_kv(b + 2, tk, tv);
-            __syncthreads();
-        };
-        for (int b = 0; b <= nblk; b += 2) {
-            step(b, k0, v0);
-            if (b + 1 <= nblk) step(b + 1, k1, v1);
-        }
-        return;
+        for (int j = 0; j < 2; ++j)
+            t.r[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * rstride, 0));
+    };
+#pragma unroll
+    for (int i = 0; i < SPF; ++i) {
+        load_rows(k, i, tk[i]);
+        load_rows(v, i, tv[i]);
     }
     const int l32 = lane & 31, g = lane >> 5;
-    f32x16 acc[4] = {};
-    for (int b = 0; b <= nblk; ++b) {  // consumes block b - 1
-        if (b >= 1) {
-            const __bf16* sK = L.k[(b - 1) & 1];
-            const __bf16* sV = L.v[(b - 1) & 1];
+    const int n = w & 3, m0 = 2 * (w >> 2);
+    f32x16 acc[2] = {};
+    for (int b0 = 0; b0 < nblk; b0 += SPF) {
+#pragma unroll
+        for (int i = 0; i < SPF; ++i) {
+            const int b = b0 + i;  // block b goes to LDS buffer b & 1
+            if (b >= nblk) break;
+            __bf16* sK = L.k[b & 1];
+            __bf16* sV = L.v[b & 1];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                *reinterpret_cast<bf16x8*>(sK + swz(rg + 32 * j, 8 * cc)) = silu8(tk[i].r[j]);
+                *reinterpret_cast<bf16x8*>(sV + swz(rg + 32 * j, 8 * cc)) = silu8(tv[i].r[j]);
+            }
+            load_rows(k, b + SPF, tk[i]);
+            load_rows(v, b + SPF, tv[i]);
+            __syncthreads();
 #pragma unroll
             for (int s = 0; s < MB / 16; ++s) {
-                const bf16x8 bb = ld_tr_operand(sV, 16 * s, 32 * w, lane);
+                const bf16x8 bb = ld_tr_operand(sV, 16 * s, 32 * n, lane);
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    acc[m] = mfma32(ld_tr_operand(sK, 16 * s, 32 * m, lane), bb, acc[m]);
+                for (int j = 0; j < 2; ++j)
+                    acc[j] = mfma32(ld_tr_operand(sK, 16 * s, 32 * (m0 + j), lane), bb, acc[j]);
             }
         }
-        __syncthreads();
     }
     float* dst = states + ((int64_t)c * H + h) * MD * MD;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int dk = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
-            dst[dk * MD + 32 * w + l32] = acc[m][r];
+            const int dk = 32 * (m0 + j) + 8 * (r >> 2) + 4 * g + (r & 3);
+            dst[dk * MD + 32 * n + l32] = acc[j][r];
         }
 }
 
