@@ -24,6 +24,7 @@ import numpy as np
 
 SEED = 2025
 CHUNK_TOKENS = 65536
+BLOCK_TOKENS = 1024
 
 # tensor ids inside a workload key
 Q, K, V, G, W, LENGTHS, HEAD_PICK, S0_K, S0_V = range(9)
@@ -102,6 +103,40 @@ def token_tensor(workload: int, tensor: int, t0: int, t1: int, H: int, D: int, s
     return out
 
 
+def block_tensor(workload: int, tensor: int, t0: int, t1: int, heads, D: int, scale: float,
+                 bf16: bool = True, threads: int = 1) -> np.ndarray:
+    """Tokens [t0, t1) of the given heads of a [T, H, D] activation whose
+    values are drawn per (1024-token block, head).
+
+    Block j of head h is the stream [2025, workload, tensor, j, h] of 1024 * D
+    values, so any window of tokens or subset of heads can be drawn without
+    drawing the rest: the full-size parity tests use this for the 1M-token
+    workloads.  Returns [t1 - t0, len(heads), D].
+    """
+    heads = list(heads)
+    out = np.empty((t1 - t0, len(heads), D), np.float32)
+    jobs = [(j, i, h) for j in range(t0 // BLOCK_TOKENS, (t1 + BLOCK_TOKENS - 1) // BLOCK_TOKENS)
+            for i, h in enumerate(heads)]
+
+    def fill(job):
+        j, i, h = job
+        base = j * BLOCK_TOKENS
+        a, b = max(t0, base), min(t1, base + BLOCK_TOKENS)
+        x = stream((SEED, workload, tensor, j, h), (b - base) * D)[(a - base) * D:]
+        x = x.reshape(b - a, D)
+        if scale != 1.0:
+            x = x * np.float32(scale)
+        out[a - t0:b - t0, i] = round_bf16(x) if bf16 else x
+
+    if threads > 1 and len(jobs) > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, jobs, chunksize=max(1, len(jobs) // (8 * threads))))
+    else:
+        for job in jobs:
+            fill(job)
+    return out
+
+
 def layer_inputs(workload: int, T: int, H: int, D: int, dist: str, bf16: bool = True,
                  t0: int = 0, threads: int = 1):
     """q, k, v, gate for tokens [t0, t0+T) and the norm weight [H*D]."""
@@ -165,7 +200,12 @@ def decode_step_inputs(step: int, nseq: int, H: int, D: int, dist: str = "unit",
                  for t in (Q, K, V, G))
 
 
+def pick(n: int, pool: int, workload: int, what: int = 0) -> list:
+    """n distinct indices in [0, pool) chosen by the seeded stream of a workload."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, workload, HEAD_PICK, what])))
+    return sorted(int(h) for h in g.choice(pool, size=n, replace=False))
+
+
 def pick_heads(n: int, H: int, workload: int) -> list:
     """n distinct heads chosen by the seeded stream of a workload."""
-    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, workload, HEAD_PICK, 0])))
-    return sorted(int(h) for h in g.choice(H, size=n, replace=False))
+    return pick(n, H, workload, 0)

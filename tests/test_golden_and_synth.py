@@ -55,6 +55,22 @@ def test_stream_is_prefix_consistent_and_chunked():
     assert np.array_equal(full, thr)
 
 
+def test_block_tensor_windows_and_heads_agree():
+    """Per-(1024-token block, head) streams: any window or head subset is the
+    same slice of the whole tensor, with or without threads."""
+    D = 8
+    full = synth.block_tensor(5, synth.K, 0, 3000, range(4), D, 0.5)
+    assert full.shape == (3000, 4, D)
+    assert np.array_equal(synth.block_tensor(5, synth.K, 1000, 2100, [1, 3], D, 0.5),
+                          full[1000:2100][:, [1, 3]])
+    assert np.array_equal(synth.block_tensor(5, synth.K, 0, 3000, range(4), D, 0.5, threads=3),
+                          full)
+    # other tensors and workloads are other streams; values are bf16-representable
+    assert not np.array_equal(synth.block_tensor(5, synth.V, 0, 3000, range(4), D, 0.5), full)
+    assert np.array_equal(synth.round_bf16(full), full)
+    assert synth.pick(3, 20, 4) == synth.pick(3, 20, 4) and len(set(synth.pick(5, 8, 4))) == 5
+
+
 def test_varlen_lengths():
     lens = synth.varlen_lengths(1 << 20)
     assert sum(lens) == 1 << 20

@@ -1,0 +1,190 @@
+"""Full-size workloads on the GPU against the CPU oracle (needs an MI355X).
+
+Every test runs the library at the workload's real shape and in the launch
+configuration bench.py times (the library's automatic chunk length), then
+compares what the fp64 oracle can compute in seconds:
+
+  * prefill, 8192 tokens x 64 heads: every output and the final state;
+  * decode, 256 sequences x 64 heads, 64 steps: each step's outputs and the
+    final states of four seeded sequences whose initial states the oracle
+    built from their seeded prefixes;
+  * varlen, 1,048,576 packed tokens: every output and final state of three
+    seeded sequences of at most 8192 tokens, packed among the others;
+  * one sequence of 1,048,576 tokens: the first 2048 outputs; the state after
+    1,047,552 tokens on four seeded heads; the last 1024 outputs, which the
+    oracle computes from the GPU's state after 1,047,552 tokens (the four
+    seeded heads of that state having been checked on their own).
+
+Inputs the comparison does not see only have to be plausible and come from
+the GPU's random generator; the compared parts come from the seeded streams.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check, dev, host, rel_state, say
+import long_context_attn_amd as la
+from long_context_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+H, D = 64, 128
+# final-state bound for bf16 inputs (see test_gpu_parity.py): the MFMA path
+# multiplies bf16-rounded SiLU(k) and SiLU(v), so the state is within 2^-8
+STATE_TOL = 4e-3
+THREADS = 16
+
+
+def gpu_normal(shape, seed, scale=1.0):
+    """Plausible bf16 N(0, scale^2) filler, drawn on the device in slices."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    t = torch.empty(shape, dtype=BF16, device="cuda")
+    flat = t.view(shape[0], -1)
+    step = max(1, (1 << 28) // flat.shape[1])
+    for a in range(0, shape[0], step):
+        b = min(shape[0], a + step)
+        x = torch.randn(b - a, flat.shape[1], device="cuda", generator=gen)
+        flat[a:b] = (x * scale).to(BF16)
+        del x
+    return t
+
+
+def put(dst, rows, heads, x):
+    """dst[rows, heads, :] = x for a [T, H, D] device tensor and a host block."""
+    xt = torch.from_numpy(x).to(BF16)
+    if list(heads) == list(range(dst.shape[1])):
+        dst[rows].copy_(xt)
+    else:
+        for i, h in enumerate(heads):
+            dst[rows, h].copy_(xt[:, i])
+
+
+def test_prefill_8k_workload():
+    N = 8192
+    q, k, v, g, w = synth.layer_inputs(synth.PREFILL_8K, N, H, D, "minimax", threads=THREADS)
+    say("prefill 8K: inputs ready")
+    out, fs = la.prefill(*(dev(a, BF16).view(1, N, H, D) for a in (q, k, v, g)), dev(w, BF16),
+                         return_final_state=True)
+    torch.cuda.synchronize()
+    ref, st = oracle.prefill(q, k, v, g, w, return_state=True)
+    check(host(out).reshape(N, H, D), ref, BF16, "prefill 8K x 64 heads")
+    err = rel_state(host(fs), st)
+    say("prefill 8K final state rel err %.2e" % err)
+    assert err < STATE_TOL
+
+
+@pytest.mark.slow
+def test_decode_256_workload():
+    S, steps = 256, 64
+    lens = synth.decode_prefix_lengths(S)
+    picks = synth.pick(4, S, synth.DECODE, 1)
+    say("decode: sampled sequences", picks, "prefix lengths", [lens[s] for s in picks])
+    # the other sequences' states only need a plausible magnitude
+    state = gpu_normal((S, H, D, D), 31, 100.0).float()
+    with ThreadPoolExecutor(len(picks)) as ex:
+        kv = list(ex.map(lambda s: synth.decode_prefix_kv(s, lens[s], H, D), picks))
+    ref_state = []
+    for s, (k, v) in zip(picks, kv):
+        s0 = oracle.state(k, v)[0].astype(np.float32)  # fp64 sum, rounded once to fp32
+        state[s].copy_(torch.from_numpy(s0))
+        ref_state.append(s0.astype(np.float64))
+    del kv
+    ref_state = np.stack(ref_state)
+    say("decode: initial states ready")
+    w = torch.ones(H * D, dtype=BF16, device="cuda")
+    wh = np.ones(H * D, np.float32)
+    out = torch.empty(S, H, D, dtype=BF16, device="cuda")
+    worst = 0.0
+    for step in range(steps):
+        qs, ks, vs, gs = synth.decode_step_inputs(step, S, H, D)
+        la.decode(*(dev(a, BF16) for a in (qs, ks, vs, gs)), w, state, out=out)
+        torch.cuda.synchronize()
+        ref, ref_state = oracle.decode(qs[picks], ks[picks], vs[picks], gs[picks], wh, ref_state)
+        emax, _ = check(host(out)[picks], ref, BF16, "decode step %d" % step)
+        worst = max(worst, emax)
+    err = rel_state(host(state[picks]), ref_state)
+    say("decode: worst step e_max %.2e, final states rel err %.2e" % (worst, err))
+    assert err < 1e-4
+
+
+@pytest.mark.slow
+def test_varlen_1m_workload():
+    T = 1 << 20
+    lens = synth.varlen_lengths(T)
+    cu = synth.cu_seqlens(lens)
+    cand = [i for i, L in enumerate(lens) if 0 < L <= 8192 and i > 0]
+    picks = [cand[i] for i in synth.pick(3, len(cand), synth.VARLEN_1M, 1)]
+    say("varlen: %d sequences, sampled" % len(lens), [(s, lens[s]) for s in picks])
+    q, k, v, g = (gpu_normal((T, H, D), 41 + t) for t in range(4))
+    wins = {}
+    for s in picks:
+        a, b = int(cu[s]), int(cu[s + 1])
+        ins = [synth.block_tensor(synth.VARLEN_1M, t, a, b, range(H), D, 1.0, threads=THREADS)
+               for t in (synth.Q, synth.K, synth.V, synth.G)]
+        for dst, x in zip((q, k, v, g), ins):
+            put(dst, slice(a, b), range(H), x)
+        wins[s] = ins
+    say("varlen: inputs ready")
+    w = torch.ones(H * D, dtype=BF16, device="cuda")
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    out, fs = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True)
+    torch.cuda.synchronize()
+    del q, k, v, g
+    wh = np.ones(H * D, np.float32)
+    for s in picks:
+        a, b = int(cu[s]), int(cu[s + 1])
+        ref, st = oracle.prefill(*wins[s], wh, return_state=True)
+        check(host(out[a:b]), ref, BF16, "varlen sequence %d (%d tokens)" % (s, b - a))
+        err = rel_state(host(fs[s:s + 1]), st)
+        say("varlen sequence %d final state rel err %.2e" % (s, err))
+        assert err < STATE_TOL
+
+
+@pytest.mark.slow
+def test_prefill_1m_workload():
+    N = 1 << 20
+    T1 = N - 1024
+    first = 2048
+    picks = synth.pick_heads(4, H, synth.PREFILL_1M)
+    say("prefill 1M: sampled heads", picks)
+    q, k, v, g = (gpu_normal((N, H, D), 51 + t) for t in range(4))
+    ids = (synth.Q, synth.K, synth.V, synth.G)
+    # the four sampled heads' k and v on every token (kept for the oracle)
+    kp = synth.block_tensor(synth.PREFILL_1M, synth.K, 0, N, picks, D, 1.0, threads=THREADS)
+    vp = synth.block_tensor(synth.PREFILL_1M, synth.V, 0, N, picks, D, 1.0, threads=THREADS)
+    put(k, slice(0, N), picks, kp)
+    put(v, slice(0, N), picks, vp)
+    say("prefill 1M: sampled heads' k, v ready")
+    # every head on the first and the last window
+    win = {}
+    for a, b in ((0, first), (T1, N)):
+        win[a] = [synth.block_tensor(synth.PREFILL_1M, t, a, b, range(H), D, 1.0, threads=THREADS)
+                  for t in ids]
+        for dst, x in zip((q, k, v, g), win[a]):
+            put(dst, slice(a, b), range(H), x)
+    w = torch.ones(H * D, dtype=BF16, device="cuda")
+    wh = np.ones(H * D, np.float32)
+    view = lambda t, n: t[:n].view(1, n, H, D)
+    _, fs1 = la.prefill(*(view(t, T1) for t in (q, k, v, g)), w, return_final_state=True)
+    out = la.prefill(*(view(t, N) for t in (q, k, v, g)), w)
+    torch.cuda.synchronize()
+    say("prefill 1M: GPU runs done")
+    out_first, out_last = host(out[0, :first]), host(out[0, T1:])
+    del q, k, v, g, out
+    # state after T1 tokens on the sampled heads
+    st = None
+    for a in range(0, T1, synth.CHUNK_TOKENS):
+        b = min(T1, a + synth.CHUNK_TOKENS)
+        st = oracle.state(kp[a:b], vp[a:b], init_state=st)
+    err = rel_state(host(fs1)[:, picks], st)
+    say("prefill 1M: state after %d tokens, heads %s, rel err %.2e" % (T1, picks, err))
+    assert err < STATE_TOL
+    ref = oracle.prefill(*win[0], wh)
+    check(out_first, ref, BF16, "prefill 1M tokens [0, %d)" % first)
+    ref = oracle.prefill(*win[T1], wh, init_state=host(fs1))
+    check(out_last, ref, BF16, "prefill 1M tokens [%d, %d) from the GPU state" % (T1, N))
