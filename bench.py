@@ -20,7 +20,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -106,12 +105,8 @@ def stage_names(lib, prefix):
 
 
 def source_sha():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "long_context_attn_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
+    from long_context_attn_amd.build import source_sha as sha
+    return sha()
 
 
 def measured_traffic(kernel, workload):

@@ -23,6 +23,16 @@ SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "decode.hip"
 ARCH = "gfx950"
 
 
+def source_sha() -> str:
+    """Short hash of the HIP/C++ sources: ties a committed profile to the kernels it measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for c in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"),
               shutil.which("hipcc") or ""):

@@ -6,21 +6,27 @@
 // then step 4's RMSNorm over the token's H*D values times sigmoid(gate).
 //
 // The step is bound by HBM: the fp32 state (64 KiB per head at D = 128) is
-// read and written once.  Kernel 1 streams the state of one (sequence, head)
-// at a time per workgroup with 16-byte accesses, each thread keeping many
-// loads in flight, and leaves y and the head's sum of squares in the
-// workspace; kernel 2 applies the norm and gate per sequence.
+// read and written once, with 16-byte accesses and every thread keeping
+// several loads in flight.  With at least as many sequences as CUs, one
+// workgroup per sequence streams its heads' states one after another, keeps
+// y in LDS and applies the norm and gate itself; otherwise long-lived
+// workgroups (one per CU) loop over (sequence, head) pairs, leave y and the
+// per-head sums of squares in the workspace, and a second kernel applies the
+// norm and gate per sequence.
+#include <atomic>
+
 #include "la_internal.h"
 
 namespace la {
 
 constexpr int DEC_THREADS = 1024;
 
+// One (sequence, head) pair: S += k~^T v~ in place, y = q~ S.  Leaves y[j] in
+// ysum[j] and returns sum_j y_j^2 in every thread of the workgroup.
 template <class TT, int D>
-__global__ __launch_bounds__(DEC_THREADS) void decode_state_kernel(
-    const TT* __restrict__ q, const TT* __restrict__ k, const TT* __restrict__ v,
-    float* __restrict__ state, float* __restrict__ ybuf, float* __restrict__ ssbuf,
-    int64_t pairs) {
+__device__ __forceinline__ float decode_pair(const TT* __restrict__ q, const TT* __restrict__ k,
+                                             const TT* __restrict__ v, float* __restrict__ state,
+                                             int64_t pair, float* __restrict__ ysum) {
     constexpr int TPR = D / 4;               // threads per state row (4 columns each)
     constexpr int NRG = DEC_THREADS / TPR;   // row groups
     constexpr int RPT = (D + NRG - 1) / NRG; // rows per thread
@@ -30,55 +36,89 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_state_kernel(
     const int tid = threadIdx.x;
     const int cq = tid % TPR, rg = tid / TPR;
     const int j0 = cq * 4;
-    // a fixed set of workgroups (one per CU) walks over the (sequence, head)
-    // pairs: long-lived workgroups keep the memory pipeline fuller than one
-    // short workgroup per pair
+    f32x4* S = reinterpret_cast<f32x4*>(state + pair * D * D);
+    f32x4 rows[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * NRG;
+        if (i < D) rows[m] = __builtin_nontemporal_load(&S[i * TPR + cq]);
+    }
+    if (tid < D) {
+        const int64_t idx = pair * D + tid;
+        qs[tid] = silu_f(to_f32(q[idx]));
+        ks[tid] = silu_f(to_f32(k[idx]));
+        vs[tid] = silu_f(to_f32(v[idx]));
+    }
+    __syncthreads();
+    const f32x4 vj = {vs[j0], vs[j0 + 1], vs[j0 + 2], vs[j0 + 3]};
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * NRG;
+        if (i < D) {
+            const f32x4 s = rows[m] + ks[i] * vj;
+            __builtin_nontemporal_store(s, &S[i * TPR + cq]);
+            y += qs[i] * s;
+        }
+    }
+    red[rg][cq] = y;
+    __syncthreads();
+    float sq = 0.f;
+    if (tid < D) {
+        float yj = 0.f;
+        for (int r = 0; r < NRG; ++r) yj += red[r][tid / 4][tid % 4];
+        ysum[tid] = yj;
+        sq = yj * yj;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = sq;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < DEC_THREADS / 64; ++i) t += wsum[i];
+    // qs/ks/vs, red and wsum are rewritten by the next pair
+    __syncthreads();
+    return t;
+}
+
+// A fixed set of workgroups (one per CU) walks over the (sequence, head)
+// pairs: long-lived workgroups keep the memory pipeline fuller than one short
+// workgroup per pair.  y and the per-head sums of squares go to the workspace
+// for the norm kernel.
+template <class TT, int D>
+__global__ __launch_bounds__(DEC_THREADS) void decode_state_kernel(
+    const TT* __restrict__ q, const TT* __restrict__ k, const TT* __restrict__ v,
+    float* __restrict__ state, float* __restrict__ ybuf, float* __restrict__ ssbuf,
+    int64_t pairs) {
     for (int64_t pair = blockIdx.x; pair < pairs; pair += gridDim.x) {  // sequence * H + head
-        f32x4* S = reinterpret_cast<f32x4*>(state + pair * D * D);
-        f32x4 rows[RPT];
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + m * NRG;
-            if (i < D) rows[m] = __builtin_nontemporal_load(&S[i * TPR + cq]);
-        }
-        if (tid < D) {
-            const int64_t idx = pair * D + tid;
-            qs[tid] = silu_f(to_f32(q[idx]));
-            ks[tid] = silu_f(to_f32(k[idx]));
-            vs[tid] = silu_f(to_f32(v[idx]));
-        }
-        __syncthreads();
-        const f32x4 vj = {vs[j0], vs[j0 + 1], vs[j0 + 2], vs[j0 + 3]};
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + m * NRG;
-            if (i < D) {
-                const f32x4 s = rows[m] + ks[i] * vj;
-                __builtin_nontemporal_store(s, &S[i * TPR + cq]);
-                y += qs[i] * s;
-            }
-        }
-        red[rg][cq] = y;
-        __syncthreads();
-        float sq = 0.f;
-        if (tid < D) {
-            float yj = 0.f;
-            for (int r = 0; r < NRG; ++r) yj += red[r][tid / 4][tid % 4];
-            ybuf[pair * D + tid] = yj;
-            sq = yj * yj;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-        if ((tid & 63) == 0) wsum[tid >> 6] = sq;
-        __syncthreads();
-        if (tid == 0) {
-            float t = 0.f;
-            for (int i = 0; i < DEC_THREADS / 64; ++i) t += wsum[i];
-            ssbuf[pair] = t;
-        }
-        // qs/ks/vs, red and wsum are rewritten for the next pair
-        __syncthreads();
+        const float t = decode_pair<TT, D>(q, k, v, state, pair, ybuf + pair * D);
+        if (threadIdx.x == 0) ssbuf[pair] = t;
+    }
+}
+
+// One workgroup per sequence: all H heads in turn, their y kept in LDS, then
+// the norm and the gate (used when there are at least as many sequences as
+// CUs, so that whole sequences still fill the chip).
+template <class TT, int D>
+__global__ __launch_bounds__(DEC_THREADS) void decode_seq_kernel(
+    const TT* __restrict__ q, const TT* __restrict__ k, const TT* __restrict__ v,
+    const TT* __restrict__ g, const TT* __restrict__ w, TT* __restrict__ out,
+    float* __restrict__ state, int H, float eps) {
+    extern __shared__ float ys[];  // [H * D] y of this token, then [H] sums of squares
+    const int64_t s = blockIdx.x;
+    const int HD = H * D;
+    float* ss = ys + HD;
+    for (int h = 0; h < H; ++h) {
+        const float t = decode_pair<TT, D>(q, k, v, state, s * H + h, ys + h * D);
+        if (threadIdx.x == 0) ss[h] = t;
+    }
+    __syncthreads();
+    float tot = 0.f;
+    for (int h = 0; h < H; ++h) tot += ss[h];  // head order
+    const float r = 1.0f / __builtin_sqrtf(tot / (float)HD + eps);
+    for (int e = threadIdx.x; e < HD; e += DEC_THREADS) {
+        const int64_t idx = s * HD + e;
+        out[idx] = from_f32<TT>(ys[e] * r * to_f32(w[e]) * sigmoid_f(to_f32(g[idx])));
     }
 }
 
@@ -107,21 +147,38 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_norm_kernel(
 // (measured on MI355X: 1024-thread workgroups, one per CU, stream the state
 // faster than more or smaller workgroups).
 static int cu_count() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
+}
+
+// The per-sequence kernel keeps a token's H * D values of y (and H sums) in
+// dynamic LDS, next to about 17 KiB of static LDS: 44 KiB keeps the total
+// within the 64 KiB a launch gets without opting in to more.
+constexpr size_t DEC_SEQ_LDS_MAX = 44 * 1024;
+
+bool decode_fused(const DecodeArgs& a) {
+    return a.nseq >= cu_count() &&
+           sizeof(float) * ((size_t)a.H * a.D + a.H) <= DEC_SEQ_LDS_MAX;
 }
 
 template <class TT, int D>
 static hipError_t decode_state_d(const DecodeArgs& a, hipStream_t st) {
+    if (decode_fused(a)) {
+        const size_t lds = sizeof(float) * ((size_t)a.H * D + a.H);
+        hipLaunchKernelGGL((decode_seq_kernel<TT, D>), dim3((unsigned)a.nseq), dim3(DEC_THREADS),
+                           lds, st, (const TT*)a.q, (const TT*)a.k, (const TT*)a.v,
+                           (const TT*)a.g, (const TT*)a.w, (TT*)a.out, a.state, a.H, a.eps);
+        return hipGetLastError();
+    }
     const int64_t pairs = (int64_t)a.nseq * a.H;
     const int64_t ncu = cu_count();
     const unsigned grid = (unsigned)(pairs < ncu ? pairs : ncu);
@@ -148,7 +205,7 @@ hipError_t launch_decode_state(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode_norm(const DecodeArgs& a, hipStream_t st) {
-    if (a.nseq == 0) return hipSuccess;
+    if (a.nseq == 0 || decode_fused(a)) return hipSuccess;
     if (a.bf16)
         hipLaunchKernelGGL((decode_norm_kernel<__bf16>), dim3((unsigned)a.nseq), dim3(DEC_THREADS),
                            0, st, (const __bf16*)a.g, (const __bf16*)a.w, (__bf16*)a.out, a.ybuf,

@@ -1,11 +1,22 @@
-"""Summarise a rocprofv3 kernel trace of this library's kernels as Markdown.
+"""Summaries of rocprofv3 output for this library's kernels, as Markdown.
 
     python -m long_context_attn_amd.rocprof_summary TRACE_CSV [--title T] [--command C]
+    python -m long_context_attn_amd.rocprof_summary pmc --fetch CSV --write CSV
+           --workload NAME --copy-bytes N [--update JSON] [--title T] [--command C]
 
-Groups the dispatches of the library's kernels (names in namespace la::) by
-kernel and launch grid, so that calls of one workload are averaged together
-and calls of another (for example the prefills that build the decode
-workload's initial states) are kept apart.  Durations are in microseconds.
+The first form groups the dispatches of the library's kernels (names in
+namespace la::) of a --kernel-trace run by kernel and launch grid, so that
+calls of one workload are averaged together and calls of another (for
+example the prefills that build the decode workload's initial states) are
+kept apart.  Durations are in microseconds.
+
+The second form reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE, in KiB per
+dispatch) of `bench.py --pmc-pass`, whose first large dispatch is a device
+copy of exactly --copy-bytes bytes.  The counters do not count bytes one to
+one, so each is scaled by what it reads for that copy (known bytes read and
+written); the result is the HBM traffic per launch of each kernel, recorded
+in --update (a JSON file keyed "kernel@workload") with the hash of the
+kernel sources it was measured on.
 """
 from __future__ import annotations
 
@@ -72,7 +83,72 @@ def markdown(groups, title, command, min_calls=1):
     return "\n".join(out) + "\n"
 
 
+def _pmc_values(path):
+    """{kernel short name: [values]} and the copy kernel's values of one --pmc csv."""
+    vals, copy = {}, []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name, x = r["Kernel_Name"], float(r["Counter_Value"])
+            if "la::" in name or name.startswith("_ZN2la"):
+                vals.setdefault(short_name(name).replace("la::", "").split("<")[0], []).append(x)
+            elif "copyBuffer" in name:
+                copy.append(x)
+    return vals, copy
+
+
+def pmc_summary(fetch_csv, write_csv, workload, copy_bytes, title, command, update=None):
+    import json
+    import os
+    from .build import source_sha
+    fv, fc = _pmc_values(fetch_csv)
+    wv, wc = _pmc_values(write_csv)
+    if not fc or not wc:
+        raise SystemExit("no device-copy dispatch in the counter runs: no calibration")
+    # the copy reads and writes copy_bytes each; counters are KiB per dispatch
+    f_fetch = copy_bytes / (max(fc) * 1024.0)
+    f_write = copy_bytes / (max(wc) * 1024.0)
+    sha = source_sha()
+    out = ["# " + title, "", "Commands (repo root, one MI355X):", ""]
+    out += ["    " + c for c in command.split(" ;; ")]
+    out += ["", "Calibration: the %d-byte device copy reads FETCH_SIZE x %.3f and WRITE_SIZE x %.3f "
+            "bytes per counted KiB/1024; kernel sources %s." % (copy_bytes, f_fetch, f_write, sha), "",
+            "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | "
+            "HBM total MB |", "|---|---|---|---|---|---|---|"]
+    entries = {}
+    for k in sorted(set(fv) & set(wv)):
+        fk = statistics.median(fv[k])
+        wk = statistics.median(wv[k])
+        rd, wr = fk * 1024 * f_fetch, wk * 1024 * f_write
+        out.append("| %s | %d | %.0f | %.0f | %.1f | %.1f | %.1f |" % (
+            k, len(fv[k]), fk, wk, rd / 1e6, wr / 1e6, (rd + wr) / 1e6))
+        entries["%s@%s" % (k, workload)] = dict(
+            hbm_bytes_per_launch=int(rd + wr), read_bytes=int(rd), write_bytes=int(wr),
+            fetch_factor=round(f_fetch, 4), write_factor=round(f_write, 4), source_sha=sha)
+    if update:
+        doc = json.load(open(update)) if os.path.exists(update) else {}
+        doc.update(entries)
+        with open(update, "w") as f:
+            json.dump(doc, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return "\n".join(out) + "\n"
+
+
 def main():
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "pmc":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("pmc")
+        ap.add_argument("--fetch", required=True)
+        ap.add_argument("--write", required=True)
+        ap.add_argument("--workload", required=True)
+        ap.add_argument("--copy-bytes", type=int, required=True)
+        ap.add_argument("--update")
+        ap.add_argument("--title", default="rocprofv3 traffic counters")
+        ap.add_argument("--command", default="")
+        a = ap.parse_args()
+        print(pmc_summary(a.fetch, a.write, a.workload, a.copy_bytes, a.title, a.command,
+                          a.update), end="")
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("trace")
     ap.add_argument("--title", default="rocprofv3 kernel trace summary")

@@ -109,9 +109,13 @@ def test_varlen_packed(dtype, D, block):
         assert rel_state(host(fs), st) < STATE_TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128), (torch.bfloat16, 32)])
-def test_decode_steps(dtype, D):
-    S, H, L = 6, 4, 40
+@pytest.mark.parametrize("dtype,D,S", [(torch.float32, 64, 6), (torch.bfloat16, 128, 6),
+                                       (torch.bfloat16, 32, 6), (torch.float32, 64, 300),
+                                       (torch.bfloat16, 128, 260)])
+def test_decode_steps(dtype, D, S):
+    """S >= the CU count (256) takes the one-workgroup-per-sequence kernel with
+    the norm fused; fewer sequences take the pair loop and the norm kernel."""
+    H, L = 4, 40
     bf = dtype == torch.bfloat16
     q, k, v, g, w = inputs(S * L, H, D, "unit", bf16=bf, key=6)
     seg = np.arange(S + 1) * L
@@ -122,7 +126,7 @@ def test_decode_steps(dtype, D):
     for step in range(3):
         qs, ks, vs, gs = (inputs(S, H, D, "unit", bf16=bf, key=100 + step)[i] for i in range(4))
         ref, state_ref = oracle.decode(qs, ks, vs, gs, w, state_ref)
-        say("decode", dtype, "D", D, "step", step)
+        say("decode", dtype, "D", D, "S", S, "step", step)
         out = la.decode(dev(qs, dtype), dev(ks, dtype), dev(vs, dtype), dev(gs, dtype), wd,
                         state_gpu)
         torch.cuda.synchronize()
