@@ -110,8 +110,9 @@ def pmc_summary(fetch_csv, write_csv, workload, copy_bytes, title, command, upda
     sha = source_sha()
     out = ["# " + title, "", "Commands (repo root, one MI355X):", ""]
     out += ["    " + c for c in command.split(" ;; ")]
-    out += ["", "Calibration: the %d-byte device copy reads FETCH_SIZE x %.3f and WRITE_SIZE x %.3f "
-            "bytes per counted KiB/1024; kernel sources %s." % (copy_bytes, f_fetch, f_write, sha), "",
+    out += ["", "Calibration: for a device copy of %d bytes FETCH_SIZE counts 1/%.3f of the bytes "
+            "read and WRITE_SIZE 1/%.3f of the bytes written; the byte columns scale the counters "
+            "by those factors.  Kernel sources %s." % (copy_bytes, f_fetch, f_write, sha), "",
             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | "
             "HBM total MB |", "|---|---|---|---|---|---|---|"]
     entries = {}
