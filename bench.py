@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the Lightning Attention layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long]
 
 Prints ONE JSON line.  A step is one call of the library's prefill on the
 MiniMax-shaped workload: batch 1, 8192 tokens, 64 heads x head_dim 128
@@ -14,7 +14,8 @@ value = prefill tokens/s.  Also reported: TFLOP/s on the block-tiled FLOP
 count, the per-kernel split (HIP events recorded between the library's
 kernels on the stream they run on), the roofline of the dominant kernel, the
 decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
-as state GB/s, and the CPU oracle timed on this host's cores.
+as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
+sequence) as time per call, and the CPU oracle timed on this host's cores.
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ PREFILL_8K = dict(workload="prefill_8k_64h_d128_bf16", batch=1, seqlen=8192, hea
                   head_dim=128, block=64, eps=1e-6, dist="minimax")
 DECODE_256 = dict(workload="decode_256seq_64h_d128_fp32state", nseq=256, heads=64, head_dim=128,
                   steps=64, prefix_lo=1024, prefix_hi=32768, eps=1e-6, dist="unit")
-# parity-only workloads (tests/test_gpu_workloads.py), listed for reference
+# 1M-token workloads: timed beside the main line, parity in tests/test_gpu_workloads.py
 PREFILL_1M = dict(workload="prefill_1m_64h_d128_bf16", batch=1, seqlen=1 << 20, heads=64,
                   head_dim=128, block=64)
 VARLEN_1M = dict(workload="varlen_1m_64h_d128_bf16", total=1 << 20, heads=64, head_dim=128,
@@ -284,6 +285,57 @@ def bench_decode(args, la, torch, hip):
     return res
 
 
+def bench_long(args, la, torch):
+    """Configs at 1,048,576 tokens: the varlen pack (log-uniform lengths) and one
+    sequence.  Their inputs come from the GPU's random generator (timing does not
+    depend on the values; parity on seeded inputs is in tests/test_gpu_workloads.py)."""
+    from long_context_attn_amd import synth
+    H, D, T = PREFILL_1M["heads"], PREFILL_1M["head_dim"], PREFILL_1M["seqlen"]
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2025)
+    x = [torch.empty(T, H, D, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    for t in x:
+        for a in range(0, T, 1 << 15):
+            t[a:a + (1 << 15)] = torch.randn(1 << 15, H, D, device=dev, generator=gen).to(t.dtype)
+    w = torch.ones(H * D, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(x[0])
+    lens = synth.varlen_lengths(T)
+    cu = torch.tensor(synth.cu_seqlens(lens).astype("int32"), device=dev)
+    runs = {
+        VARLEN_1M["workload"]: (lambda ws: la.prefill_varlen(*x, w, cu, out=out, workspace=ws),
+                                la.prefill_workspace_size(T, len(lens), H, D, 64, 0)),
+        PREFILL_1M["workload"]: (lambda ws: la.prefill(*(t.view(1, T, H, D) for t in x), w,
+                                                       out=out.view(1, T, H, D), workspace=ws),
+                                 la.prefill_workspace_size(T, 1, H, D, 64, 0)),
+    }
+    res = {}
+    for name, (call, nbytes) in runs.items():
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        call(ws)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call(ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        res[name] = dict(ms_median=round(ms, 3), ms_min=round(min(times), 3),
+                         tokens_per_s=round(T / (ms * 1e-3), 1),
+                         layer_hbm_frac=round(layer_bytes_per_token(H, D) * T / (ms * 1e-3) / 1e9
+                                              / HBM_PEAK_GBS, 4))
+        if name == VARLEN_1M["workload"]:
+            res[name]["sequences"] = len(lens)
+        log("%s: %.2f ms (median of 5), %.2f M tok/s" % (name, ms, T / ms / 1e3))
+        del ws
+    del x, out
+    return res
+
+
 def pmc_pass(args, la, torch):
     """Kernels for one rocprofv3 --pmc pass: a copy of exactly 1 GiB (the
     calibration reference for the traffic counters) and the prefill workload."""
@@ -333,6 +385,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-long", action="store_true", help="skip the 1M-token workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter-collection run: a 1 GiB device copy (calibrates FETCH_SIZE / "
@@ -356,6 +409,7 @@ def main():
     hip = Hip()
     pre = bench_prefill(args, la, torch, hip)
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)
+    long_ctx = None if args.no_long else bench_long(args, la, torch)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(pre["inputs"], args.cpu_seconds)
@@ -383,6 +437,7 @@ def main():
         "kernels_us": pre["kernels_us"],
         "roofline": pre["roofline"],
         "decode": dec,
+        "long_context": long_ctx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
