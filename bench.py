@@ -182,12 +182,12 @@ def bench_prefill(args, la, torch, hip):
     walk_us = per["walk"] * 1e3
     walk_bytes = walk_bytes_per_token(H, D) * tokens
     achieved = walk_bytes / (walk_us * 1e-6) / 1e9
-    traffic = measured_traffic("walk_norm_mfma_kernel", cfg["workload"])
+    traffic = measured_traffic("prefill_mfma_kernel", cfg["workload"])
     res = dict(
         ms_per_step=ms, tokens_per_s=tok_s, tflops=fl / (ms * 1e-3) / 1e12,
         layer_hbm_frac=layer_bytes_per_token(H, D) * tokens / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         kernels_us={n: round(per[n] * 1e3, 2) for n in names},
-        roofline=dict(kernel="walk_norm_mfma_kernel", bound="hbm", achieved=round(achieved, 1),
+        roofline=dict(kernel="prefill_mfma_kernel", bound="hbm", achieved=round(achieved, 1),
                       peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=traffic, algorithmic_bytes_per_launch=walk_bytes,
                       avg_launch_us=round(walk_us, 2)),

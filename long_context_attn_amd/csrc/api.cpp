@@ -33,7 +33,8 @@ struct Layout {
     int chunk = 0;
     int max_chunks = 0;
     int n_slots = 0;
-    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rsub = 0, bytes = 0;
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_ring = 0, off_flag = 0, off_part = 0,
+           off_rsub = 0, off_clear_end = 0, bytes = 0;
 };
 
 // the fused bf16 MFMA path (walk + RMSNorm in one kernel)
@@ -41,17 +42,25 @@ bool fused_path(int head_dim, int block, la_dtype dtype) {
     return dtype == LA_DTYPE_BF16 && head_dim == 128 && block == 64;
 }
 
-// Workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks][states]
-// and, for the fused path, the per-(chunk, block) RMSNorm exchange buffers.
+// Workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks], then
+//  * portable path: per-chunk states [max_chunks][H][D][D] fp32;
+//  * single-pass MFMA path: the chunk-state ring [slots][H][D*D] fp32, and the
+//    words the plan kernel clears on every call: ring flags [slots][H][4],
+//    the per-(chunk, block) RMSNorm exchange part [n_slots][H][64] and
+//    rsub [n_slots][ceil(H/16)][64].
 bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
                  bool fused, Layout* L) {
     if (total < 0 || nseq < 0 || heads < 1 || !supported_dim(head_dim) || !supported_block(block))
         return false;
     int chunk = chunk_tokens;
-    if (chunk == 0) chunk = auto_chunk(total, nseq, heads, block);
+    // The single-pass MFMA kernel reads K and V of every chunk but a
+    // sequence's last one twice (state pass, then walk); 2048-token chunks
+    // measured fastest at 8192 tokens x 64 heads (one item per CU).
+    if (chunk == 0) chunk = fused ? 2048 : auto_chunk(total, nseq, heads, block);
     if (chunk < block || chunk % block != 0) return false;
     const int64_t maxc = total / chunk + nseq;  // >= sum over sequences of ceil(L_s / chunk)
-    if (maxc > (int64_t)0x7fffffff / 2 || maxc * heads > (int64_t)0xffffffffLL) return false;
+    // work-item tickets (chunk items + one per sequence) are 32-bit
+    if (maxc > (int64_t)0x7fffffff / 2 || maxc * heads + nseq > (int64_t)0x7fffffffLL) return false;
     L->chunk = chunk;
     L->max_chunks = (int)maxc;
     size_t off = align_up(sizeof(la::PlanHeader));
@@ -59,15 +68,25 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     off = align_up(off + sizeof(la::SegEntry) * (size_t)nseq);
     L->off_chunks = off;
     off = align_up(off + sizeof(la::ChunkEntry) * (size_t)maxc);
-    L->off_states = off;
-    off = align_up(off + sizeof(float) * (size_t)maxc * heads * head_dim * head_dim);
-    const int64_t slots = fused ? maxc * (chunk / block) : 0;
+    if (!fused) {
+        L->off_states = off;
+        off = align_up(off + sizeof(float) * (size_t)maxc * heads * head_dim * head_dim);
+        L->bytes = off;
+        return true;
+    }
+    const int ring = la::prefill_mfma_ring_slots();
+    L->off_ring = off;
+    off = align_up(off + sizeof(float) * (size_t)ring * heads * head_dim * head_dim);
+    const int64_t slots = maxc * (chunk / block);
     if (slots > (int64_t)0x7fffffff) return false;
     L->n_slots = (int)slots;
+    L->off_flag = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)ring * heads * 4);
     L->off_part = off;
     off = align_up(off + sizeof(uint64_t) * (size_t)slots * heads * block);
     L->off_rsub = off;
     off = align_up(off + sizeof(uint64_t) * (size_t)slots * ((heads + 15) / 16) * block);
+    L->off_clear_end = off;
     L->bytes = off;
     return true;
 }
@@ -100,23 +119,38 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     a.hdr = reinterpret_cast<la::PlanHeader*>(ws);
     a.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
-    a.states = reinterpret_cast<float*>(ws + L.off_states);
-    a.n_slots = L.n_slots;
-    a.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
-    a.rsub = reinterpret_cast<uint64_t*>(ws + L.off_rsub);
     const bool mfma = la::mfma_supported(a);
+    if (mfma) {
+        a.states = nullptr;
+        a.ring = reinterpret_cast<float*>(ws + L.off_ring);
+        a.ring_flag = reinterpret_cast<int32_t*>(ws + L.off_flag);
+        a.n_slots = L.n_slots;
+        a.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
+        a.rsub = reinterpret_cast<uint64_t*>(ws + L.off_rsub);
+        a.clear = reinterpret_cast<uint64_t*>(ws + L.off_flag);
+        a.clear_words = (int64_t)((L.off_clear_end - L.off_flag) / sizeof(uint64_t));
+    } else {
+        a.states = reinterpret_cast<float*>(ws + L.off_states);
+    }
     hipError_t e = marks.mark(stream);
     if (e == hipSuccess) e = la::launch_plan(a, stream);
     if (e == hipSuccess) e = marks.mark(stream);
-    if (e == hipSuccess)
-        e = mfma ? la::launch_chunk_state_mfma(a, stream) : la::launch_chunk_state_valu(a, stream);
-    if (e == hipSuccess) e = marks.mark(stream);
-    if (e == hipSuccess) e = la::launch_state_scan(a, stream);
-    if (e == hipSuccess) e = marks.mark(stream);
-    if (e == hipSuccess) e = mfma ? la::launch_walk_mfma(a, stream) : la::launch_walk_valu(a, stream);
-    if (e == hipSuccess) e = marks.mark(stream);
-    // the MFMA walk applies the RMSNorm * gate epilogue itself
-    if (e == hipSuccess && !mfma) e = la::launch_norm_gate(a, stream);
+    if (mfma) {
+        // one kernel: state pass, chunk-state hand-over, walk and RMSNorm
+        // (the stage marks of the portable path's kernels stay empty)
+        if (e == hipSuccess) e = marks.mark(stream);
+        if (e == hipSuccess) e = marks.mark(stream);
+        if (e == hipSuccess) e = la::launch_prefill_mfma(a, stream);
+        if (e == hipSuccess) e = marks.mark(stream);
+    } else {
+        if (e == hipSuccess) e = la::launch_chunk_state_valu(a, stream);
+        if (e == hipSuccess) e = marks.mark(stream);
+        if (e == hipSuccess) e = la::launch_state_scan(a, stream);
+        if (e == hipSuccess) e = marks.mark(stream);
+        if (e == hipSuccess) e = la::launch_walk_valu(a, stream);
+        if (e == hipSuccess) e = marks.mark(stream);
+        if (e == hipSuccess) e = la::launch_norm_gate(a, stream);
+    }
     if (e == hipSuccess) e = marks.mark(stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

@@ -21,7 +21,11 @@ struct PlanHeader {
     int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow,
                        // 3 = a cross-head wait of the fused walk timed out
     int32_t ticket;    // start-order ticket of the fused walk's workgroups
-    int32_t pad[13];
+    int32_t wait_site; // error 3: which wait gave up first (1 group sums, 2 previous chunk's
+                       // state, 3 free state slot, 4 norm factors), its chunk and head
+    int32_t wait_chunk;
+    int32_t wait_head;
+    int32_t pad[10];
 };
 struct SegEntry {
     int32_t first;  // index of the sequence's first chunk
@@ -74,6 +78,12 @@ struct PrefillArgs {
     int n_slots;
     uint64_t* part;           // [n_slots][H][64] per-head sums of y^2 per token
     uint64_t* rsub;           // [n_slots][ceil(H / 16)][64] sums over groups of 16 heads
+    // chunk-state hand-over of the single-pass MFMA prefill
+    float* ring;              // [ring slots][H][64][256] fp32 (a consumer-register image)
+    int32_t* ring_flag;       // [ring slots][H][4]
+    // words the plan kernel zeroes on every call (ring flags and exchange words)
+    uint64_t* clear;
+    int64_t clear_words;
 };
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st);
@@ -82,10 +92,11 @@ hipError_t launch_norm_gate(const PrefillArgs& a, hipStream_t st);
 // portable fp32 vector-ALU kernels (any supported shape)
 hipError_t launch_chunk_state_valu(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_walk_valu(const PrefillArgs& a, hipStream_t st);
-// bf16 MFMA kernels (D = 128, block = 64)
+// single-pass bf16 MFMA prefill (D = 128, block = 64): state pass, hand-over
+// of the chunk states, walk and RMSNorm in one kernel after the plan
 bool mfma_supported(const PrefillArgs& a);
-hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
-hipError_t launch_walk_mfma(const PrefillArgs& a, hipStream_t st);
+int prefill_mfma_ring_slots();
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *w;

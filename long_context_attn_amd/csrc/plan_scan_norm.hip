@@ -11,18 +11,31 @@
 namespace la {
 
 // ------------------------------------------------------------------- plan
-// One workgroup of 1024 threads: chunk counts per sequence, exclusive scan,
-// then each thread writes the chunk records of its sequences.
+// Workgroup 0 (1024 threads): chunk counts per sequence, exclusive scan,
+// then each thread writes the chunk records of its sequences.  The other
+// workgroups zero the words the single-pass MFMA prefill expects cleared on
+// every call (its chunk-state flags and RMSNorm exchange words).
 constexpr int PLAN_THREADS = 1024;
+constexpr int CLEAR_BLOCKS = 256;
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu, int nseq, int64_t seqlen, int64_t total, int chunk,
     int max_chunks, PlanHeader* __restrict__ hdr, SegEntry* __restrict__ segs,
-    ChunkEntry* __restrict__ chunks) {
+    ChunkEntry* __restrict__ chunks, uint64_t* __restrict__ clear, int64_t clear_words) {
+    if (blockIdx.x > 0) {
+        const int64_t stride = (int64_t)(gridDim.x - 1) * PLAN_THREADS;
+        for (int64_t i = (int64_t)(blockIdx.x - 1) * PLAN_THREADS + threadIdx.x; i < clear_words;
+             i += stride)
+            clear[i] = 0;
+        return;
+    }
     __shared__ int32_t scan[PLAN_THREADS];
     __shared__ int32_t bad;
     const int tid = threadIdx.x;
-    if (tid == 0) hdr->ticket = 0;  // start-order ticket of the fused walk
+    if (tid == 0) {
+        hdr->ticket = 0;  // start-order ticket of the single-pass prefill
+        hdr->wait_site = hdr->wait_chunk = hdr->wait_head = 0;
+    }
     if (tid == 0) {
         bad = 0;
         if (cu != nullptr && (cu[0] != 0 || (int64_t)cu[nseq] != total)) bad = 1;
@@ -82,8 +95,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
 }
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a.cu, a.nseq, a.seqlen,
-                       a.total, a.chunk, a.max_chunks, a.hdr, a.segs, a.chunks);
+    int64_t blocks = (a.clear_words + PLAN_THREADS - 1) / PLAN_THREADS;
+    if (blocks > CLEAR_BLOCKS) blocks = CLEAR_BLOCKS;
+    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(1 + blocks)), dim3(PLAN_THREADS), 0, st, a.cu,
+                       a.nseq, a.seqlen, a.total, a.chunk, a.max_chunks, a.hdr, a.segs, a.chunks,
+                       a.clear, a.clear_words);
     return hipGetLastError();
 }
 

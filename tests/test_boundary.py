@@ -61,13 +61,17 @@ def test_status_strings(lib):
 
 def test_prefill_workspace_size(lib):
     ws = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024)
-    # 8 chunks of 1024 tokens (+ one spare per sequence) x 64 heads x 128 x 128 fp32 states,
-    # plus the fused path's per-(chunk, 64-token block) exchange: 64 heads x 64 tokens of
-    # partial sums and 64 sums for each group of 16 heads per slot, each an 8-byte
-    # {value, written} word
+    # bf16 MFMA path, 8 chunks of 1024 tokens (+ one spare per sequence): a 4-slot ring of
+    # 64 heads x 128 x 128 fp32 chunk states, 4 flags per ring slot and head, and per
+    # (chunk, 64-token block) the RMSNorm exchange: 64 heads x 64 tokens of partial sums
+    # and 64 sums for each group of 16 heads, each an 8-byte {value, written} word
     slots = 9 * (1024 // 64)
-    need = 9 * 64 * 128 * 128 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
+    need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ws < need + 65536
+    # the automatic chunk length of this path is 2048 tokens
+    slots = (4 + 1) * (2048 // 64)
+    need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
+    assert need <= ops.prefill_workspace_size(8192, 1, 64, 128, 64, 0) < need + 65536
     ws32 = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024, dtype=torch.float32)
     assert 9 * 64 * 128 * 128 * 4 <= ws32 < 9 * 64 * 128 * 128 * 4 + 65536
     assert ops.prefill_workspace_size(8192, 1, 64, 96, 64, 0) == 0      # head_dim
