@@ -146,7 +146,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_norm_kernel(
 // Workgroups of the state kernel: one per CU, each looping over pairs
 // (measured on MI355X: 1024-thread workgroups, one per CU, stream the state
 // faster than more or smaller workgroups).
-static int cu_count() {
+int device_cu_count() {
     static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -166,7 +166,7 @@ static int cu_count() {
 constexpr size_t DEC_SEQ_LDS_MAX = 44 * 1024;
 
 bool decode_fused(const DecodeArgs& a) {
-    return a.nseq >= cu_count() &&
+    return a.nseq >= device_cu_count() &&
            sizeof(float) * ((size_t)a.H * a.D + a.H) <= DEC_SEQ_LDS_MAX;
 }
 
@@ -180,7 +180,7 @@ static hipError_t decode_state_d(const DecodeArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     const int64_t pairs = (int64_t)a.nseq * a.H;
-    const int64_t ncu = cu_count();
+    const int64_t ncu = device_cu_count();
     const unsigned grid = (unsigned)(pairs < ncu ? pairs : ncu);
     hipLaunchKernelGGL((decode_state_kernel<TT, D>), dim3(grid), dim3(DEC_THREADS), 0, st,
                        (const TT*)a.q, (const TT*)a.k, (const TT*)a.v, a.state, a.ybuf, a.ssbuf,

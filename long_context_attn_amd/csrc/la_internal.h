@@ -19,10 +19,12 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 struct PlanHeader {
     int32_t n_chunks;  // chunks in the table (0 if cu_seqlens was invalid)
     int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow,
-                       // 3 = a cross-head wait of the fused walk timed out
+                       // 3 = a cross-workgroup wait of an MFMA prefill timed out
     int32_t ticket;    // start-order ticket of the fused walk's workgroups
-    int32_t wait_site; // error 3: which wait gave up first (1 group sums, 2 previous chunk's
-                       // state, 3 free state slot, 4 norm factors), its chunk and head
+    int32_t wait_site; // error 3: which wait gave up first, where and who.  Single-pass
+                       // kernel: 1 group sums, 2 previous chunk's state, 3 free state slot,
+                       // 4 norm factors (chunk, head).  Lane kernel: 1 lanes' sums,
+                       // 2 group sums, 4 totals (block, lane).
     int32_t wait_chunk;
     int32_t wait_head;
     int32_t pad[10];
@@ -84,7 +86,14 @@ struct PrefillArgs {
     // words the plan kernel zeroes on every call (ring flags and exchange words)
     uint64_t* clear;
     int64_t clear_words;
+    // lane kernel: per-token totals over all lanes, [ring slots][64]
+    // (part and rsub are rings of the same depth, [slots][lanes][64] and
+    // [slots][ceil(lanes / group)][64])
+    uint64_t* tot;
 };
+
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cu_count();
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_state_scan(const PrefillArgs& a, hipStream_t st);
@@ -97,6 +106,15 @@ hipError_t launch_walk_valu(const PrefillArgs& a, hipStream_t st);
 bool mfma_supported(const PrefillArgs& a);
 int prefill_mfma_ring_slots();
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
+// lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,
+// 32-column state slice) walks every sequence whole; needs heads * 4 <= cus
+// (all lanes resident at once).  The plan runs first with chunk = 64 and no
+// chunk table, and clears the exchange rings.
+int lane_max_lanes();
+int lane_ring_slots();
+int lane_group_size();
+int lane_slices();
+hipError_t launch_prefill_lane(const PrefillArgs& a, hipStream_t st);
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *w;

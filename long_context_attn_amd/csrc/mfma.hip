@@ -149,15 +149,18 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
         // The state pass visits the chunk's blocks last to first, so the walk,
         // which starts with the first block, re-reads the most recently read
         // K and V first (still in the caches).
-        auto load_qk = [&](int i, Tile& tq, Tile& tk) {
-            const bool st = i < nA;
-            const int blk = st ? nA - 1 - i : i - nA;
-            const int64_t t0 = (int64_t)blk * MB * HD;
-            load_tile(tq, tile_rsrc(q + off0 + t0, st ? 0 : rows(blk), HD), voff, rstride);
-            load_tile(tk, tile_rsrc(k + off0 + t0, rows(blk), HD), voff, rstride);
+        auto blk_of = [&](int i) { return i < nA ? nA - 1 - i : i - nA; };
+        auto load_q = [&](int i, Tile& tq) {
+            const int blk = blk_of(i);
+            load_tile(tq, tile_rsrc(q + off0 + (int64_t)blk * MB * HD, i < nA ? 0 : rows(blk), HD),
+                      voff, rstride);
+        };
+        auto load_k = [&](int i, Tile& tk) {
+            const int blk = blk_of(i);
+            load_tile(tk, tile_rsrc(k + off0 + (int64_t)blk * MB * HD, rows(blk), HD), voff, rstride);
         };
         auto load_v = [&](int i, Tile& tv) {
-            const int blk = i < nA ? nA - 1 - i : i - nA;
+            const int blk = blk_of(i);
             load_tile(tv, tile_rsrc(v + off0 + (int64_t)blk * MB * HD, rows(blk), HD), voff, rstride);
         };
         auto load_gate = [&](int jf, Tile& tg) {
@@ -165,9 +168,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                       rstride);
         };
         Tile q0, k0, v0, g0, q1, k1, v1, g1;
-        load_qk(0, q0, k0);
+        load_q(0, q0);
+        load_k(0, k0);
         load_v(0, v0);
-        load_qk(1, q1, k1);
+        load_q(1, q1);
+        load_k(1, k1);
         load_v(1, v1);
         auto step = [&](int it, Tile& tq, Tile& tk, Tile& tv, Tile& tg) {
             const int buf = it & 1;
@@ -220,12 +225,13 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                 store_rows(qs, L.q[buf], cc, rg);
                 store_rows(ks, L.k[buf], cc, rg);
             }
-            load_qk(it + 2, tq, tk);
+            load_q(it + 2, tq);
+            load_k(it + 2, tk);
             __syncthreads();  // A
             if (jf >= 0 && jf < nblk)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) keep(od[r]);
-            // ---- phase 2: stage v
+            // ---- phase 2: stage V~
             if (b < nblk) {
                 bf16x8 vs[4];
 #pragma unroll
@@ -300,12 +306,25 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
         }
         // ---- phase 1: state pass, S += K~^T V~ of block it - 1
         if (it >= 1 && it <= nA) {
+            // all operands in flight before the products (an MFMA chain that
+            // waits for each operand load in turn exposes the LDS latency at
+            // every step)
+            // (half of the tokens at a time)
 #pragma unroll
-            for (int s = 0; s < MB / 16; ++s) {
-                const bf16x8 bb = ld_tr_operand(sV, 16 * s, 32 * w, lane);
+            for (int h2 = 0; h2 < 2; ++h2) {
+                bf16x8 vb[2], ka[2][4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    S[m] = mfma32(ld_tr_operand(sK, 16 * s, 32 * m, lane), bb, S[m]);
+                for (int i = 0; i < 2; ++i) {
+                    const int s = 2 * h2 + i;
+                    vb[i] = ld_tr_operand(sV, 16 * s, 32 * w, lane);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) ka[i][m] = ld_tr_operand(sK, 16 * s, 32 * m, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) S[m] = mfma32(ka[i][m], vb[i], S[m]);
             }
         }
         // ---- phase 1: walk: S^T Q~^T into O, and the scores of block jc
@@ -316,8 +335,18 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
             // tile m hold dk = 16 s + 8 (j / 4) + 4 g + j % 4; one exchange
             // between the lane halves turns that into dk = 16 s + 8 g + j, so
             // that the matching Q~ operand is one 16-byte row read.
+            // (Q~ operands loaded half of the features at a time)
+            bf16x8 qo[MD / 32][2];
 #pragma unroll
             for (int s = 0; s < MD / 16; ++s) {
+                if (s % (MD / 32) == 0) {
+#pragma unroll
+                    for (int i = 0; i < MD / 32; ++i)
+#pragma unroll
+                        for (int tb = 0; tb < 2; ++tb)
+                            qo[i][tb] = ld_row_operand(sQ, 32 * tb + l32, 16 * (s + i) + 8 * g);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 const int m = s >> 1, r0 = 8 * (s & 1);
                 unsigned p0 = pack_bf16(S[m][r0 + 0], S[m][r0 + 1]);
                 unsigned p1 = pack_bf16(S[m][r0 + 2], S[m][r0 + 3]);
@@ -327,15 +356,19 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                 const auto x13 = __builtin_amdgcn_permlane32_swap(p1, p3, false, false);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{x02[0], x13[0], x02[1], x13[1]});
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    O[tb] = mfma32(a, ld_row_operand(sQ, 32 * tb + l32, 16 * s + 8 * g), O[tb]);
+                for (int tb = 0; tb < 2; ++tb) O[tb] = mfma32(a, qo[s % (MD / 32)][tb], O[tb]);
             }
             if (!(qa == 1 && qb == 0)) {
+                bf16x8 kr[MD / 16], qr[MD / 16];
+#pragma unroll
+                for (int s = 0; s < MD / 16; ++s) {
+                    kr[s] = ld_row_operand(sK, 32 * qa + l32, 16 * s + 8 * g);
+                    qr[s] = ld_row_operand(sQ, 32 * qb + l32, 16 * s + 8 * g);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 f32x16 pacc = {};
 #pragma unroll
-                for (int s = 0; s < MD / 16; ++s)
-                    pacc = mfma32(ld_row_operand(sK, 32 * qa + l32, 16 * s + 8 * g),
-                                  ld_row_operand(sQ, 32 * qb + l32, 16 * s + 8 * g), pacc);
+                for (int s = 0; s < MD / 16; ++s) pacc = mfma32(kr[s], qr[s], pacc);
                 const int t = 32 * qb + l32;
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
@@ -407,22 +440,41 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
         }
         // ---- phase 2: walk: V~^T P^T into O, state update, y staging
         if (comp) {
-            bf16x8 vop[MB / 16];  // V~^T operands, shared by both tiles and the state update
+            bf16x8 vop[MB / 16];     // V~^T operands, shared by both tiles and the state update
+            bf16x8 pb[MB / 16][2];   // P^T operands (tile tb = 0 needs s < 2 only)
+            bf16x8 ko[2][4];         // K~^T operands, half of the tokens at a time
 #pragma unroll
-            for (int s = 0; s < MB / 16; ++s) vop[s] = ld_tr_operand(sV, 16 * s, 32 * w, lane);
+            for (int s = 0; s < MB / 16; ++s) {
+                vop[s] = ld_tr_operand(sV, 16 * s, 32 * w, lane);
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+                    if (tb == 1 || s < 2)
+                        pb[s][tb] = *reinterpret_cast<const bf16x8*>(L.p + (32 * tb + l32) * PP + 16 * s + 8 * g);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) ko[s][m] = ld_tr_operand(sK, 16 * s, 32 * m, lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                for (int s = 0; s < MB / 16; ++s) {
-                    if (tb == 0 && s >= 2) continue;  // t < 32 sees only t' < 32
-                    const bf16x8 bb = *reinterpret_cast<const bf16x8*>(L.p + (32 * tb + l32) * PP + 16 * s + 8 * g);
-                    O[tb] = mfma32(vop[s], bb, O[tb]);
-                }
+                for (int s = 0; s < MB / 16; ++s)
+                    if (tb == 1 || s < 2)  // t < 32 sees only t' < 32
+                        O[tb] = mfma32(vop[s], pb[s][tb], O[tb]);
 #pragma unroll
-            for (int s = 0; s < MB / 16; ++s)
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    S[m] = mfma32(ld_tr_operand(sK, 16 * s, 32 * m, lane), vop[s], S[m]);
+                for (int m = 0; m < 4; ++m) S[m] = mfma32(ko[s][m], vop[s], S[m]);
+#pragma unroll
+            for (int s = 2; s < MB / 16; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) ko[s - 2][m] = ld_tr_operand(sK, 16 * s, 32 * m, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 2; s < MB / 16; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) S[m] = mfma32(ko[s - 2][m], vop[s], S[m]);
             // per-token sum of y^2 over this wave's 32 columns; y staged as bf16
             __bf16* ys = L.y[jc % YRING];
 #pragma unroll

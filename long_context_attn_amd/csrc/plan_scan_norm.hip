@@ -12,9 +12,10 @@ namespace la {
 
 // ------------------------------------------------------------------- plan
 // Workgroup 0 (1024 threads): chunk counts per sequence, exclusive scan,
-// then each thread writes the chunk records of its sequences.  The other
-// workgroups zero the words the single-pass MFMA prefill expects cleared on
-// every call (its chunk-state flags and RMSNorm exchange words).
+// then each thread writes the chunk records of its sequences (none when
+// `chunks` is null: the lane kernel only needs the count).  The other
+// workgroups zero the words the MFMA prefills expect cleared on every call
+// (chunk-state flags and RMSNorm exchange words).
 constexpr int PLAN_THREADS = 1024;
 constexpr int CLEAR_BLOCKS = 256;
 
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
         if (s < nseq) {
             segs[s].first = first;
             segs[s].count = cnt;
-            if (first + cnt <= max_chunks) {
+            if (chunks != nullptr && first + cnt <= max_chunks) {
                 for (int32_t c = 0; c < cnt; ++c) {
                     ChunkEntry e;
                     e.start = start + (int64_t)c * chunk;
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     }
     __shared__ int32_t err;
     if (tid == 0) {
-        err = bad ? 1 : (carry > max_chunks ? 2 : 0);
+        err = bad ? 1 : (chunks != nullptr && carry > max_chunks ? 2 : 0);
         hdr->error = err;
         hdr->n_chunks = err ? 0 : carry;
     }

@@ -68,10 +68,23 @@ def test_prefill_workspace_size(lib):
     slots = 9 * (1024 // 64)
     need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ws < need + 65536
-    # the automatic chunk length of this path is 2048 tokens
+    # the automatic choice is the single-pass chunked kernel at 2048-token chunks
     slots = (4 + 1) * (2048 // 64)
     need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ops.prefill_workspace_size(8192, 1, 64, 128, 64, 0) < need + 65536
+    need = 4 * 4 * 128 * 128 * 4 + 4 * 4 * 4 * 4 + slots * (4 * 64 * 8 + 1 * 64 * 8)
+    assert need <= ops.prefill_workspace_size(8192, 1, 4, 128, 64, 0) < need + 65536
+    # -1: the lane kernel (sequences walked whole, 64 x 4 lanes), whose workspace is the
+    # plan header, a record per sequence and three exchange rings of 16 slots of 8-byte
+    # words: 256 lanes x 64 tokens, 16 groups x 64 tokens, 64 totals
+    lane = 16 * (256 * 64 + 16 * 64 + 64) * 8
+    assert lane <= ops.prefill_workspace_size(8192, 1, 64, 128, 64, -1) < lane + 65536
+    lane4 = 16 * (16 * 64 + 1 * 64 + 64) * 8
+    assert lane4 <= ops.prefill_workspace_size(8192, 1, 4, 128, 64, -1) < lane4 + 65536
+    assert ops.prefill_workspace_size(8192, 1, 128, 128, 64, -1) == 0  # 512 lanes > CUs
+    assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, -1, dtype=torch.float32) == 0
+    assert ops.prefill_workspace_size(8192, 1, 64, 64, 64, -1) == 0     # head_dim 64
+    assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, -2) == 0
     ws32 = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024, dtype=torch.float32)
     assert 9 * 64 * 128 * 128 * 4 <= ws32 < 9 * 64 * 128 * 128 * 4 + 65536
     assert ops.prefill_workspace_size(8192, 1, 64, 96, 64, 0) == 0      # head_dim

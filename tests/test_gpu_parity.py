@@ -79,7 +79,10 @@ def test_bf16_ragged(D, block, dist):
     B, N, H = 2, 1000, 4
     q, k, v, g, w = inputs(B * N, H, D, dist, key=3)
     ref, st = oracle_prefill(q, k, v, g, w, B)
-    for chunk in (0, block, 4 * block):
+    # -1: the lane kernel (one workgroup per head and 32-column slice), for the
+    # shapes it supports; 0 picks the chunked kernel at 4 heads
+    chunks = (0, block, 4 * block) + ((-1,) if (D, block) == (128, 64) else ())
+    for chunk in chunks:
         say("bf16 D", D, "block", block, dist, "chunk", chunk)
         out, fs = run_prefill(q, k, v, g, w, B, torch.bfloat16, block, chunk)
         check(out, ref, torch.bfloat16, "bf16 D=%d block=%d %s chunk=%d" % (D, block, dist, chunk))
@@ -95,7 +98,8 @@ def test_varlen_packed(dtype, D, block):
     init = np.random.default_rng(5).standard_normal((len(lens), H, D, D)).astype(np.float32)
     ref, st = oracle.prefill(q, k, v, g, w, cu_seqlens=seg, init_state=init, return_state=True)
     cu = torch.from_numpy(seg.astype(np.int32)).cuda()
-    for chunk in (0, block, 2 * block):
+    chunks = (0, block, 2 * block) + ((-1,) if (dtype, D, block) == (torch.bfloat16, 128, 64) else ())
+    for chunk in chunks:
         say("varlen", dtype, "chunk", chunk)
         ws = torch.empty(la.prefill_workspace_size(T, len(lens), H, D, block, chunk, dtype),
                          dtype=torch.uint8, device="cuda")
@@ -134,13 +138,14 @@ def test_decode_steps(dtype, D, S):
         assert rel_state(host(state_gpu), state_ref) < 1e-6
 
 
-def test_decode_after_prefill_on_gpu():
+@pytest.mark.parametrize("chunk", [0, -1])
+def test_decode_after_prefill_on_gpu(chunk):
     """GPU prefill of L tokens then m GPU decode steps == GPU prefill of L+m."""
     H, D, L, m = 4, 128, 200, 3
     q, k, v, g, w = inputs(L + m, H, D, "unit", key=8)
     dt = torch.bfloat16
-    full, _ = run_prefill(q, k, v, g, w, 1, dt, 64)
-    _, st = run_prefill(q[:L], k[:L], v[:L], g[:L], w, 1, dt, 64)
+    full, _ = run_prefill(q, k, v, g, w, 1, dt, 64, chunk)
+    _, st = run_prefill(q[:L], k[:L], v[:L], g[:L], w, 1, dt, 64, chunk)
     st = st.contiguous()
     ref = oracle.prefill(q, k, v, g, w)
     for i in range(m):
@@ -163,7 +168,8 @@ def test_empty_and_repeatable():
     torch.cuda.synchronize()
     assert out.numel() == 0 and torch.equal(fs, init)
     q, k, v, g, w = inputs(777, H, D, "unit", key=9)
-    say("repeatability")
-    a, sa = run_prefill(q, k, v, g, w, 1, dt, 64)
-    b, sb = run_prefill(q, k, v, g, w, 1, dt, 64)
-    assert torch.equal(a, b) and torch.equal(sa, sb)
+    for chunk in (0, -1):
+        say("repeatability, chunk", chunk)
+        a, sa = run_prefill(q, k, v, g, w, 1, dt, 64, chunk)
+        b, sb = run_prefill(q, k, v, g, w, 1, dt, 64, chunk)
+        assert torch.equal(a, b) and torch.equal(sa, sb)
