@@ -17,9 +17,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Chunk length when the caller leaves it to the library: the longest power
 // of two (up to 8192 tokens) that still gives about 256 (chunk, head) work
-// items, one per CU.  The walk holds one workgroup per CU, and every chunk
-// costs a D*D*4-byte state per head that is written, scanned and read back,
-// so fewer, longer chunks are cheaper as long as the CUs stay busy.
+// items, one per CU.  Both prefill paths hold one workgroup per CU, and
+// every chunk costs a D*D*4-byte state per head that is handed on, so fewer,
+// longer chunks are cheaper as long as the CUs stay busy.
 int auto_chunk(int64_t total, int nseq, int heads, int block) {
     const int64_t target_items = 256;
     int64_t per = total * heads / target_items;
@@ -92,10 +92,11 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
         return true;
     }
     int chunk = chunk_tokens;
-    // The single-pass MFMA kernel reads K and V of every chunk but a
-    // sequence's last one twice (state pass, then walk); 2048-token chunks
-    // measured fastest at 8192 tokens x 64 heads (one item per CU).
-    if (chunk == 0) chunk = fused ? 2048 : auto_chunk(total, nseq, heads, block);
+    // Both paths: about one (chunk, head) item per CU.  For the single-pass
+    // MFMA kernel that is 2048-token chunks at 8192 tokens x 64 heads, the
+    // fastest measured there; at 1M tokens longer chunks (8192) spread the
+    // per-item fill and drain over more blocks.
+    if (chunk == 0) chunk = auto_chunk(total, nseq, heads, block);
     if (chunk < block || chunk % block != 0) return false;
     const int64_t maxc = total / chunk + nseq;  // >= sum over sequences of ceil(L_s / chunk)
     // work-item tickets (chunk items + one per sequence) are 32-bit

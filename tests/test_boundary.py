@@ -68,10 +68,12 @@ def test_prefill_workspace_size(lib):
     slots = 9 * (1024 // 64)
     need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ws < need + 65536
-    # the automatic choice is the single-pass chunked kernel at 2048-token chunks
+    # the automatic choice is the single-pass chunked kernel with about 256 (chunk, head)
+    # items: 2048-token chunks for 64 heads, 128-token chunks for 4 heads
     slots = (4 + 1) * (2048 // 64)
     need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ops.prefill_workspace_size(8192, 1, 64, 128, 64, 0) < need + 65536
+    slots = (64 + 1) * (128 // 64)
     need = 4 * 4 * 128 * 128 * 4 + 4 * 4 * 4 * 4 + slots * (4 * 64 * 8 + 1 * 64 * 8)
     assert need <= ops.prefill_workspace_size(8192, 1, 4, 128, 64, 0) < need + 65536
     # -1: the lane kernel (sequences walked whole, 64 x 4 lanes), whose workspace is the
