@@ -66,9 +66,14 @@ LA_API const char* lightning_attn_status_string(la_status s);
  *
  * chunk_tokens: the sequence is cut into chunks of this many tokens that are
  * processed in parallel (the running state entering each chunk is an
- * exclusive prefix sum of per-chunk states).  0 lets the library choose; a
- * nonzero value must be a multiple of `block`.  The result does not depend on
- * it beyond rounding.
+ * exclusive prefix sum of per-chunk states).  0 lets the library choose (about
+ * one (chunk, head) work item per compute unit, at most 8192 tokens); a
+ * positive value must be a multiple of `block`.  -1 asks the MFMA path not to
+ * cut sequences at all: one workgroup per (head, 32-column slice of the
+ * state) walks each sequence whole, which needs heads * 4 <= the device's
+ * compute units and bf16 with head_dim 128 and block 64 (else the workspace
+ * size is 0 and the call returns LA_ERR_UNSUPPORTED).  The result does not
+ * depend on it beyond rounding.
  *
  * Workspace bytes needed by a prefill over `total_tokens` tokens in `nseq`
  * sequences (a batch of B rows of N tokens is nseq = B, total = B*N).
