@@ -173,3 +173,27 @@ def test_empty_and_repeatable():
         a, sa = run_prefill(q, k, v, g, w, 1, dt, 64, chunk)
         b, sb = run_prefill(q, k, v, g, w, 1, dt, 64, chunk)
         assert torch.equal(a, b) and torch.equal(sa, sb)
+
+
+@pytest.mark.parametrize("chunk", [0, -1])
+def test_invalid_cu_seqlens_reported(chunk):
+    """cu_seqlens that does not end at total_tokens: the plan records error 1 in
+    the workspace header, the launch finishes, and a valid call on the same
+    workspace afterwards is correct again."""
+    H, D, T = 4, 128, 300
+    q, k, v, g, w = inputs(T, H, D, "unit", key=11)
+    dt = torch.bfloat16
+    args = [dev(a, dt) for a in (q, k, v, g, w)]
+    bad = torch.tensor([0, 100, 250], dtype=torch.int32, device="cuda")  # ends at 250, not 300
+    ws = torch.empty(la.prefill_workspace_size(T, 2, H, D, 64, chunk, dt), dtype=torch.uint8,
+                     device="cuda")
+    say("invalid cu_seqlens, chunk", chunk)
+    la.prefill_varlen(*args, bad, chunk_tokens=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    assert plan_error(ws) == 1
+    good = torch.tensor([0, 100, 300], dtype=torch.int32, device="cuda")
+    out = la.prefill_varlen(*args, good, chunk_tokens=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    assert plan_error(ws) == 0
+    ref = oracle.prefill(q, k, v, g, w, cu_seqlens=np.array([0, 100, 300]))
+    check(out, ref, dt, "after an invalid call, chunk %d" % chunk)

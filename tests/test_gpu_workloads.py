@@ -4,12 +4,14 @@ Every test runs the library at the workload's real shape and in the launch
 configuration bench.py times (the library's automatic chunk length), then
 compares what the fp64 oracle can compute in seconds:
 
-  * prefill, 8192 tokens x 64 heads: every output and the final state;
+  * prefill, 8192 tokens x 64 heads: every output and the final state, for the
+    automatic configuration and for the lane kernel;
   * decode, 256 sequences x 64 heads, 64 steps: each step's outputs and the
     final states of four seeded sequences whose initial states the oracle
     built from their seeded prefixes;
   * varlen, 1,048,576 packed tokens: every output and final state of three
-    seeded sequences of at most 8192 tokens, packed among the others;
+    seeded sequences of at most 8192 tokens, packed among the others (also
+    for the lane kernel);
   * one sequence of 1,048,576 tokens: the first 2048 outputs; the state after
     1,047,552 tokens on four seeded heads; the last 1024 outputs, which the
     oracle computes from the GPU's state after 1,047,552 tokens (the four
@@ -65,17 +67,23 @@ def put(dst, rows, heads, x):
 
 
 def test_prefill_8k_workload():
+    """The automatic configuration bench.py times, and the lane kernel (sequences
+    walked whole, chunk_tokens = -1), both against the oracle."""
     N = 8192
     q, k, v, g, w = synth.layer_inputs(synth.PREFILL_8K, N, H, D, "minimax", threads=THREADS)
     say("prefill 8K: inputs ready")
-    out, fs = la.prefill(*(dev(a, BF16).view(1, N, H, D) for a in (q, k, v, g)), dev(w, BF16),
-                         return_final_state=True)
-    torch.cuda.synchronize()
+    args = [dev(a, BF16).view(1, N, H, D) for a in (q, k, v, g)] + [dev(w, BF16)]
+    runs = {}
+    for chunk in (0, -1):
+        say("prefill 8K: chunk_tokens", chunk)
+        runs[chunk] = la.prefill(*args, return_final_state=True, chunk_tokens=chunk)
+        torch.cuda.synchronize()
     ref, st = oracle.prefill(q, k, v, g, w, return_state=True)
-    check(host(out).reshape(N, H, D), ref, BF16, "prefill 8K x 64 heads")
-    err = rel_state(host(fs), st)
-    say("prefill 8K final state rel err %.2e" % err)
-    assert err < STATE_TOL
+    for chunk, (out, fs) in runs.items():
+        check(host(out).reshape(N, H, D), ref, BF16, "prefill 8K x 64 heads, chunk_tokens %d" % chunk)
+        err = rel_state(host(fs), st)
+        say("prefill 8K chunk_tokens %d final state rel err %.2e" % (chunk, err))
+        assert err < STATE_TOL
 
 
 @pytest.mark.slow
@@ -134,7 +142,13 @@ def test_varlen_1m_workload():
     cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
     out, fs = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True)
     torch.cuda.synchronize()
-    del q, k, v, g
+    # the lane kernel on the same pack: only the sampled sequences are kept
+    say("varlen: lane kernel (chunk_tokens -1)")
+    out_l, fs_l = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True,
+                                    chunk_tokens=-1)
+    torch.cuda.synchronize()
+    lane = {s: (host(out_l[int(cu[s]):int(cu[s + 1])]), host(fs_l[s:s + 1])) for s in picks}
+    del q, k, v, g, out_l, fs_l
     wh = np.ones(H * D, np.float32)
     for s in picks:
         a, b = int(cu[s]), int(cu[s + 1])
@@ -143,6 +157,8 @@ def test_varlen_1m_workload():
         err = rel_state(host(fs[s:s + 1]), st)
         say("varlen sequence %d final state rel err %.2e" % (s, err))
         assert err < STATE_TOL
+        check(lane[s][0], ref, BF16, "varlen sequence %d, lane kernel" % s)
+        assert rel_state(lane[s][1], st) < STATE_TOL
 
 
 @pytest.mark.slow
