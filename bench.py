@@ -200,7 +200,27 @@ def bench_prefill(args, la, torch, hip):
         inputs=(q, k, v, g, w))
     log("prefill: %.1f us/step, %.2f M tok/s, %.1f TFLOP/s, kernels %s" %
         (ms * 1e3, tok_s / 1e6, res["tflops"], res["kernels_us"]))
-    del qd, kd, vd, gd, out, ws
+    # state-only pass (first pass of a prefill split along the sequence) on the
+    # same k, v: reads k and v once, writes one state per (chunk, head)
+    sws = torch.empty(la.state_workspace_size(B * N, B, H, D, blk, 0), dtype=torch.uint8,
+                      device=dev)
+    fs = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    scall = lambda: la.state(kd, vd, block=blk, final_state=fs, workspace=sws)
+    for _ in range(3):
+        scall()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        scall()
+    e1.record()
+    torch.cuda.synchronize()
+    s_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    kv_bytes = 2 * tokens * H * D * 2
+    res["state_only"] = dict(us_per_call=round(s_us, 2),
+                             kv_GBps=round(kv_bytes / (s_us * 1e-6) / 1e9, 1),
+                             kv_hbm_frac=round(kv_bytes / (s_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    log("state-only pass: %.1f us/call, k+v at %.0f GB/s" % (s_us, res["state_only"]["kv_GBps"]))
+    del qd, kd, vd, gd, out, ws, sws, fs
     return res
 
 
@@ -442,6 +462,7 @@ def main():
         "layer_hbm_frac": round(pre["layer_hbm_frac"], 4),
         "kernels_us": pre["kernels_us"],
         "roofline": pre["roofline"],
+        "state_only": pre["state_only"],
         "decode": dec,
         "long_context": long_ctx,
         "cpu_baseline": cpu,

@@ -116,6 +116,40 @@ LA_API la_status lightning_attn_prefill_varlen(const void* q, const void* k, con
                                         la_dtype dtype, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/*
+ * Final states only: for each sequence, initial_state (or zeros) plus the sum
+ * over its tokens of k~^T v~ -- the running state of Mechanism step 3 after
+ * the sequence's last token -- without computing any output.  This is the
+ * first pass of a prefill split along the sequence (the sequence-parallel
+ * scheme the MiniMax-Text-01 summary page lists as LASP+): every part's state
+ * sum, then an exclusive prefix over the parts (by the caller), then
+ * lightning_attn_prefill of each part with its prefix as initial_state.
+ * q, gate and the norm weight are not read.
+ *   k, v:          [batch][seqlen][heads][head_dim], or packed [total][heads]
+ *                  [head_dim] with device cu_seqlens int32 [nseq+1] (as for
+ *                  lightning_attn_prefill_varlen)
+ *   initial_state: [nseq][heads][head_dim][head_dim] fp32, or NULL (zeros)
+ *   final_state:   same shape, required; may alias initial_state
+ * chunk_tokens: as for the prefill (0 = automatic); negative values return
+ * LA_ERR_BAD_SHAPE.
+ * Shapes, dtypes and errors as for the prefill.
+ */
+LA_API size_t lightning_attn_state_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                                  int head_dim, int block, int chunk_tokens,
+                                                  la_dtype dtype);
+LA_API la_status lightning_attn_state(const void* k, const void* v, const float* initial_state,
+                                      float* final_state, int batch, int64_t seqlen, int heads,
+                                      int head_dim, int block, int chunk_tokens, la_dtype dtype,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+LA_API la_status lightning_attn_state_varlen(const void* k, const void* v,
+                                             const int32_t* cu_seqlens, int nseq,
+                                             int64_t total_tokens, const float* initial_state,
+                                             float* final_state, int heads, int head_dim,
+                                             int block, int chunk_tokens, la_dtype dtype,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+
 /* Workspace bytes needed by lightning_attn_decode. */
 LA_API size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim);
 

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning_attn.so")
-SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "lane.hip", "decode.hip"]
+SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "lane.hip", "state_mfma.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 
 

@@ -370,6 +370,108 @@ la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void
     return run_prefill(a, L, workspace, stream);
 }
 
+size_t lightning_attn_state_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                           int head_dim, int block, int chunk_tokens,
+                                           la_dtype dtype) {
+    if (check_dtype(dtype) != LA_OK || chunk_tokens < 0) return 0;
+    Layout L;
+    if (!plan_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, false, &L)) return 0;
+    return L.bytes;
+}
+
+// State-only pass: plan, per-chunk sums of k~^T v~, then the scan, which
+// writes initial state + all chunk sums of each sequence as its final state.
+static la_status run_state(la::PrefillArgs& a, const Layout& L, void* workspace,
+                           hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    a.chunk = L.chunk;
+    a.max_chunks = L.max_chunks;
+    a.hdr = reinterpret_cast<la::PlanHeader*>(ws);
+    a.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
+    a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
+    a.states = reinterpret_cast<float*>(ws + L.off_states);
+    a.clear = nullptr;
+    a.clear_words = 0;
+    hipError_t e = la::launch_plan(a, stream);
+    if (e == hipSuccess)
+        e = la::state_mfma_supported(a) ? la::launch_chunk_state_mfma(a, stream)
+                                        : la::launch_chunk_state_valu(a, stream);
+    if (e == hipSuccess) e = la::launch_state_scan(a, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+static la_status state_checks(const void* k, const void* v, const float* initial_state,
+                              float* final_state, int64_t total, int nseq, int heads,
+                              int head_dim, int block, int chunk_tokens, la_dtype dtype,
+                              void* workspace, size_t workspace_bytes, Layout* L) {
+    if (heads < 1 || chunk_tokens < 0) return LA_ERR_BAD_SHAPE;
+    if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
+        return LA_ERR_UNSUPPORTED;
+    if (total > 0) {
+        if (!k || !v) return LA_ERR_NULL_POINTER;
+        if (!aligned16(k) || !aligned16(v)) return LA_ERR_MISALIGNED;
+    }
+    if (nseq > 0 && !final_state) return LA_ERR_NULL_POINTER;
+    if (final_state && !aligned16(final_state)) return LA_ERR_MISALIGNED;
+    if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
+    if (!plan_layout(total, nseq, heads, head_dim, block, chunk_tokens, false, L))
+        return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L->bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    return LA_OK;
+}
+
+la_status lightning_attn_state(const void* k, const void* v, const float* initial_state,
+                               float* final_state, int batch, int64_t seqlen, int heads,
+                               int head_dim, int block, int chunk_tokens, la_dtype dtype,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (batch < 0 || seqlen < 0) return LA_ERR_BAD_SHAPE;
+    if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
+    const int64_t total = (int64_t)batch * seqlen;
+    Layout L;
+    la_status s = state_checks(k, v, initial_state, final_state, total, batch, heads, head_dim,
+                               block, chunk_tokens, dtype, workspace, workspace_bytes, &L);
+    if (s != LA_OK || batch == 0) return s;
+    la::PrefillArgs a{};
+    a.k = k; a.v = v;
+    a.init_state = initial_state;
+    a.final_state = final_state;
+    a.cu = nullptr;
+    a.nseq = batch;
+    a.seqlen = seqlen;
+    a.total = total;
+    a.H = heads; a.D = head_dim; a.block = block;
+    a.bf16 = dtype == LA_DTYPE_BF16;
+    return run_state(a, L, workspace, stream);
+}
+
+la_status lightning_attn_state_varlen(const void* k, const void* v, const int32_t* cu_seqlens,
+                                      int nseq, int64_t total_tokens, const float* initial_state,
+                                      float* final_state, int heads, int head_dim, int block,
+                                      int chunk_tokens, la_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    if (nseq < 0 || total_tokens < 0 || total_tokens > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
+    if (nseq == 0 && total_tokens != 0) return LA_ERR_BAD_SHAPE;
+    if (nseq > 0 && !cu_seqlens) return LA_ERR_NULL_POINTER;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return LA_ERR_MISALIGNED;
+    Layout L;
+    la_status s = state_checks(k, v, initial_state, final_state, total_tokens, nseq, heads,
+                               head_dim, block, chunk_tokens, dtype, workspace, workspace_bytes, &L);
+    if (s != LA_OK || nseq == 0) return s;
+    la::PrefillArgs a{};
+    a.k = k; a.v = v;
+    a.init_state = initial_state;
+    a.final_state = final_state;
+    a.cu = cu_seqlens;
+    a.nseq = nseq;
+    a.seqlen = 0;
+    a.total = total_tokens;
+    a.H = heads; a.D = head_dim; a.block = block;
+    a.bf16 = dtype == LA_DTYPE_BF16;
+    return run_state(a, L, workspace, stream);
+}
+
 size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {
     if (nseq < 0 || heads < 1 || !supported_dim(head_dim)) return 0;
     return align_up(sizeof(float) * (size_t)nseq * heads * head_dim) +

@@ -106,6 +106,9 @@ hipError_t launch_walk_valu(const PrefillArgs& a, hipStream_t st);
 bool mfma_supported(const PrefillArgs& a);
 int prefill_mfma_ring_slots();
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
+// bf16 MFMA chunk states (D = 128, block = 64), the state-only pass
+bool state_mfma_supported(const PrefillArgs& a);
+hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
 // lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,
 // 32-column state slice) walks every sequence whole; needs heads * 4 <= cus
 // (all lanes resident at once).  The plan runs first with chunk = 64 and no

@@ -1,0 +1,123 @@
+// Chunk states of the Lightning Attention layer on bf16 MFMA for gfx950
+// (head_dim 128, 64-token blocks, fp32 accumulation):
+//   states[c][h][dk][dv] = sum over chunk c's tokens t of k~_t[dk] v~_t[dv],
+// k~ = SiLU(k), v~ = SiLU(v) -- the running-state sum of Mechanism step 3 of
+// "Diving into MiniMax01 405B MoE" (section "Hybrid Modeling") over one chunk.
+// With the prefix scan over a sequence's chunks (plan_scan_norm.hip) it gives
+// each sequence's final state without the walk: the first pass of a prefill
+// split along the sequence, whose second pass is a prefill started from the
+// prefix of the preceding parts' states.
+#include "mfma_common.h"
+
+namespace la {
+
+namespace {
+
+constexpr int ST_THREADS = 512;  // 8 waves, all of which load, apply SiLU and multiply
+constexpr int SPF = 4;           // blocks in flight per thread (register sets)
+
+struct StateLds {
+    __bf16 k[2][TILE];
+    __bf16 v[2][TILE];
+};
+
+// One workgroup per (chunk, head).  Thread t loads rows t / 16 and t / 16 + 32
+// of a block, features 8 (t % 16) .. + 7, applies SiLU and writes the swizzled
+// bf16 tiles; wave w accumulates the state tiles dk in [64 (w / 4), +64),
+// dv in [32 (w % 4), +32).  Every wave takes part in the SiLU: it is a chain
+// of dependent transcendental operations, and two waves per SIMD hide its
+// latency where one could not.
+__global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const PlanHeader* __restrict__ hdr, const ChunkEntry* __restrict__ chunks,
+    float* __restrict__ states, int H) {
+    __shared__ __attribute__((aligned(16))) StateLds L;
+    const int nch = hdr->n_chunks;
+    const int c = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    if (c >= nch) return;
+    const ChunkEntry ce = chunks[c];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int HD = H * MD;
+    const int64_t off0 = ce.start * (int64_t)HD + (int64_t)h * MD;
+    const int nblk = (ce.len + MB - 1) / MB;
+    const int cc = tid & 15, rg = tid >> 4;
+    const int voff = (rg * HD + 8 * cc) * 2, rstride = 32 * HD * 2;
+    // Block b is loaded into register set b % SPF, SPF blocks ahead.  Loads
+    // are issued unconditionally (blocks past the chunk's end get an empty
+    // range and return zeros): a conditional load would make the compiler
+    // copy registers that still have a load in flight.
+    struct Rows {
+        bf16x8 r[2];
+    };
+    Rows tk[SPF], tv[SPF];
+    auto load_rows = [&](const __bf16* base, int b, Rows& t) {
+        const int t0 = b * MB, n = max(0, min(MB, ce.len - t0));
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base + off0 + (int64_t)t0 * HD, n, HD);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            t.r[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * rstride, 0));
+    };
+#pragma unroll
+    for (int i = 0; i < SPF; ++i) {
+        load_rows(k, i, tk[i]);
+        load_rows(v, i, tv[i]);
+    }
+    const int l32 = lane & 31, g = lane >> 5;
+    const int n = w & 3, m0 = 2 * (w >> 2);
+    f32x16 acc[2] = {};
+    // One barrier per block with two LDS buffers: a wave writes buffer b & 1
+    // only after passing block b - 1's barrier, which every wave reaches only
+    // after its products of block b - 2 (the same buffer).
+    for (int b0 = 0; b0 < nblk; b0 += SPF) {
+#pragma unroll
+        for (int i = 0; i < SPF; ++i) {
+            const int b = b0 + i;
+            if (b >= nblk) break;
+            __bf16* sK = L.k[b & 1];
+            __bf16* sV = L.v[b & 1];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                *reinterpret_cast<bf16x8*>(sK + swz(rg + 32 * j, 8 * cc)) = silu8(tk[i].r[j]);
+                *reinterpret_cast<bf16x8*>(sV + swz(rg + 32 * j, 8 * cc)) = silu8(tv[i].r[j]);
+            }
+            load_rows(k, b + SPF, tk[i]);
+            load_rows(v, b + SPF, tv[i]);
+            __syncthreads();
+            // all operands in flight before the products
+            bf16x8 vb[MB / 16], ka[MB / 16][2];
+#pragma unroll
+            for (int s = 0; s < MB / 16; ++s) {
+                vb[s] = ld_tr_operand(sV, 16 * s, 32 * n, lane);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) ka[s][j] = ld_tr_operand(sK, 16 * s, 32 * (m0 + j), lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < MB / 16; ++s)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[j] = mfma32(ka[s][j], vb[s], acc[j]);
+        }
+    }
+    float* dst = states + ((int64_t)c * H + h) * MD * MD;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int dk = 32 * (m0 + j) + 8 * (r >> 2) + 4 * g + (r & 3);
+            dst[dk * MD + 32 * n + l32] = acc[j][r];
+        }
+}
+
+}  // namespace
+
+bool state_mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.block == MB; }
+
+hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st) {
+    if (a.max_chunks == 0) return hipSuccess;
+    const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H));
+    hipLaunchKernelGGL(chunk_state_mfma_kernel, grid, dim3(ST_THREADS), 0, st, (const __bf16*)a.k,
+                       (const __bf16*)a.v, a.hdr, a.chunks, a.states, a.H);
+    return hipGetLastError();
+}
+
+}  // namespace la

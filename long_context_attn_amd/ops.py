@@ -6,6 +6,7 @@ include/lightning_attn.h:
 
     prefill(q, k, v, gate, weight, ...)            q: [B, N, H, D]
     prefill_varlen(q, k, v, gate, weight, cu, ...) q: [T, H, D], cu: int32 [nseq+1]
+    state(k, v, ...) / state_varlen(k, v, cu, ...) final states only, [nseq, H, D, D]
     decode(q, k, v, gate, weight, state, ...)      q: [S, H, D], state updated in place
 
 The layer is the Lightning Attention Mechanism of "Diving into MiniMax01 405B
@@ -56,6 +57,14 @@ def library():
         lib.lightning_attn_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _P,
                                                       _P, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]
         lib.lightning_attn_prefill_varlen.restype = _I
+        lib.lightning_attn_state_workspace_size.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        lib.lightning_attn_state_workspace_size.restype = _SZ
+        lib.lightning_attn_state.argtypes = [_P, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _P, _SZ,
+                                             _P]
+        lib.lightning_attn_state.restype = _I
+        lib.lightning_attn_state_varlen.argtypes = [_P, _P, _P, _I, _I64, _P, _P, _I, _I, _I, _I,
+                                                    _I, _P, _SZ, _P]
+        lib.lightning_attn_state_varlen.restype = _I
         lib.lightning_attn_decode_workspace_size.argtypes = [_I, _I, _I]
         lib.lightning_attn_decode_workspace_size.restype = _SZ
         lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
@@ -198,6 +207,65 @@ def prefill_varlen(q, k, v, gate, weight, cu_seqlens, *, block=64, eps=1e-6, ini
         T, _ptr(init), _ptr(fs), H, D, int(block), int(chunk_tokens), float(eps), _dtype(q),
         _ptr(ws), ws_bytes, _stream(dev)))
     return (out, fs) if return_final_state else out
+
+
+def state_workspace_size(total_tokens, nseq, heads, head_dim, block=64, chunk_tokens=0,
+                         dtype=torch.bfloat16) -> int:
+    return int(library().lightning_attn_state_workspace_size(
+        int(total_tokens), int(nseq), int(heads), int(head_dim), int(block), int(chunk_tokens),
+        LA_DTYPE[dtype]))
+
+
+def state(k, v, *, block=64, initial_state=None, final_state=None, chunk_tokens=0,
+          workspace=None):
+    """Final states of B rows of N tokens without outputs: initial_state (or zeros)
+    + sum_t SiLU(k_t)^T SiLU(v_t).  k, v: [B, N, H, D]; returns [B, H, D, D] fp32."""
+    _same(k, v)
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k, v must share one [B, N, H, D] shape")
+    B, N, H, D = k.shape
+    dev = k.device
+    init = _state(initial_state, (B, H, D, D), dev, "initial_state")
+    fs = final_state if final_state is not None else torch.empty(B, H, D, D, dtype=torch.float32,
+                                                                device=dev)
+    _state(fs, (B, H, D, D), dev, "final_state")
+    ws_bytes = state_workspace_size(B * N, B, H, D, block, chunk_tokens, k.dtype)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_state(
+        _ptr(k), _ptr(v), _ptr(init), _ptr(fs), B, N, H, D, int(block), int(chunk_tokens),
+        _dtype(k), _ptr(ws), ws_bytes, _stream(dev)))
+    return fs
+
+
+def state_varlen(k, v, cu_seqlens, *, block=64, initial_state=None, final_state=None,
+                 chunk_tokens=0, workspace=None):
+    """Final states of packed sequences without outputs.  k, v: [T, H, D];
+    cu_seqlens: int32 [nseq+1] on the same device; returns [nseq, H, D, D] fp32."""
+    _same(k, v)
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k, v must share one [T, H, D] shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != k.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector on the activations' device")
+    T, H, D = k.shape
+    nseq = cu_seqlens.numel() - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    dev = k.device
+    init = _state(initial_state, (nseq, H, D, D), dev, "initial_state")
+    fs = final_state if final_state is not None else torch.empty(nseq, H, D, D,
+                                                                dtype=torch.float32, device=dev)
+    _state(fs, (nseq, H, D, D), dev, "final_state")
+    ws_bytes = state_workspace_size(T, nseq, H, D, block, chunk_tokens, k.dtype)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_state_varlen(
+        _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, T, _ptr(init), _ptr(fs), H, D, int(block),
+        int(chunk_tokens), _dtype(k), _ptr(ws), ws_bytes, _stream(dev)))
+    return fs
 
 
 def decode(q, k, v, gate, weight, state, *, eps=1e-6, out=None, workspace=None):

@@ -36,9 +36,11 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("lightning_attn_prefill", "lightning_attn_prefill_varlen", "lightning_attn_decode"):
         assert n in names
-    for n in ("lightning_attn_prefill_profiled", "lightning_attn_decode_profiled"):
+    for n in ("lightning_attn_prefill_profiled", "lightning_attn_decode_profiled",
+              "lightning_attn_state", "lightning_attn_state_varlen",
+              "lightning_attn_state_workspace_size"):
         assert n in names
-    assert len(names) == 12
+    assert len(names) == 15
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -142,6 +144,52 @@ def test_varlen_validation(lib):
     assert call(d=48) == UNSUP
     assert call(ws_bytes=64) == WS
     assert call(nseq=0, total=0, q=None, cu=None) == OK
+
+
+def test_state_workspace_size(lib):
+    # the plan and one fp32 state per (chunk, head)
+    for args in ((8192, 1, 64, 128, 64, 0), (1000, 3, 2, 64, 32, 64)):
+        assert ops.state_workspace_size(*args) > 0
+    assert ops.state_workspace_size(1000, 3, 2, 64, 32, 64) >= (1000 // 64 + 3) * 2 * 64 * 64 * 4
+    st = ops.state_workspace_size(8192, 1, 64, 128, 64, 1024)
+    # room for total / chunk + nseq chunks (a sequence's last chunk may be partial)
+    assert 9 * 64 * 128 * 128 * 4 <= st < 9 * 64 * 128 * 128 * 4 + 65536
+    assert ops.state_workspace_size(8192, 1, 64, 128, 64, -1) == 0  # no lane variant
+    assert ops.state_workspace_size(8192, 1, 64, 96, 64, 0) == 0
+    assert ops.state_workspace_size(8192, 1, 64, 128, 64, 100) == 0
+    assert ops.state_workspace_size(0, 0, 64, 128, 64, 0) > 0
+
+
+def test_state_validation(lib):
+    def call(k=A, v=A, init=None, fin=A, batch=2, seqlen=100, heads=2, d=64, block=32, chunk=0,
+             dtype=BF16, ws=A, ws_bytes=1 << 40):
+        return lib.lightning_attn_state(k, v, init, fin, batch, seqlen, heads, d, block, chunk,
+                                        dtype, ws, ws_bytes, None)
+    assert call(k=None) == NULLP
+    assert call(fin=None) == NULLP          # the final state is the only output
+    assert call(ws=None) == NULLP
+    assert call(v=A + 8) == MISAL
+    assert call(init=A + 4) == MISAL
+    assert call(fin=A + 4) == MISAL
+    assert call(d=96) == UNSUP
+    assert call(block=48) == UNSUP
+    assert call(dtype=3) == UNSUP
+    assert call(chunk=-1) == SHAPE
+    assert call(batch=-1) == SHAPE
+    assert call(heads=0) == SHAPE
+    assert call(ws_bytes=100) == WS
+    assert call(batch=0, k=None, v=None, fin=None) == OK
+
+    def vcall(k=A, cu=A, nseq=2, total=100, fin=A, ws_bytes=1 << 40):
+        return lib.lightning_attn_state_varlen(k, A, cu, nseq, total, None, fin, 2, 64, 32, 0, F32,
+                                               A, ws_bytes, None)
+    assert vcall(cu=None) == NULLP
+    assert vcall(fin=None) == NULLP
+    assert vcall(cu=A + 2) == MISAL
+    assert vcall(nseq=0, total=10) == SHAPE
+    assert vcall(total=1 << 31) == SHAPE
+    assert vcall(ws_bytes=8) == WS
+    assert vcall(nseq=0, total=0, k=None, cu=None, fin=None) == OK
 
 
 def test_decode_validation(lib):

@@ -5,7 +5,8 @@ configuration bench.py times (the library's automatic chunk length), then
 compares what the fp64 oracle can compute in seconds:
 
   * prefill, 8192 tokens x 64 heads: every output and the final state, for the
-    automatic configuration and for the lane kernel;
+    automatic configuration and for the lane kernel; the state-only pass's
+    final state;
   * decode, 256 sequences x 64 heads, 64 steps: each step's outputs and the
     final states of four seeded sequences whose initial states the oracle
     built from their seeded prefixes;
@@ -78,12 +79,18 @@ def test_prefill_8k_workload():
         say("prefill 8K: chunk_tokens", chunk)
         runs[chunk] = la.prefill(*args, return_final_state=True, chunk_tokens=chunk)
         torch.cuda.synchronize()
+    say("prefill 8K: state-only pass")
+    fs_only = la.state(args[1], args[2])
+    torch.cuda.synchronize()
     ref, st = oracle.prefill(q, k, v, g, w, return_state=True)
     for chunk, (out, fs) in runs.items():
         check(host(out).reshape(N, H, D), ref, BF16, "prefill 8K x 64 heads, chunk_tokens %d" % chunk)
         err = rel_state(host(fs), st)
         say("prefill 8K chunk_tokens %d final state rel err %.2e" % (chunk, err))
         assert err < STATE_TOL
+    err = rel_state(host(fs_only), st)
+    say("state-only 8K x 64 heads: final state rel err %.2e" % err)
+    assert err < STATE_TOL
 
 
 @pytest.mark.slow
