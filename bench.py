@@ -10,11 +10,13 @@ gate ~ N(0,1), norm weight ~ N(1, 0.02), eps 1e-6 -- the whole layer: SiLU on
 q/k/v, causal Y = Q(K^T V) against the running fp32 state, RMSNorm(Y) *
 sigmoid(gate).  Inputs are synthetic (seeded), resident in HBM before timing.
 
-value = prefill tokens/s.  Also reported: TFLOP/s on the block-tiled FLOP
+value = prefill tokens/s, in steady state: the warm-up (default 200 calls,
+about 45 ms) lets the clocks settle first; the first few dozen calls on an
+idle GPU run ~20% slower.  Also reported: TFLOP/s on the block-tiled FLOP
 count, the per-kernel split (HIP events recorded between the library's
-kernels on the stream they run on: the plan, then the single-pass kernel that
-does the state pass, the chunk-state hand-over, the walk and the RMSNorm), the
-roofline of that kernel, the
+kernels on the stream they run on: the plan, the chunk sums, the scan of the
+states entering the chunks, and the walk with the RMSNorm fused), the
+roofline of the walk kernel, the state-only pass on the same K and V, the
 decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
 as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores.
@@ -54,9 +56,9 @@ def layer_bytes_per_token(H, D, elem=2):
 
 
 def walk_bytes_per_token(H, D, elem=2):
-    """Algorithmic bytes of the single-pass prefill kernel per token: read q, k, v,
-    gate; write out.  (Its state pass reads K and V of every chunk but a sequence's
-    last one a second time; those re-reads are traffic, not algorithmic bytes.)"""
+    """Algorithmic bytes of the walk kernel per token: read q, k, v, gate; write
+    out.  (The chunk-sum kernel before it reads K and V of every chunk but a
+    sequence's last one a first time: traffic of the layer, not of the walk.)"""
     return 5 * H * D * elem
 
 
@@ -189,9 +191,11 @@ def bench_prefill(args, la, torch, hip):
     res = dict(
         ms_per_step=ms, tokens_per_s=tok_s, tflops=fl / (ms * 1e-3) / 1e12,
         layer_hbm_frac=layer_bytes_per_token(H, D) * tokens / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        # the single-pass kernel runs between the "walk" marks; the marks of the
-        # portable path's other kernels stay empty on this path
-        kernels_us={"plan": round(per["plan"] * 1e3, 2),
+        # stage marks: plan, chunk_state (chunk sums), state_scan, walk (the
+        # walk kernel with the RMSNorm fused; the norm_gate mark stays empty)
+        kernels_us={"plan_kernel": round(per["plan"] * 1e3, 2),
+                    "chunk_state_mfma_kernel": round(per["chunk_state"] * 1e3, 2),
+                    "state_scan_kernel": round(per["state_scan"] * 1e3, 2),
                     "prefill_mfma_kernel": round(per["walk"] * 1e3, 2)},
         roofline=dict(kernel="prefill_mfma_kernel", bound="hbm", achieved=round(achieved, 1),
                       peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
@@ -407,8 +411,8 @@ def cpu_baseline(inputs, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-long", action="store_true", help="skip the 1M-token workloads")

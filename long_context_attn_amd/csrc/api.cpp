@@ -17,9 +17,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Chunk length when the caller leaves it to the library: the longest power
 // of two (up to 8192 tokens) that still gives about 256 (chunk, head) work
-// items, one per CU.  Both prefill paths hold one workgroup per CU, and
-// every chunk costs a D*D*4-byte state per head that is handed on, so fewer,
-// longer chunks are cheaper as long as the CUs stay busy.
+// items, one per CU.  Both prefill walks hold one workgroup per CU, and
+// every chunk costs a D*D*4-byte state per head that is written and read
+// back, so fewer, longer chunks are cheaper as long as the CUs stay busy.
 int auto_chunk(int64_t total, int nseq, int heads, int block) {
     const int64_t target_items = 256;
     int64_t per = total * heads / target_items;
@@ -34,20 +34,20 @@ struct Layout {
     int chunk = 0;
     int max_chunks = 0;
     int n_slots = 0;
-    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_ring = 0, off_flag = 0, off_part = 0,
-           off_rsub = 0, off_tot = 0, off_clear_end = 0, bytes = 0;
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rsub = 0, off_tot = 0,
+           off_clear_end = 0, bytes = 0;
 };
 
-// the fused bf16 MFMA path (walk + RMSNorm in one kernel)
+// the bf16 MFMA path (walk + RMSNorm in one kernel)
 bool fused_path(int head_dim, int block, la_dtype dtype) {
     return dtype == LA_DTYPE_BF16 && head_dim == 128 && block == 64;
 }
 
 // Which bf16 MFMA kernel runs.  chunk_tokens = -1 asks for the lane kernel
 // (sequences never cut, K and V read once; needs heads * 4 <= CUs).  The
-// automatic choice (0) is the single-pass chunked kernel: on MI355X the lane
+// automatic choice (0) is the chunked two-pass prefill: on MI355X the lane
 // kernel's four workgroups per head each apply SiLU to the head's full Q and
-// K, and at 8192 tokens x 64 heads it measured 343 us against 230 us.
+// K, and at 8192 tokens x 64 heads it measured 364 us against 211 us.
 bool lane_path(int heads, int chunk_tokens, bool fused, int cus) {
     if (!fused || chunk_tokens != -1) return false;
     const int lanes = heads * la::lane_slices();
@@ -57,11 +57,11 @@ bool lane_path(int heads, int chunk_tokens, bool fused, int cus) {
 // Workspace: [PlanHeader][SegEntry x nseq], then
 //  * lane kernel: exchange rings part [XR][lanes][64], rsub [XR][groups][64]
 //    and tot [XR][64] of 8-byte words, cleared by the plan on every call;
-//  * otherwise [ChunkEntry x max_chunks], then
-//  * portable path: per-chunk states [max_chunks][H][D][D] fp32;
-//  * single-pass MFMA path: the chunk-state ring [slots][H][D*D] fp32, and the
-//    words the plan kernel clears on every call: ring flags [slots][H][4],
-//    the per-(chunk, block) RMSNorm exchange part [n_slots][H][64] and
+//  * otherwise [ChunkEntry x max_chunks], then per-chunk states
+//    [max_chunks][H][D][D] fp32 (chunk sums, then the states entering the
+//    chunks), then
+//  * MFMA path: the words the plan kernel clears on every call, the
+//    per-(chunk, block) RMSNorm exchange part [n_slots][H][64] and
 //    rsub [n_slots][ceil(H/16)][64].
 bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
                  bool fused, Layout* L) {
@@ -92,10 +92,11 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
         return true;
     }
     int chunk = chunk_tokens;
-    // Both paths: about one (chunk, head) item per CU.  For the single-pass
-    // MFMA kernel that is 2048-token chunks at 8192 tokens x 64 heads, the
-    // fastest measured there; at 1M tokens longer chunks (8192) spread the
-    // per-item fill and drain over more blocks.
+    // Both paths: about one (chunk, head) item per CU.  For the MFMA walk
+    // that is 2048-token chunks at 8192 tokens x 64 heads, the fastest
+    // measured there (1024: 236 us, 2048: 211 us per call); at 1M tokens
+    // longer chunks (8192) spread the per-item fill and drain over more
+    // blocks.
     if (chunk == 0) chunk = auto_chunk(total, nseq, heads, block);
     if (chunk < block || chunk % block != 0) return false;
     const int64_t maxc = total / chunk + nseq;  // >= sum over sequences of ceil(L_s / chunk)
@@ -108,20 +109,15 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     off = align_up(off + sizeof(la::SegEntry) * (size_t)nseq);
     L->off_chunks = off;
     off = align_up(off + sizeof(la::ChunkEntry) * (size_t)maxc);
+    L->off_states = off;
+    off = align_up(off + sizeof(float) * (size_t)maxc * heads * head_dim * head_dim);
     if (!fused) {
-        L->off_states = off;
-        off = align_up(off + sizeof(float) * (size_t)maxc * heads * head_dim * head_dim);
         L->bytes = off;
         return true;
     }
-    const int ring = la::prefill_mfma_ring_slots();
-    L->off_ring = off;
-    off = align_up(off + sizeof(float) * (size_t)ring * heads * head_dim * head_dim);
     const int64_t slots = maxc * (chunk / block);
     if (slots > (int64_t)0x7fffffff) return false;
     L->n_slots = (int)slots;
-    L->off_flag = off;
-    off = align_up(off + sizeof(int32_t) * (size_t)ring * heads * 4);
     L->off_part = off;
     off = align_up(off + sizeof(uint64_t) * (size_t)slots * heads * block);
     L->off_rsub = off;
@@ -176,26 +172,26 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
         return e == hipSuccess ? LA_OK : LA_ERR_HIP;
     }
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
+    a.states = reinterpret_cast<float*>(ws + L.off_states);
     const bool mfma = la::mfma_supported(a);
     if (mfma) {
-        a.states = nullptr;
-        a.ring = reinterpret_cast<float*>(ws + L.off_ring);
-        a.ring_flag = reinterpret_cast<int32_t*>(ws + L.off_flag);
+        a.skip_last = true;
         a.n_slots = L.n_slots;
         a.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
         a.rsub = reinterpret_cast<uint64_t*>(ws + L.off_rsub);
-        a.clear = reinterpret_cast<uint64_t*>(ws + L.off_flag);
-        a.clear_words = (int64_t)((L.off_clear_end - L.off_flag) / sizeof(uint64_t));
-    } else {
-        a.states = reinterpret_cast<float*>(ws + L.off_states);
+        a.clear = a.part;
+        a.clear_words = (int64_t)((L.off_clear_end - L.off_part) / sizeof(uint64_t));
     }
     hipError_t e = marks.mark(stream);
     if (e == hipSuccess) e = la::launch_plan(a, stream);
     if (e == hipSuccess) e = marks.mark(stream);
     if (mfma) {
-        // one kernel: state pass, chunk-state hand-over, walk and RMSNorm
-        // (the stage marks of the portable path's kernels stay empty)
+        // chunk sums (every chunk but each sequence's last), the scan of the
+        // states entering the chunks, then every chunk's walk with the
+        // RMSNorm fused (the norm_gate mark stays empty)
+        if (e == hipSuccess) e = la::launch_chunk_state_mfma(a, stream);
         if (e == hipSuccess) e = marks.mark(stream);
+        if (e == hipSuccess) e = la::launch_state_scan(a, stream);
         if (e == hipSuccess) e = marks.mark(stream);
         if (e == hipSuccess) e = la::launch_prefill_mfma(a, stream);
         if (e == hipSuccess) e = marks.mark(stream);

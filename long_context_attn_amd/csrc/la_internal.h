@@ -21,10 +21,9 @@ struct PlanHeader {
     int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow,
                        // 3 = a cross-workgroup wait of an MFMA prefill timed out
     int32_t ticket;    // start-order ticket of the fused walk's workgroups
-    int32_t wait_site; // error 3: which wait gave up first, where and who.  Single-pass
-                       // kernel: 1 group sums, 2 previous chunk's state, 3 free state slot,
-                       // 4 norm factors (chunk, head).  Lane kernel: 1 lanes' sums,
-                       // 2 group sums, 4 totals (block, lane).
+    int32_t wait_site; // error 3: which wait gave up first, where and who.  Chunked
+                       // walk: 1 group sums, 4 norm factors (chunk, head).  Lane kernel:
+                       // 1 lanes' sums, 2 group sums, 4 totals (block, lane).
     int32_t wait_chunk;
     int32_t wait_head;
     int32_t pad[10];
@@ -72,18 +71,20 @@ struct PrefillArgs {
     PlanHeader* hdr;
     SegEntry* segs;
     ChunkEntry* chunks;
-    float* states;            // [max_chunks][H][D][D]
+    float* states;            // [max_chunks][H][D][D]: chunk sums, then (after the
+                              // scan) the state entering each chunk
+    // with skip_last the last chunk of each sequence is not summed (its sum is
+    // neither computed nor read by the scan, and the scan writes no final
+    // state: the MFMA walk forms it)
+    bool skip_last;
     // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
     // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block.
     // Each word holds a float in its low half and 1 in its high half once
-    // written (0 = not yet written); the chunk-state kernel clears them.
+    // written (0 = not yet written); the plan kernel clears them.
     int n_slots;
     uint64_t* part;           // [n_slots][H][64] per-head sums of y^2 per token
     uint64_t* rsub;           // [n_slots][ceil(H / 16)][64] sums over groups of 16 heads
-    // chunk-state hand-over of the single-pass MFMA prefill
-    float* ring;              // [ring slots][H][64][256] fp32 (a consumer-register image)
-    int32_t* ring_flag;       // [ring slots][H][4]
-    // words the plan kernel zeroes on every call (ring flags and exchange words)
+    // words the plan kernel zeroes on every call (exchange words)
     uint64_t* clear;
     int64_t clear_words;
     // lane kernel: per-token totals over all lanes, [ring slots][64]
@@ -101,12 +102,12 @@ hipError_t launch_norm_gate(const PrefillArgs& a, hipStream_t st);
 // portable fp32 vector-ALU kernels (any supported shape)
 hipError_t launch_chunk_state_valu(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_walk_valu(const PrefillArgs& a, hipStream_t st);
-// single-pass bf16 MFMA prefill (D = 128, block = 64): state pass, hand-over
-// of the chunk states, walk and RMSNorm in one kernel after the plan
+// bf16 MFMA prefill walk (D = 128, block = 64): every chunk walked from the
+// scanned state entering it (states), with the RMSNorm fused
 bool mfma_supported(const PrefillArgs& a);
-int prefill_mfma_ring_slots();
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
-// bf16 MFMA chunk states (D = 128, block = 64), the state-only pass
+// bf16 MFMA chunk states (D = 128, block = 64): the state-only calls and the
+// first pass of the two-pass prefill
 bool state_mfma_supported(const PrefillArgs& a);
 hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
 // lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,

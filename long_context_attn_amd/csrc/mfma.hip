@@ -1,4 +1,4 @@
-// Single-pass bf16 MFMA prefill of the Lightning Attention layer for gfx950
+// bf16 MFMA prefill walk of the Lightning Attention layer for gfx950
 // (head_dim 128, block 64 tokens, fp32 accumulation).
 //
 // Mechanism step 3 of "Diving into MiniMax01 405B MoE" (section "Hybrid
@@ -35,58 +35,40 @@ constexpr int PP = MB + 8;     // pitch of the score tile
 constexpr int YP = MD + 8;     // pitch of the y staging tiles (rows 16-byte aligned)
 constexpr int RGRP = 16;       // heads per sub-reducer group of the RMSNorm exchange
 
-// --------------------------------------------- single-pass prefill
-// Workgroups take (chunk, head) items in start order from a ticket, chunk
-// major and head fastest, so a workgroup only ever waits on items that
-// started before it: the previous chunk of its head, or the other heads of
-// its own chunk (which are all started before any head of the next chunk).
+// --------------------------------------------- prefill walk
+// Second pass of the two-pass prefill.  The plan cut the sequences into
+// chunks; chunk_state_mfma_kernel summed K~^T V~ over every chunk but each
+// sequence's last, and state_scan_kernel turned those sums into the state
+// entering each chunk, entry[c][h] ([dk][dv] layout, the initial state
+// included).  Every (chunk, head) item then walks its chunk from that state.
+// Workgroups take items in start order from a ticket, chunk major and head
+// fastest, so all heads of a chunk are started before any head of the next
+// one: the cross-head RMSNorm exchange only ever waits on started items.
 //
-// An item runs nA + nblk + FIN iterations of two phases (barriers A and B):
-//   * state pass, iterations 0 .. nA-1 (nA = nblk, or 0 for the last chunk
-//     of a sequence, whose state nobody waits for): the producers stage
-//     K~ and V~ of block nA-1-it; one iteration later the consumers add
-//     K~^T V~ into S, which holds the chunk's own state sum until iteration nA;
-//   * iteration nA, phase 2: each consumer wave takes its quarter of the state
-//     entering the chunk (the initial state for a sequence's first chunk,
-//     else what the previous chunk published), hands that state plus the
-//     chunk's own sum to the next chunk (unless this is the sequence's last
-//     chunk), and keeps the entering state in S for the walk;
-//   * walk, from iteration nA on, with walk iteration b = it - nA: per
-//     64-token block j of the chunk (exchange slot s = c * slots_per_chunk + j)
-//       - iteration j: the producers stage Q~, K~ (phase 1) and V~ (phase 2);
-//       - iteration j + 1: the consumers compute S^T Q~^T and the scores
-//         (phase 1), then V~^T P^T and the state update (phase 2); y is staged
-//         as bf16 in LDS ring slot j % 3, sum_dv y^2 per token is reduced over
-//         the four waves, and after barrier B consumer wave 2 writes it to
-//         part[s][h][t];
-//       - iteration j + 2, phase 1: sub-reducer heads (s * G + g) % H, one per
-//         group g of RGRP heads, wait for their group's words and write the
-//         group sum to rsub[s][g][t];
-//       - iteration j + 3: wave 2 issues the loads of rsub[s][*][t] in phase 1
-//         and, at the end of phase 2, adds the G group sums in group order
-//         (deterministic) and leaves 1 / sqrt(mean y^2 + eps) in LDS;
-//       - iteration j + 4, phase 1: the producers write
-//         out = y * rnorm * w * sigmoid(gate), freeing ring slot j % 3 before
-//         block j + 3 is staged there in phase 2.
-// The state pass and the walk read each K and V block twice; the state pass
-// runs over the blocks in reverse, so the walk's first blocks are re-read
-// shortly after their first read.  Only wave 2 touches the exchange words (its score
-// quadrant is empty), and no wave with global loads in flight waits on them.
-//
-// Chunk-state hand-over: every chunk c uses ring slot c % RING of its head
-// once, in chunk order across all sequences.  Its consumer wave w first waits
-// until the slot's flag says chunk c - RING is done with it (-(c - RING + 1);
-// 0 for the first RING chunks), then writes its quarter of the state (64
-// registers x 64 lanes, lane-contiguous) and raises the flag to c + 1 -- or,
-// for a sequence's last chunk, which hands nothing on, sets it to -(c + 1)
-// at once.  The next chunk's wave w waits for tag c + 1, reads the quarter
-// and sets the flag to -(c + 1).  Every wait is on an earlier chunk, each
-// slot has one writer at a time, and the result does not depend on timing:
-// every chunk gets the state from its predecessor alone.
+// An item runs nblk + FIN iterations of two phases (barriers A and B).  Per
+// 64-token block j of the chunk (exchange slot s = c * slots_per_chunk + j):
+//   - iteration j: the producers stage Q~, K~ (phase 1) and V~ (phase 2);
+//   - iteration j + 1: the consumers compute S^T Q~^T and the scores (phase
+//     1), then V~^T P^T and the state update (phase 2); y is staged as bf16
+//     in LDS ring slot j % 3, sum_dv y^2 per token is reduced over the four
+//     waves, and after barrier B consumer wave 2 writes it to part[s][h][t];
+//   - iteration j + 2, phase 1: sub-reducer heads (s * G + g) % H, one per
+//     group g of RGRP heads, wait for their group's words and write the group
+//     sum to rsub[s][g][t];
+//   - iteration j + 3: wave 2 issues the loads of rsub[s][*][t] in phase 1
+//     and, at the end of phase 2, adds the G group sums in group order
+//     (deterministic) and leaves 1 / sqrt(mean y^2 + eps) in LDS;
+//   - iteration j + 4, phase 1: the producers write
+//     out = y * rnorm * w * sigmoid(gate), freeing ring slot j % 3 before
+//     block j + 3 is staged there in phase 2.
+// The state enters the consumers' registers in phase 2 of iteration 0.  Only
+// wave 2 touches the exchange words (its score quadrant is empty), and no
+// wave with global loads in flight waits on them.  Q, K, V and the gate are
+// streamed with the non-temporal hint, and so is the output.
 constexpr int FIN = 4;      // iterations from a block's staging to its final store
 constexpr int YRING = 3;    // y tiles in LDS
 constexpr int RPRE = 4;     // group sums whose loads are issued a phase ahead
-constexpr int RING = 4;     // chunk-state slots per head
+constexpr int NT = 2;       // cache policy of streamed loads and stores: non-temporal
 
 struct WalkLds {
     __bf16 q[2][TILE];        // Q~
@@ -104,7 +86,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     const __bf16* __restrict__ gate, const __bf16* __restrict__ wgt, __bf16* __restrict__ out,
     PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
     const ChunkEntry* __restrict__ chunks, const float* __restrict__ init_state,
-    float* __restrict__ final_state, float* __restrict__ ring, int32_t* __restrict__ ring_flag,
+    float* __restrict__ final_state, const float* __restrict__ entry,
     uint64_t* __restrict__ part, uint64_t* __restrict__ rsub, int H, int nseq,
     int slots_per_chunk, float eps) {
     __shared__ __attribute__((aligned(16))) WalkLds L;
@@ -125,13 +107,12 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     const int c = (int)(item / H), h = (int)(item - (int64_t)c * H);
     const ChunkEntry ce = chunks[c];
     const SegEntry se = segs[ce.seg];
-    const bool first = c == se.first, last = c == se.first + se.count - 1;
+    const bool last = c == se.first + se.count - 1;
     const int HD = H * MD;
     const int64_t off0 = ce.start * (int64_t)HD + (int64_t)h * MD;
     const int nblk = (ce.len + MB - 1) / MB;
-    const int nA = last ? 0 : nblk;
     const int slot0 = c * slots_per_chunk;
-    const int iters = nA + nblk + FIN;
+    const int iters = nblk + FIN;
 
     if (w >= 4) {
         // ------------------------------------------------------ producers
@@ -139,44 +120,27 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
         const int cc = ptid & 15, rg = ptid >> 4;
         const int voff = (4 * rg * HD + 8 * cc) * 2, rstride = HD * 2;
         const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wgt + h * MD + 8 * cc);
-        // Two register sets: the tiles of iteration i are loaded into set
-        // i & 1 two iterations ahead, and so is the gate of the block that
+        // Two register sets: the tiles of block i are loaded into set i & 1
+        // two iterations ahead, and so is the gate of the block that
         // iteration i finalises.  Loads are issued unconditionally (blocks
-        // outside the chunk, and q during the state pass, get an empty range
-        // and return zeros): a conditional load would make the compiler copy
-        // registers that still have a load in flight.
+        // outside the chunk get an empty range and return zeros): a
+        // conditional load would make the compiler copy registers that still
+        // have a load in flight.
         auto rows = [&](int blk) { return blk < 0 ? 0 : max(0, min(MB, ce.len - blk * MB)); };
-        // The state pass visits the chunk's blocks last to first, so the walk,
-        // which starts with the first block, re-reads the most recently read
-        // K and V first (still in the caches).
-        auto blk_of = [&](int i) { return i < nA ? nA - 1 - i : i - nA; };
-        auto load_q = [&](int i, Tile& tq) {
-            const int blk = blk_of(i);
-            load_tile(tq, tile_rsrc(q + off0 + (int64_t)blk * MB * HD, i < nA ? 0 : rows(blk), HD),
-                      voff, rstride);
-        };
-        auto load_k = [&](int i, Tile& tk) {
-            const int blk = blk_of(i);
-            load_tile(tk, tile_rsrc(k + off0 + (int64_t)blk * MB * HD, rows(blk), HD), voff, rstride);
-        };
-        auto load_v = [&](int i, Tile& tv) {
-            const int blk = blk_of(i);
-            load_tile(tv, tile_rsrc(v + off0 + (int64_t)blk * MB * HD, rows(blk), HD), voff, rstride);
-        };
-        auto load_gate = [&](int jf, Tile& tg) {
-            load_tile(tg, tile_rsrc(gate + off0 + (int64_t)jf * MB * HD, rows(jf), HD), voff,
-                      rstride);
+        auto load = [&](const __bf16* base, int blk, Tile& t) {
+            load_tile<NT>(t, tile_rsrc(base + off0 + (int64_t)max(blk, 0) * MB * HD, rows(blk), HD),
+                          voff, rstride);
         };
         Tile q0, k0, v0, g0, q1, k1, v1, g1;
-        load_q(0, q0);
-        load_k(0, k0);
-        load_v(0, v0);
-        load_q(1, q1);
-        load_k(1, k1);
-        load_v(1, v1);
+        load(q, 0, q0);
+        load(k, 0, k0);
+        load(v, 0, v0);
+        load(q, 1, q1);
+        load(k, 1, k1);
+        load(v, 1, v1);
         auto step = [&](int it, Tile& tq, Tile& tk, Tile& tv, Tile& tg) {
             const int buf = it & 1;
-            const int b = it - nA;  // walk block staged in this iteration
+            const int b = it;  // block staged in this iteration
             // ---- phase 1: finalise block jf (its y in LDS, its norm factors
             // left by wave 2 in the previous iteration), then stage q and k
             const int jf = b - FIN;
@@ -206,16 +170,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     od[r] = __builtin_bit_cast(u32x4, o[r]);
-                    __builtin_amdgcn_raw_buffer_store_b128(od[r], ro, voff, r * rstride, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(od[r], ro, voff, r * rstride, NT);
                 }
             }
-            load_gate(jf + 2, tg);  // finalised in iteration it + 2, same register set
-            if (it < nA) {
-                bf16x8 ks[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ks[r] = silu8(tk.r[r]);
-                store_rows(ks, L.k[buf], cc, rg);
-            } else if (b < nblk) {
+            load(gate, jf + 2, tg);  // finalised in iteration it + 2, same register set
+            if (b < nblk) {
                 bf16x8 qs[4], ks[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -225,8 +184,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                 store_rows(qs, L.q[buf], cc, rg);
                 store_rows(ks, L.k[buf], cc, rg);
             }
-            load_q(it + 2, tq);
-            load_k(it + 2, tk);
+            load(q, it + 2, tq);
+            load(k, it + 2, tk);
             __syncthreads();  // A
             if (jf >= 0 && jf < nblk)
 #pragma unroll
@@ -238,7 +197,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                 for (int r = 0; r < 4; ++r) vs[r] = silu8(tv.r[r]);
                 store_rows(vs, L.v[buf], cc, rg);
             }
-            load_v(it + 2, tv);
+            load(v, it + 2, tv);
             __syncthreads();  // B
         };
         for (int it = 0; it < iters; it += 2) {
@@ -255,14 +214,13 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     // accumulator register r of tile m in this lane holds state entry
     // dk = 32 m + 8 (r / 4) + 4 g + r % 4, dv = 32 w + l32
     const int dv = 32 * w + l32;
-    // S holds the chunk's own state sum during the state pass, then, from
-    // the hand-over on, the walk's running state
+    // the walk's running state (this wave's 32 columns)
     f32x16 S[4] = {};
     const int qa = w >> 1, qb = w & 1;  // score quadrant: t' in [32 qa, +32), t in [32 qb, +32)
     uint64_t held_pub = 0, held_red = 0;  // exchange words stored by wave 2, kept live
     for (int it = 0; it < iters; ++it) {
-        const int b = it - nA;  // walk iteration
-        const int jc = b - 1;   // walk block computed in this iteration
+        const int b = it;
+        const int jc = b - 1;   // block computed in this iteration
         const bool comp = jc >= 0 && jc < nblk;
         const int buf = (it - 1) & 1;  // tiles staged in the previous iteration
         const __bf16* sQ = L.q[buf];
@@ -302,29 +260,6 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < RGRP; ++i) tot += word_value(x[i]);
                 held_red = put_word(rsub + ((int64_t)slot * G + gi) * MB + lane, tot);
-            }
-        }
-        // ---- phase 1: state pass, S += K~^T V~ of block it - 1
-        if (it >= 1 && it <= nA) {
-            // all operands in flight before the products (an MFMA chain that
-            // waits for each operand load in turn exposes the LDS latency at
-            // every step)
-            // (half of the tokens at a time)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                bf16x8 vb[2], ka[2][4];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int s = 2 * h2 + i;
-                    vb[i] = ld_tr_operand(sV, 16 * s, 32 * w, lane);
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) ka[i][m] = ld_tr_operand(sK, 16 * s, 32 * m, lane);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) S[m] = mfma32(ka[i][m], vb[i], S[m]);
             }
         }
         // ---- phase 1: walk: S^T Q~^T into O, and the scores of block jc
@@ -383,60 +318,17 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
         __syncthreads();  // A
         keep(held_pub);
         keep(held_red);
-        // ---- phase 2, iteration nA: the state entering the chunk replaces the
-        // chunk's own sum in S, and their sum is handed to the next chunk
-        if (it == nA) {
-            const int ps = (c + RING - 1) % RING, cs = c % RING;
-            int32_t* pfl = ring_flag + ((int64_t)ps * H + h) * 4 + w;
-            int32_t* cfl = ring_flag + ((int64_t)cs * H + h) * 4 + w;
-            if (lane == 0) {
-                int polls = 0;
-                if (!first)  // the previous chunk's state is in its slot
-                    while (get_i(pfl) != c && poll_again(polls, hdr, 2, c, h)) {
-                    }
-                // this chunk's slot is done with by chunk c - RING
-                const int32_t prev_done = c < RING ? 0 : -(c - RING + 1);
-                while (get_i(cfl) != prev_done && poll_again(polls, hdr, 3, c, h)) {
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            drain();
-            // Buffer accesses: one VGPR offset per lane, the register index in
-            // the scalar offset.  Ring slots are lane-contiguous images of
-            // the consumer registers (coherent sc1 accesses); the initial
-            // state has the [dk][dv] layout of the interface.
-            const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-                ring + ((int64_t)ps * H + h) * DD, (short)0, (int)(DD * 4), 0x00020000);
-            const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
-                ring + ((int64_t)cs * H + h) * DD, (short)0, (int)(DD * 4), 0x00020000);
-            const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(init_state ? init_state + ((int64_t)ce.seg * H + h) * DD : ring), (short)0,
-                first && init_state ? (int)(DD * 4) : 0, 0x00020000);
-            const int roff = (64 * w + lane) * 4, ioff = (4 * g * MD + dv) * 4;
-            f32x16 P[4];  // loaded in one batch
+        // ---- phase 2, iteration 0: the state entering the chunk
+        if (it == 0) {
+            const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(entry + ((int64_t)c * H + h) * DD), (short)0, (int)(DD * 4), 0x00020000);
+            const int ioff = (4 * g * MD + dv) * 4;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    P[m][r] = __uint_as_float(
-                        !first ? __builtin_amdgcn_raw_buffer_load_b32(pr, roff, (16 * m + r) * 1024, SC1)
-                               : __builtin_amdgcn_raw_buffer_load_b32(
-                                     ir, ioff, (32 * m + 8 * (r >> 2) + (r & 3)) * MD * 4, 0));
-            if (!last) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(P[m][r] + S[m][r]), cr,
-                                                              roff, (16 * m + r) * 1024, SC1);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) S[m] = P[m];
-            drain();  // loads returned and stores completed
-            if (lane == 0) {
-                if (!first) put_i(pfl, -c);          // chunk c - 1's slot is done with
-                put_i(cfl, last ? -(c + 1) : c + 1);  // nothing to read, or this state
-            }
+                    S[m][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        er, ioff, (32 * m + 8 * (r >> 2) + (r & 3)) * MD * 4, 0));
         }
         // ---- phase 2: walk: V~^T P^T into O, state update, y staging
         if (comp) {
@@ -536,16 +428,14 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
 
 bool mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.block == MB; }
 
-int prefill_mfma_ring_slots() { return RING; }
-
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
     if (a.max_chunks == 0 && a.nseq == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H + a.nseq));
     hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(NTHREADS), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.g,
                        (const __bf16*)a.w, (__bf16*)a.out, a.hdr, a.segs, a.chunks, a.init_state,
-                       a.final_state, a.ring, a.ring_flag, a.part, a.rsub, a.H, a.nseq,
-                       a.chunk / MB, a.eps);
+                       a.final_state, a.states, a.part, a.rsub, a.H, a.nseq, a.chunk / MB,
+                       a.eps);
     return hipGetLastError();
 }
 

@@ -80,11 +80,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, 
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
-// voff = byte offset of (row 4 rg, feature 8 cc); rows r are rstride bytes apart
+// voff = byte offset of (row 4 rg, feature 8 cc); rows r are rstride bytes
+// apart; AUX = cache policy bits of the loads
+template <int AUX = 0>
 __device__ __forceinline__ void load_tile(Tile& t, __amdgpu_buffer_rsrc_t rs, int voff, int rstride) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-        t.r[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, r * rstride, 0));
+        t.r[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, r * rstride, AUX));
 }
 
 // a producer thread's four 16-byte pieces of a swizzled tile
@@ -151,16 +153,6 @@ __device__ __forceinline__ bool poll_again(int& polls, PlanHeader* hdr, int site
     return true;
 }
 
-// Coherent 4-byte flag accesses for the chunk-state hand-over (sc1 on gfx950,
-// seen by workgroups on every XCD once the stores have completed).
-__device__ __forceinline__ void put_i(int32_t* p, int32_t x) {
-    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t get_i(int32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// waits for this wave's outstanding memory accesses; also a compiler fence
-__device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // cache-policy operand of the buffer builtins selecting sc1 (device-coherent)
 constexpr int SC1 = 16;
 

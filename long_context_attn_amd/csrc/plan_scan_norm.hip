@@ -34,7 +34,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     __shared__ int32_t bad;
     const int tid = threadIdx.x;
     if (tid == 0) {
-        hdr->ticket = 0;  // start-order ticket of the single-pass prefill
+        hdr->ticket = 0;  // start-order ticket of the MFMA walk
         hdr->wait_site = hdr->wait_chunk = hdr->wait_head = 0;
     }
     if (tid == 0) {
@@ -107,12 +107,14 @@ hipError_t launch_plan(const PrefillArgs& a, hipStream_t st) {
 // ------------------------------------------------------------- state scan
 // One thread per 4 state entries of one (sequence, head): walks the
 // sequence's chunks in order, replacing each chunk sum by the state that
-// enters the chunk, and stores the state after the last chunk.
+// enters the chunk, and stores the state after the last chunk.  With
+// skip_last the last chunk of a sequence has no sum (only its entering
+// state is written, and no final state).
 constexpr int SCAN_THREADS = 256;
 
 __global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(
     float* __restrict__ states, const SegEntry* __restrict__ segs, const float* init,
-    float* fin, int H, int DD, int tiles) {
+    float* fin, int H, int DD, int tiles, bool skip_last) {
     const int pair = blockIdx.x / tiles;  // sequence * H + head
     const int tile = blockIdx.x - pair * tiles;
     const int e = (tile * SCAN_THREADS + threadIdx.x) * 4;
@@ -121,13 +123,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(
     f32x4 run = {0.f, 0.f, 0.f, 0.f};
     if (init != nullptr) run = *reinterpret_cast<const f32x4*>(init + (int64_t)pair * DD + e);
     const SegEntry se = segs[s];
-    for (int c = se.first; c < se.first + se.count; ++c) {
+    const int end = se.first + se.count;
+    for (int c = se.first; c < end; ++c) {
         f32x4* p = reinterpret_cast<f32x4*>(states + ((int64_t)c * H + h) * DD + e);
+        if (skip_last && c == end - 1) {
+            *p = run;
+            break;
+        }
         const f32x4 sum = *p;
         *p = run;
         run += sum;
     }
-    if (fin != nullptr) *reinterpret_cast<f32x4*>(fin + (int64_t)pair * DD + e) = run;
+    if (fin != nullptr && !skip_last) *reinterpret_cast<f32x4*>(fin + (int64_t)pair * DD + e) = run;
 }
 
 hipError_t launch_state_scan(const PrefillArgs& a, hipStream_t st) {
@@ -136,7 +143,8 @@ hipError_t launch_state_scan(const PrefillArgs& a, hipStream_t st) {
     const int64_t grid = (int64_t)a.nseq * a.H * tiles;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(state_scan_kernel, dim3((unsigned)grid), dim3(SCAN_THREADS), 0, st,
-                       a.states, a.segs, a.init_state, a.final_state, a.H, DD, tiles);
+                       a.states, a.segs, a.init_state, a.final_state, a.H, DD, tiles,
+                       a.skip_last);
     return hipGetLastError();
 }
 

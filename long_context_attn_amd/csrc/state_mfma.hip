@@ -4,9 +4,9 @@
 // k~ = SiLU(k), v~ = SiLU(v) -- the running-state sum of Mechanism step 3 of
 // "Diving into MiniMax01 405B MoE" (section "Hybrid Modeling") over one chunk.
 // With the prefix scan over a sequence's chunks (plan_scan_norm.hip) it gives
-// each sequence's final state without the walk: the first pass of a prefill
-// split along the sequence, whose second pass is a prefill started from the
-// prefix of the preceding parts' states.
+// each sequence's final state without the walk (the state-only calls), and
+// the state entering every chunk for the MFMA prefill, whose walk then
+// starts every chunk at once.
 #include "mfma_common.h"
 
 namespace la {
@@ -21,7 +21,10 @@ struct StateLds {
     __bf16 v[2][TILE];
 };
 
-// One workgroup per (chunk, head).  Thread t loads rows t / 16 and t / 16 + 32
+// One workgroup per (chunk, head), state written at states[c][h].  With
+// skip_last, the last chunk of each sequence is left out (the prefill does
+// not need its sum: its walk forms the final state).  Thread t loads rows
+// t / 16 and t / 16 + 32
 // of a block, features 8 (t % 16) .. + 7, applies SiLU and writes the swizzled
 // bf16 tiles; wave w accumulates the state tiles dk in [64 (w / 4), +64),
 // dv in [32 (w % 4), +32).  Every wave takes part in the SiLU: it is a chain
@@ -29,17 +32,22 @@ struct StateLds {
 // latency where one could not.
 __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const PlanHeader* __restrict__ hdr, const ChunkEntry* __restrict__ chunks,
-    float* __restrict__ states, int H) {
+    const PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
+    const ChunkEntry* __restrict__ chunks, float* __restrict__ states, int H, bool skip_last) {
     __shared__ __attribute__((aligned(16))) StateLds L;
     const int nch = hdr->n_chunks;
-    const int c = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    const int c = blockIdx.x / H, h = blockIdx.x - c * H;
     if (c >= nch) return;
     const ChunkEntry ce = chunks[c];
+    if (skip_last) {
+        const SegEntry se = segs[ce.seg];
+        if (c == se.first + se.count - 1) return;
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int HD = H * MD;
+    const int len = ce.len;
+    const int nblk = (len + MB - 1) / MB;
     const int64_t off0 = ce.start * (int64_t)HD + (int64_t)h * MD;
-    const int nblk = (ce.len + MB - 1) / MB;
     const int cc = tid & 15, rg = tid >> 4;
     const int voff = (rg * HD + 8 * cc) * 2, rstride = 32 * HD * 2;
     // Block b is loaded into register set b % SPF, SPF blocks ahead.  Loads
@@ -50,8 +58,12 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
         bf16x8 r[2];
     };
     Rows tk[SPF], tv[SPF];
-    auto load_rows = [&](const __bf16* base, int b, Rows& t) {
-        const int t0 = b * MB, n = max(0, min(MB, ce.len - t0));
+    // The blocks are visited last to first: a prefill's walk, which starts
+    // with each chunk's first block, then finds the most recently read K and
+    // V first (still in the caches).
+    auto load_rows = [&](const __bf16* base, int i, Rows& t) {
+        const int b = nblk - 1 - i;
+        const int t0 = max(b, 0) * MB, n = b < 0 ? 0 : max(0, min(MB, len - t0));
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base + off0 + (int64_t)t0 * HD, n, HD);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -116,7 +128,7 @@ hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st) {
     if (a.max_chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H));
     hipLaunchKernelGGL(chunk_state_mfma_kernel, grid, dim3(ST_THREADS), 0, st, (const __bf16*)a.k,
-                       (const __bf16*)a.v, a.hdr, a.chunks, a.states, a.H);
+                       (const __bf16*)a.v, a.hdr, a.segs, a.chunks, a.states, a.H, a.skip_last);
     return hipGetLastError();
 }
 

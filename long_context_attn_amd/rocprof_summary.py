@@ -48,6 +48,8 @@ def short_name(name: str) -> str:
         k = int(m.group(1))
         ident = n[m.end():m.end() + k]
         return "la::" + ident + ("<bf16>" if "DF16b" in n else "")
+    # kernels in an anonymous namespace: "la::(anonymous namespace)::name(args)"
+    n = n.replace("(anonymous namespace)::", "")
     return n.split("(")[0]
 
 

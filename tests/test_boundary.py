@@ -63,20 +63,20 @@ def test_status_strings(lib):
 
 def test_prefill_workspace_size(lib):
     ws = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024)
-    # bf16 MFMA path, 8 chunks of 1024 tokens (+ one spare per sequence): a 4-slot ring of
-    # 64 heads x 128 x 128 fp32 chunk states, 4 flags per ring slot and head, and per
-    # (chunk, 64-token block) the RMSNorm exchange: 64 heads x 64 tokens of partial sums
-    # and 64 sums for each group of 16 heads, each an 8-byte {value, written} word
+    # bf16 MFMA path, 8 chunks of 1024 tokens (+ one spare per sequence): a 64 heads x
+    # 128 x 128 fp32 state per chunk (chunk sum, then the state entering the chunk), and
+    # per (chunk, 64-token block) the RMSNorm exchange: 64 heads x 64 tokens of partial
+    # sums and 64 sums for each group of 16 heads, each an 8-byte {value, written} word
     slots = 9 * (1024 // 64)
-    need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
+    need = 9 * 64 * 128 * 128 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ws < need + 65536
-    # the automatic choice is the single-pass chunked kernel with about 256 (chunk, head)
-    # items: 2048-token chunks for 64 heads, 128-token chunks for 4 heads
+    # the automatic choice is the chunked prefill with about 256 (chunk, head) items:
+    # 2048-token chunks for 64 heads, 128-token chunks for 4 heads
     slots = (4 + 1) * (2048 // 64)
-    need = 4 * 64 * 128 * 128 * 4 + 4 * 64 * 4 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
+    need = 5 * 64 * 128 * 128 * 4 + slots * (64 * 64 * 8 + 4 * 64 * 8)
     assert need <= ops.prefill_workspace_size(8192, 1, 64, 128, 64, 0) < need + 65536
     slots = (64 + 1) * (128 // 64)
-    need = 4 * 4 * 128 * 128 * 4 + 4 * 4 * 4 * 4 + slots * (4 * 64 * 8 + 1 * 64 * 8)
+    need = 65 * 4 * 128 * 128 * 4 + slots * (4 * 64 * 8 + 1 * 64 * 8)
     assert need <= ops.prefill_workspace_size(8192, 1, 4, 128, 64, 0) < need + 65536
     # -1: the lane kernel (sequences walked whole, 64 x 4 lanes), whose workspace is the
     # plan header, a record per sequence and three exchange rings of 16 slots of 8-byte

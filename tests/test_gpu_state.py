@@ -79,7 +79,7 @@ def test_state_varlen_with_empty_sequences(dtype, D, block):
 @pytest.mark.parametrize("dtype,D,block", [(torch.bfloat16, 128, 64), (torch.float32, 64, 32)])
 def test_sequence_split_prefill(dtype, D, block):
     """One 2000-token sequence cut into parts of uneven lengths (not multiples
-    of the block): state pass over every part, exclusive prefix of the part
+    of the block): state-only pass over every part, exclusive prefix of the part
     states on the host in fp64, prefill of each part from its prefix."""
     N, H = 2000, 4
     q, k, v, g, w = inputs(N, H, D, "minimax", bf16=dtype == torch.bfloat16, key=15)
