@@ -51,6 +51,9 @@ def _bind(path):
                                      ctypes.c_int64, ctypes.c_double, _D, _D]
     lib.la_oracle_state.argtypes = [_D, _D, _I64, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int64, _D]
+    lib.la_oracle_backward.argtypes = [_D, _D, _D, _D, _D, _D, _I64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _D, _D,
+                                       _D, _D, _D, _D, _D, _D]
     lib.la_oracle_sigmoid.argtypes = [ctypes.c_double]
     lib.la_oracle_sigmoid.restype = ctypes.c_double
     lib.la_oracle_silu.argtypes = [ctypes.c_double]
@@ -58,7 +61,7 @@ def _bind(path):
     lib.la_oracle_set_threads.argtypes = [ctypes.c_int]
     lib.la_oracle_max_threads.restype = ctypes.c_int
     for f in ("la_oracle_prefill", "la_oracle_prefill_blocked", "la_oracle_decode",
-              "la_oracle_state"):
+              "la_oracle_state", "la_oracle_backward"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -177,6 +180,32 @@ def state(k, v, cu_seqlens=None, init_state=None):
     st = np.zeros((nseq, H, D, D), np.float64) if init_state is None else _f64(init_state).copy()
     _load().la_oracle_state(_p(k), _p(v), seg.ctypes.data_as(_I64), nseq, H, D, _p(st))
     return st
+
+
+def backward(q, k, v, g, w, dout, cu_seqlens=None, eps=1e-6, init_state=None,
+             d_final_state=None):
+    """Gradient of the prefill (chain rule through Mechanism steps 4, 3, 2 in
+    reverse).  dout: [T, H, D], the loss gradient w.r.t. the output;
+    d_final_state: [nseq, H, D, D] or None, w.r.t. the final states.
+    Returns dict(dq, dk, dv, dg [T, H, D], dw [H*D], d_init [nseq, H, D, D]) in float64.
+    """
+    q, k, v, g, w, dout = (_f64(a) for a in (q, k, v, g, w, dout))
+    T, H, D = q.shape
+    seg = _segments(T, cu_seqlens)
+    nseq = len(seg) - 1
+    init = _f64(init_state)
+    dfin = _f64(d_final_state)
+    for x, name in ((init, "init_state"), (dfin, "d_final_state")):
+        if x is not None and x.shape != (nseq, H, D, D):
+            raise ValueError(name + " shape")
+    res = {n: np.empty((T, H, D), np.float64) for n in ("dq", "dk", "dv", "dg")}
+    res["dw"] = np.empty(H * D, np.float64)
+    res["d_init"] = np.empty((nseq, H, D, D), np.float64)
+    _load().la_oracle_backward(_p(q), _p(k), _p(v), _p(g), _p(w), _p(dout),
+                               seg.ctypes.data_as(_I64), nseq, H, D, float(eps), _p(init), _p(dfin),
+                               _p(res["dq"]), _p(res["dk"]), _p(res["dv"]), _p(res["dg"]),
+                               _p(res["dw"]), _p(res["d_init"]))
+    return res
 
 
 def compare(out_dev, out_ref):

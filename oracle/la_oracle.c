@@ -218,6 +218,128 @@ int la_oracle_state(const double* k, const double* v, const int64_t* seg, int64_
     return 0;
 }
 
+/* derivative of SiLU: sigmoid(x) (1 + x (1 - sigmoid(x))) */
+static double silu_grad(double x) {
+    const double s = sigmoid(x);
+    return s * (1.0 + x * (1.0 - s));
+}
+
+/*
+ * Gradient of the layer: the reverse-mode derivative of la_oracle_prefill
+ * for a loss L whose gradient w.r.t. the output is dout [T][H][D] and, if
+ * d_final is given, w.r.t. the final states [nseq][H][D][D].  Writes dq, dk,
+ * dv, dg [T][H][D], dw [H*D] and, if d_init is given, dL/dS0 [nseq][H][D][D].
+ * The chain rule is taken through the forward steps in reverse order:
+ *  step 4, per token (out = yhat c, yhat = y r, r = (mean y^2 + eps)^-1/2,
+ *    c = w sigmoid(g)):  a = dout c;  dy = r (a - yhat <a, yhat> / HD);
+ *    dg = dout yhat w sigmoid(g) (1 - sigmoid(g));  dw = sum_t dout yhat sigmoid(g);
+ *  step 3, per segment and head:  with dS_t = dL/dS_t, the gradient reaching
+ *    S_t = S_{t-1} + k~_t^T v~_t through y_t = q~_t S_t and through S_{t+1}:
+ *      dS_t = q~_t^T dy_t + dS_{t+1}  (dS after the last token = d_final);
+ *      dq~_t = dy_t S_t^T;  dk~_t = v~_t dS_t^T;  dv~_t = k~_t dS_t;
+ *      dL/dS0 = dS_first;
+ *    a forward sweep recomputes S_t for dq~, a reverse sweep accumulates dS;
+ *  step 2:  dq = dq~ SiLU'(q), and likewise for k and v.
+ */
+int la_oracle_backward(const double* q, const double* k, const double* v, const double* g,
+                       const double* w, const double* dout, const int64_t* seg, int64_t nseq,
+                       int64_t H, int64_t D, double eps, const double* init_state,
+                       const double* d_final, double* dq, double* dk, double* dv, double* dg,
+                       double* dw, double* d_init) {
+    const int64_t HD = H * D;
+    const int64_t T = seg[nseq];
+    /* forward recomputation of the pre-norm y */
+    double* y = (double*)malloc(sizeof(double) * (T > 0 ? T * HD : 1));
+    double* outs = (double*)malloc(sizeof(double) * (T > 0 ? T * HD : 1));
+    double* dy = (double*)malloc(sizeof(double) * (T > 0 ? T * HD : 1));
+    double* yhat = outs;  /* reused: y r per element */
+    la_oracle_prefill(q, k, v, g, w, seg, nseq, H, D, eps, init_state, outs, y, NULL);
+    /* step 4 backward, per token */
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* yt = y + t * HD;
+        double ss = 0.0;
+        for (int64_t i = 0; i < HD; ++i) ss += yt[i] * yt[i];
+        const double r = 1.0 / sqrt(eps + ss / (double)HD);  /* the forward's r */
+        double ay = 0.0;
+        for (int64_t i = 0; i < HD; ++i) {
+            const int64_t e = t * HD + i;
+            yhat[e] = yt[i] * r;
+            const double sg = sigmoid(g[e]);
+            ay += dout[e] * w[i] * sg * yhat[e];
+            dg[e] = dout[e] * yhat[e] * w[i] * sg * (1.0 - sg);
+        }
+        for (int64_t i = 0; i < HD; ++i) {
+            const int64_t e = t * HD + i;
+            const double a = dout[e] * w[i] * sigmoid(g[e]);
+            dy[e] = r * (a - yhat[e] * ay / (double)HD);
+        }
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < HD; ++i) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t) acc += dout[t * HD + i] * yhat[t * HD + i] * sigmoid(g[t * HD + i]);
+        dw[i] = acc;
+    }
+    /* step 3 backward, per segment and head */
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t s = 0; s < nseq; ++s) {
+        for (int64_t h = 0; h < H; ++h) {
+            double* S = (double*)malloc(sizeof(double) * D * D);
+            double* qt = (double*)malloc(sizeof(double) * D * 3);
+            double* kt = qt + D;
+            double* vt = qt + 2 * D;
+            /* forward sweep: S_t, then dq~_t = dy_t S_t^T */
+            const double* S0 = init_state ? init_state + (s * H + h) * D * D : NULL;
+            for (int64_t e = 0; e < D * D; ++e) S[e] = S0 ? S0[e] : 0.0;
+            for (int64_t t = seg[s]; t < seg[s + 1]; ++t) {
+                const int64_t base = t * HD + h * D;
+                for (int64_t d = 0; d < D; ++d) {
+                    kt[d] = silu(k[base + d]);
+                    vt[d] = silu(v[base + d]);
+                }
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += kt[i] * vt[j];
+                for (int64_t i = 0; i < D; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < D; ++j) acc += dy[base + j] * S[i * D + j];
+                    dq[base + i] = acc * silu_grad(q[base + i]);
+                }
+            }
+            /* reverse sweep: dS_t, then dk~_t and dv~_t */
+            if (d_final) memcpy(S, d_final + (s * H + h) * D * D, sizeof(double) * D * D);
+            else memset(S, 0, sizeof(double) * D * D);
+            for (int64_t t = seg[s + 1] - 1; t >= seg[s]; --t) {
+                const int64_t base = t * HD + h * D;
+                for (int64_t d = 0; d < D; ++d) {
+                    qt[d] = silu(q[base + d]);
+                    kt[d] = silu(k[base + d]);
+                    vt[d] = silu(v[base + d]);
+                }
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += qt[i] * dy[base + j];
+                for (int64_t i = 0; i < D; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < D; ++j) acc += S[i * D + j] * vt[j];
+                    dk[base + i] = acc * silu_grad(k[base + i]);
+                }
+                for (int64_t j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < D; ++i) acc += kt[i] * S[i * D + j];
+                    dv[base + j] = acc * silu_grad(v[base + j]);
+                }
+            }
+            if (d_init) memcpy(d_init + (s * H + h) * D * D, S, sizeof(double) * D * D);
+            free(qt);
+            free(S);
+        }
+    }
+    free(dy);
+    free(outs);
+    free(y);
+    return 0;
+}
+
 /* thread control for the timed baseline (OpenMP over segments x heads) */
 #ifdef _OPENMP
 #include <omp.h>

@@ -220,6 +220,111 @@ def pin_segments_and_resume(orc):
     assert rel(st_b, st_all) < TIGHT
 
 
+# ------------------------------------------------------------- backward
+# The gradient of the layer (oracle.backward) is pinned to the derivative of
+# the forward by central finite differences, to reverse-mode autodiff of an
+# independent PyTorch statement of the forward, and to a closed form.
+
+def _bwd_inputs(seed, T, H, D, nseq):
+    q, k, v, g = (rnd(seed + i, (T, H, D)) for i in range(4))
+    w = rnd(seed + 4, (H * D,), 0.5) + 1.0
+    init = rnd(seed + 5, (nseq, H, D, D), 0.5)
+    dout = rnd(seed + 6, (T, H, D))
+    dfin = rnd(seed + 7, (nseq, H, D, D), 0.3)
+    return q, k, v, g, w, init, dout, dfin
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient entry against a central difference of the oracle's own
+    forward, loss = <out, dout> + <final state, dfin>; segments include an
+    empty one."""
+    T, H, D, seg, eps = 6, 2, 3, [0, 2, 2, 6], 1e-6
+    q, k, v, g, w, init, dout, dfin = _bwd_inputs(71, T, H, D, 3)
+    grads = orc.backward(q, k, v, g, w, dout, cu_seqlens=seg, eps=eps, init_state=init,
+                         d_final_state=dfin)
+    args = {"q": q, "k": k, "v": v, "g": g, "w": w, "init": init}
+
+    def loss(a):
+        out, fs = orc.prefill(a["q"], a["k"], a["v"], a["g"], a["w"], cu_seqlens=seg, eps=eps,
+                              init_state=a["init"], return_state=True)
+        return float(np.sum(out * dout) + np.sum(fs * dfin))
+
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "w": "dw", "init": "d_init"}
+    step = 1e-5
+    for n, x in args.items():
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = {m: y.copy() for m, y in args.items()}
+            a[n][idx] = x[idx] + step
+            lp = loss(a)
+            a[n][idx] = x[idx] - step
+            lm = loss(a)
+            fd[idx] = (lp - lm) / (2 * step)
+        got = grads[names[n]]
+        assert np.max(np.abs(got - fd)) <= 1e-6 * max(1.0, np.max(np.abs(fd))), (n, got, fd)
+
+
+def _torch_forward(q, k, v, g, w, seg, eps, init):
+    """Plain PyTorch statement of the layer (left product per segment and head)."""
+    import torch
+    silu = lambda x: x * torch.sigmoid(x)
+    qs, ks, vs = silu(q), silu(k), silu(v)
+    T, H, D = q.shape
+    y = torch.zeros(T, H, D, dtype=q.dtype)
+    finals = []
+    for s in range(len(seg) - 1):
+        a, b = seg[s], seg[s + 1]
+        for h in range(H):
+            Q, K, V = qs[a:b, h], ks[a:b, h], vs[a:b, h]
+            y[a:b, h] = torch.tril(Q @ K.T) @ V + Q @ init[s, h]
+            finals.append(init[s, h] + K.T @ V)
+    fs = torch.stack(finals).reshape(len(seg) - 1, H, D, D)
+    yf = y.reshape(T, H * D)
+    r = torch.rsqrt(torch.mean(yf * yf, dim=1, keepdim=True) + eps)
+    out = (yf * r * w * torch.sigmoid(g.reshape(T, H * D))).reshape(T, H, D)
+    return out, fs
+
+
+def pin_backward_autograd(orc):
+    """All gradients against torch.autograd (float64, CPU) of the PyTorch forward."""
+    import torch
+    T, H, D, seg, eps = 29, 3, 5, [0, 11, 11, 29], 1e-6
+    q, k, v, g, w, init, dout, dfin = _bwd_inputs(91, T, H, D, 3)
+    grads = orc.backward(q, k, v, g, w, dout, cu_seqlens=seg, eps=eps, init_state=init,
+                         d_final_state=dfin)
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, g, w, init)]
+    out, fs = _torch_forward(*ts[:5], seg, eps, ts[5])
+    L = (out * torch.tensor(dout)).sum() + (fs * torch.tensor(dfin)).sum()
+    ref = torch.autograd.grad(L, ts)
+    for n, r in zip(("dq", "dk", "dv", "dg", "dw", "d_init"), ref):
+        assert rel(grads[n], r.numpy()) < 1e-11, (n, rel(grads[n], r.numpy()))
+
+
+def pin_backward_final_state_only(orc):
+    """dout = 0: only the final state carries gradient, so dq = dg = dw = 0,
+    dL/dS0 = dfin, and every token sees dS_t = dfin: dk_t = (v~_t dfin^T) SiLU'(k_t),
+    dv_t = (k~_t dfin) SiLU'(v_t), with SiLU' from scipy's expit."""
+    T, H, D, seg = 9, 2, 4, [0, 4, 9]
+    q, k, v, g, w, init, _, dfin = _bwd_inputs(113, T, H, D, 2)
+    grads = orc.backward(q, k, v, g, w, np.zeros((T, H, D)), cu_seqlens=seg, init_state=init,
+                         d_final_state=dfin)
+    for n in ("dq", "dg", "dw"):
+        assert np.all(grads[n] == 0.0), n
+    assert rel(grads["d_init"], dfin) < TIGHT
+    dsilu = lambda x: expit(x) * (1.0 + x * (1.0 - expit(x)))
+    silu = lambda x: x * expit(x)
+    for s in range(2):
+        for t in range(seg[s], seg[s + 1]):
+            for h in range(H):
+                dk = (dfin[s, h] @ silu(v[t, h])) * dsilu(k[t, h])
+                dv = (silu(k[t, h]) @ dfin[s, h]) * dsilu(v[t, h])
+                assert rel(grads["dk"][t, h], dk) < TIGHT
+                assert rel(grads["dv"][t, h], dv) < TIGHT
+
+
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_autograd,
+                 pin_backward_final_state_only]
+
 ALL_PINS = [pin_elementwise, pin_brute_force, pin_first_token, pin_constant_closed_form,
             pin_rmsnorm_invariant, pin_causality, pin_head_permutation, pin_blocked,
-            pin_decode_after_prefill, pin_segments_and_resume]
+            pin_decode_after_prefill, pin_segments_and_resume] + BACKWARD_PINS

@@ -73,6 +73,35 @@ MUTANTS = [
      "            for (int64_t i = 0; i < D; ++i)\n"
      "                for (int64_t j = 0; j < D; ++j) S[i * D + j] += silu(k[base + i]) * silu(v[base + j]);\n"),
     ("blocked_mask_strict", "for (int64_t c = 0; c <= a; ++c)", "for (int64_t c = 0; c < a; ++c)"),
+    # backward
+    ("bwd_norm_mean_term_dropped", "dy[e] = r * (a - yhat[e] * ay / (double)HD);", "dy[e] = r * a;"),
+    ("bwd_dq_state_not_transposed", "acc += dy[base + j] * S[i * D + j];",
+     "acc += dy[base + j] * S[j * D + i];"),
+    ("bwd_dk_uses_k", "acc += S[i * D + j] * vt[j];", "acc += S[i * D + j] * kt[j];"),
+    ("bwd_dv_silu_grad_missing", "dv[base + j] = acc * silu_grad(v[base + j]);", "dv[base + j] = acc;"),
+    ("bwd_gate_derivative", "dg[e] = dout[e] * yhat[e] * w[i] * sg * (1.0 - sg);",
+     "dg[e] = dout[e] * yhat[e] * w[i] * sg;"),
+    ("bwd_dw_without_gate", "acc += dout[t * HD + i] * yhat[t * HD + i] * sigmoid(g[t * HD + i]);",
+     "acc += dout[t * HD + i] * yhat[t * HD + i];"),
+    ("bwd_final_state_gradient_ignored",
+     "            if (d_final) memcpy(S, d_final + (s * H + h) * D * D, sizeof(double) * D * D);\n"
+     "            else memset(S, 0, sizeof(double) * D * D);\n",
+     "            memset(S, 0, sizeof(double) * D * D);\n"),
+    ("bwd_state_gradient_one_token_late",
+     "                for (int64_t i = 0; i < D; ++i)\n"
+     "                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += qt[i] * dy[base + j];\n"
+     "                for (int64_t i = 0; i < D; ++i) {\n"
+     "                    double acc = 0.0;\n"
+     "                    for (int64_t j = 0; j < D; ++j) acc += S[i * D + j] * vt[j];\n"
+     "                    dk[base + i] = acc * silu_grad(k[base + i]);\n"
+     "                }\n",
+     "                for (int64_t i = 0; i < D; ++i) {\n"
+     "                    double acc = 0.0;\n"
+     "                    for (int64_t j = 0; j < D; ++j) acc += S[i * D + j] * vt[j];\n"
+     "                    dk[base + i] = acc * silu_grad(k[base + i]);\n"
+     "                }\n"
+     "                for (int64_t i = 0; i < D; ++i)\n"
+     "                    for (int64_t j = 0; j < D; ++j) S[i * D + j] += qt[i] * dy[base + j];\n"),
 ]
 
 
