@@ -17,6 +17,7 @@ count, the per-kernel split (HIP events recorded between the library's
 kernels on the stream they run on: the plan, the chunk sums, the scan of the
 states entering the chunks, and the walk with the RMSNorm fused), the
 roofline of the walk kernel, the state-only pass on the same K and V, the
+backward pass on the same inputs (time per call against its HBM bytes), the
 decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
 as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores.
@@ -228,6 +229,45 @@ def bench_prefill(args, la, torch, hip):
     return res
 
 
+def bench_backward(args, la, torch, inputs):
+    """Backward pass of the 8K workload: the gradients of every input for a
+    random output gradient (no final-state gradient).  Algorithmic HBM bytes:
+    read q, k, v, gate, dout and write dq, dk, dv, dgate, 2 bytes each per
+    (token, head, d)."""
+    cfg = PREFILL_8K
+    B, N, H, D = cfg["batch"], cfg["seqlen"], cfg["heads"], cfg["head_dim"]
+    dt = torch.bfloat16
+    to = lambda a: torch.from_numpy(a).cuda().to(dt).view(B, N, H, D).contiguous()
+    q, k, v, g, w = inputs
+    x = [to(a) for a in (q, k, v, g)]
+    wd = torch.from_numpy(w).cuda().to(dt)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2025 * 1000 + 77)
+    dout = torch.randn(B, N, H, D, device="cuda", generator=gen).to(dt)
+    ws = torch.empty(la.backward_workspace_size(B * N, B, H, D, cfg["block"], 0), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: la.backward(*x, wd, dout, block=cfg["block"], eps=cfg["eps"], workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    n = 10
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    nbytes = 9 * B * N * H * D * 2
+    res = dict(workload=cfg["workload"] + "_backward", us_per_call=round(us, 1),
+               tokens_per_s=round(B * N / (us * 1e-6), 1), algorithmic_bytes=nbytes,
+               hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    log("backward: %.1f us/call (%.2f%% of the HBM roofline)" % (us, 100 * res["hbm_frac"]))
+    del x, dout, ws
+    return res
+
+
 def bench_decode(args, la, torch, hip):
     from long_context_attn_amd import synth
     cfg = DECODE_256
@@ -415,6 +455,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-long", action="store_true", help="skip the 1M-token workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-pass", action="store_true",
@@ -438,6 +479,7 @@ def main():
         return
     hip = Hip()
     pre = bench_prefill(args, la, torch, hip)
+    bwd = None if args.no_backward else bench_backward(args, la, torch, pre["inputs"])
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)
     long_ctx = None if args.no_long else bench_long(args, la, torch)
     cpu = None
@@ -467,6 +509,7 @@ def main():
         "kernels_us": pre["kernels_us"],
         "roofline": pre["roofline"],
         "state_only": pre["state_only"],
+        "backward": bwd,
         "decode": dec,
         "long_context": long_ctx,
         "cpu_baseline": cpu,

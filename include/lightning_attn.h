@@ -150,6 +150,51 @@ LA_API la_status lightning_attn_state_varlen(const void* k, const void* v,
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream);
 
+/*
+ * Backward pass: gradients of a prefill (same inputs, same eps) for a loss L
+ * given dL/dout and, optionally, dL/d(final state).  By the chain rule
+ * through Mechanism steps 4, 3, 2 in reverse:
+ *     a = dout * w * sigmoid(gate),  yhat = y * r  (y, r as in the forward)
+ *     dy    = r * (a - yhat * mean_{h,d}(a * yhat))            per token
+ *     dgate = dout * yhat * w * sigmoid(gate) * (1 - sigmoid(gate))
+ *     dw    = sum over tokens of dout * yhat * sigmoid(gate)
+ *     dS_t  = dS_final + sum_{u >= t} q~_u^T dy_u              (dL/dS_t)
+ *     dq = (dy_t S_t^T) * SiLU'(q),  dk = (v~_t dS_t^T) * SiLU'(k),
+ *     dv = (k~_t dS_t) * SiLU'(v),   dS0 = dS at the sequence's first token
+ * with SiLU'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))).  y is recomputed.
+ *   q, k, v, gate, dout, dq, dk, dv, dgate: [batch][seqlen][heads][head_dim]
+ *                    (or packed [total][heads][head_dim] with cu_seqlens)
+ *   norm_weight:     [heads*head_dim], dtype of the activations
+ *   dweight:         [heads*head_dim] fp32, required
+ *   initial_state:   [nseq][heads][head_dim][head_dim] fp32 or NULL (zeros)
+ *   d_final_state:   same shape, or NULL (no gradient reaches the final state)
+ *   d_initial_state: same shape, or NULL (not written)
+ * All arithmetic is fp32 (portable vector-ALU kernels, any supported shape);
+ * the workspace holds fp32 copies of q~, k~, v~, y and dy (20 bytes per
+ * element of q) plus two states per chunk.  chunk_tokens: 0 = automatic, or
+ * a multiple of `block` (the result does not depend on it beyond rounding).
+ * Outputs must not alias inputs.  Errors as for the prefill.
+ */
+LA_API size_t lightning_attn_backward_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                                     int head_dim, int block, int chunk_tokens,
+                                                     la_dtype dtype);
+LA_API la_status lightning_attn_backward(const void* q, const void* k, const void* v,
+                                         const void* gate, const void* norm_weight,
+                                         const void* dout, const float* initial_state,
+                                         const float* d_final_state, void* dq, void* dk, void* dv,
+                                         void* dgate, float* dweight, float* d_initial_state,
+                                         int batch, int64_t seqlen, int heads, int head_dim,
+                                         int block, int chunk_tokens, float eps, la_dtype dtype,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+LA_API la_status lightning_attn_backward_varlen(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    const void* dout, const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+    const float* initial_state, const float* d_final_state, void* dq, void* dk, void* dv,
+    void* dgate, float* dweight, float* d_initial_state, int heads, int head_dim, int block,
+    int chunk_tokens, float eps, la_dtype dtype, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
 /* Workspace bytes needed by lightning_attn_decode. */
 LA_API size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim);
 

@@ -1,16 +1,17 @@
 """Lightning Attention (MiniMax-01 linear-attention layer) on AMD MI355X.
 
-    from long_context_attn_amd import prefill, prefill_varlen, state, state_varlen, decode
+    from long_context_attn_amd import prefill, prefill_varlen, state, backward, decode
 
 The compute path is liblightning_attn.so (hand-written HIP kernels for
 gfx950, C ABI in include/lightning_attn.h); this package only marshals torch
 tensors into it.  There is no CPU fallback: if the library is not built the
 calls raise.
 """
-from .ops import (LightningAttnError, decode, decode_workspace_size, library, prefill,  # noqa: F401
+from .ops import (LightningAttnError, backward, backward_varlen,  # noqa: F401
+                  backward_workspace_size, decode, decode_workspace_size, library, prefill,
                   prefill_varlen, prefill_workspace_size, state, state_varlen,
                   state_workspace_size, status_string)
 
-__all__ = ["prefill", "prefill_varlen", "state", "state_varlen", "decode",
-           "prefill_workspace_size", "state_workspace_size", "decode_workspace_size", "library",
-           "status_string", "LightningAttnError"]
+__all__ = ["prefill", "prefill_varlen", "state", "state_varlen", "backward", "backward_varlen",
+           "decode", "prefill_workspace_size", "state_workspace_size", "backward_workspace_size",
+           "decode_workspace_size", "library", "status_string", "LightningAttnError"]

@@ -127,6 +127,60 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     return true;
 }
 
+// Backward workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks],
+// the forward chunk states and the reverse ones [max_chunks][H][D][D] fp32,
+// q~, k~, v~, y, dy [total][H][D] fp32 and the dw partial sums
+// [ceil(total / norm tokens)][H*D] fp32.  Automatic chunks: the longest
+// power of two (at least the block) that gives about 8 (chunk, head) walks
+// per CU, since each walk is a workgroup of only head_dim threads.
+struct BwdLayout {
+    int chunk = 0, max_chunks = 0, n_tb = 0;
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_gstates = 0, off_qs = 0, off_ks = 0,
+           off_vs = 0, off_y = 0, off_dy = 0, off_dw = 0, bytes = 0;
+};
+
+bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
+                     BwdLayout* L) {
+    if (total < 0 || nseq < 0 || heads < 1 || chunk_tokens < 0 || !supported_dim(head_dim) ||
+        !supported_block(block))
+        return false;
+    int chunk = chunk_tokens;
+    if (chunk == 0) {
+        const int64_t per = total * heads / (8 * (int64_t)la::device_cu_count());
+        int64_t c = block;
+        while (c * 2 <= per && c < 8192) c *= 2;
+        chunk = (int)c;
+    }
+    if (chunk < block || chunk % block != 0) return false;
+    const int64_t maxc = total / chunk + nseq;
+    if (maxc * heads > (int64_t)0x7fffffff) return false;
+    const int64_t ntb = (total + la::backward_norm_tokens() - 1) / la::backward_norm_tokens();
+    if (ntb > (int64_t)0x7fffffff) return false;
+    L->chunk = chunk;
+    L->max_chunks = (int)maxc;
+    L->n_tb = (int)ntb;
+    const size_t DD = (size_t)head_dim * head_dim;
+    const size_t act = sizeof(float) * (size_t)total * heads * head_dim;
+    size_t off = align_up(sizeof(la::PlanHeader));
+    L->off_segs = off;
+    off = align_up(off + sizeof(la::SegEntry) * (size_t)nseq);
+    L->off_chunks = off;
+    off = align_up(off + sizeof(la::ChunkEntry) * (size_t)maxc);
+    L->off_states = off;
+    off = align_up(off + sizeof(float) * (size_t)maxc * heads * DD);
+    L->off_gstates = off;
+    off = align_up(off + sizeof(float) * (size_t)maxc * heads * DD);
+    size_t* acts[5] = {&L->off_qs, &L->off_ks, &L->off_vs, &L->off_y, &L->off_dy};
+    for (size_t* o : acts) {
+        *o = off;
+        off = align_up(off + act);
+    }
+    L->off_dw = off;
+    off = align_up(off + sizeof(float) * (size_t)ntb * heads * head_dim);
+    L->bytes = off;
+    return true;
+}
+
 la_status check_dtype(la_dtype dtype) {
     return (dtype == LA_DTYPE_F32 || dtype == LA_DTYPE_BF16) ? LA_OK : LA_ERR_UNSUPPORTED;
 }
@@ -466,6 +520,115 @@ la_status lightning_attn_state_varlen(const void* k, const void* v, const int32_
     a.H = heads; a.D = head_dim; a.block = block;
     a.bf16 = dtype == LA_DTYPE_BF16;
     return run_state(a, L, workspace, stream);
+}
+
+size_t lightning_attn_backward_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                              int head_dim, int block, int chunk_tokens,
+                                              la_dtype dtype) {
+    if (check_dtype(dtype) != LA_OK) return 0;
+    BwdLayout L;
+    if (!backward_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, &L)) return 0;
+    return L.bytes;
+}
+
+// Shared checks and launch of the backward (batch rows when cu == null).
+static la_status backward_impl(const void* q, const void* k, const void* v, const void* gate,
+                               const void* norm_weight, const void* dout,
+                               const float* initial_state, const float* d_final_state, void* dq,
+                               void* dk, void* dv, void* dgate, float* dweight,
+                               float* d_initial_state, const int32_t* cu, int nseq,
+                               int64_t seqlen, int64_t total, int heads, int head_dim, int block,
+                               int chunk_tokens, float eps, la_dtype dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (heads < 1 || chunk_tokens < 0 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
+    if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
+        return LA_ERR_UNSUPPORTED;
+    if (total > 0) {
+        la_status st = check_ptrs(q, k, v, gate, norm_weight, dout);
+        if (st != LA_OK) return st;
+        st = check_ptrs(dq, dk, dv, dgate, dweight, dweight);
+        if (st != LA_OK) return st;
+    }
+    if (nseq > 0 && !dweight) return LA_ERR_NULL_POINTER;
+    if (dweight && !aligned16(dweight)) return LA_ERR_MISALIGNED;
+    if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
+    if (d_final_state && !aligned16(d_final_state)) return LA_ERR_MISALIGNED;
+    if (d_initial_state && !aligned16(d_initial_state)) return LA_ERR_MISALIGNED;
+    BwdLayout L;
+    if (!backward_layout(total, nseq, heads, head_dim, block, chunk_tokens, &L))
+        return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (nseq == 0) return LA_OK;
+    char* ws = static_cast<char*>(workspace);
+    la::BackwardArgs a{};
+    la::PrefillArgs& p = a.p;
+    p.q = q; p.k = k; p.v = v; p.g = gate; p.w = norm_weight;
+    p.init_state = initial_state;
+    p.cu = cu;
+    p.nseq = nseq;
+    p.seqlen = seqlen;
+    p.total = total;
+    p.H = heads; p.D = head_dim; p.block = block;
+    p.eps = eps;
+    p.bf16 = dtype == LA_DTYPE_BF16;
+    p.chunk = L.chunk;
+    p.max_chunks = L.max_chunks;
+    p.hdr = reinterpret_cast<la::PlanHeader*>(ws);
+    p.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
+    p.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
+    p.states = reinterpret_cast<float*>(ws + L.off_states);
+    a.stream = stream;
+    a.dout = dout;
+    a.d_final = d_final_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dgate;
+    a.dw = dweight;
+    a.d_init = d_initial_state;
+    a.gstates = reinterpret_cast<float*>(ws + L.off_gstates);
+    a.qs = reinterpret_cast<float*>(ws + L.off_qs);
+    a.ks = reinterpret_cast<float*>(ws + L.off_ks);
+    a.vs = reinterpret_cast<float*>(ws + L.off_vs);
+    a.y = reinterpret_cast<float*>(ws + L.off_y);
+    a.dy = reinterpret_cast<float*>(ws + L.off_dy);
+    a.dw_part = reinterpret_cast<float*>(ws + L.off_dw);
+    a.n_tb = L.n_tb;
+    hipError_t e = la::launch_plan(p, stream);
+    if (e == hipSuccess) e = la::launch_backward(a);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status lightning_attn_backward(const void* q, const void* k, const void* v, const void* gate,
+                                  const void* norm_weight, const void* dout,
+                                  const float* initial_state, const float* d_final_state,
+                                  void* dq, void* dk, void* dv, void* dgate, float* dweight,
+                                  float* d_initial_state, int batch, int64_t seqlen, int heads,
+                                  int head_dim, int block, int chunk_tokens, float eps,
+                                  la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    if (batch < 0 || seqlen < 0) return LA_ERR_BAD_SHAPE;
+    if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
+    return backward_impl(q, k, v, gate, norm_weight, dout, initial_state, d_final_state, dq, dk,
+                         dv, dgate, dweight, d_initial_state, nullptr, batch, seqlen,
+                         (int64_t)batch * seqlen, heads, head_dim, block, chunk_tokens, eps, dtype,
+                         workspace, workspace_bytes, stream);
+}
+
+la_status lightning_attn_backward_varlen(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    const void* dout, const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+    const float* initial_state, const float* d_final_state, void* dq, void* dk, void* dv,
+    void* dgate, float* dweight, float* d_initial_state, int heads, int head_dim, int block,
+    int chunk_tokens, float eps, la_dtype dtype, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+    if (nseq < 0 || total_tokens < 0 || total_tokens > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
+    if (nseq == 0 && total_tokens != 0) return LA_ERR_BAD_SHAPE;
+    if (nseq > 0 && !cu_seqlens) return LA_ERR_NULL_POINTER;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return LA_ERR_MISALIGNED;
+    return backward_impl(q, k, v, gate, norm_weight, dout, initial_state, d_final_state, dq, dk,
+                         dv, dgate, dweight, d_initial_state, cu_seqlens, nseq, 0, total_tokens,
+                         heads, head_dim, block, chunk_tokens, eps, dtype, workspace,
+                         workspace_bytes, stream);
 }
 
 size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {

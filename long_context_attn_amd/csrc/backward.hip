@@ -1,0 +1,355 @@
+// Backward pass of the Lightning Attention layer: portable fp32 vector-ALU
+// kernels (any supported head_dim / block, fp32 or bf16 storage).
+//
+// The forward is Mechanism steps 2-4 of "Diving into MiniMax01 405B MoE"
+// (section "Hybrid Modeling"): q~, k~, v~ = SiLU(q, k, v), S_t = S0 +
+// sum_{u<=t} k~_u^T v~_u, y_t = q~_t S_t, out = y r w sigmoid(g) with
+// r = (mean_{h,d} y^2 + eps)^-1/2.  Given dout (and optionally dS_final, the
+// gradient reaching the final state), the chain rule in reverse gives:
+//   norm:  a = dout w sigmoid(g), yhat = y r:  dy = r (a - yhat <a, yhat> / HD),
+//          dgate = dout yhat w sigmoid'(g),  dw = sum_t dout yhat sigmoid(g);
+//   state: dS_t = dS_final + sum_{u>=t} q~_u^T dy_u  (the gradient w.r.t. S_t),
+//          dq~_t = dy_t S_t^T,  dk~_t = v~_t dS_t^T,  dv~_t = k~_t dS_t,
+//          dS0 = dS at the first token;
+//   input: dq = dq~ SiLU'(q), and likewise for k and v.
+// Each of y, dq~, dk~ and dv~ is one linear-attention walk over the chunks,
+//   Y_t = X_t R + sum_{u in window(t), same chunk} (X_t . K_u) V_u,
+// causal (u <= t, R = the state entering the chunk from the left) or
+// anti-causal (u >= t, R = the state entering from the right):
+//   y   = causal(q~, k~, v~, S_entry)          dq~ = causal(dy, v~, k~, S_entry^T)
+//   dk~ = anti-causal(v~, dy, q~, G_exit^T)    dv~ = anti-causal(k~, q~, dy, G_exit)
+// with S_entry from the forward prefix of the chunk sums sum k~^T v~ and
+// G_exit = dS_final + the suffix of the chunk sums sum q~^T dy.
+#include "la_internal.h"
+
+namespace la {
+
+namespace {
+
+constexpr int EW_THREADS = 256;  // elementwise and norm kernels
+constexpr int NB_TOKENS = 32;    // tokens per workgroup of the norm backward
+
+__device__ __forceinline__ float silu_grad_f(float x) {
+    const float s = sigmoid_f(x);
+    return s * (1.0f + x * (1.0f - s));
+}
+
+// q~, k~, v~ = SiLU(q, k, v) in fp32
+template <class TT>
+__global__ __launch_bounds__(EW_THREADS) void silu3_kernel(const TT* __restrict__ q,
+                                                           const TT* __restrict__ k,
+                                                           const TT* __restrict__ v,
+                                                           float* __restrict__ qs,
+                                                           float* __restrict__ ks,
+                                                           float* __restrict__ vs, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * EW_THREADS) {
+        qs[i] = silu_f(to_f32(q[i]));
+        ks[i] = silu_f(to_f32(k[i]));
+        vs[i] = silu_f(to_f32(v[i]));
+    }
+}
+
+// states[c][h][i][j] = sum over chunk c's tokens u of X_u[i] Y_u[j]
+template <int D>
+__global__ __launch_bounds__(D) void chunk_sum_kernel(const float* __restrict__ X,
+                                                      const float* __restrict__ Y,
+                                                      const PlanHeader* __restrict__ hdr,
+                                                      const ChunkEntry* __restrict__ chunks,
+                                                      float* __restrict__ states, int H) {
+    constexpr int TILE = 16;
+    __shared__ float xs[TILE][D];
+    __shared__ float ys[TILE][D];
+    const int c = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    if (c >= hdr->n_chunks) return;
+    const ChunkEntry ce = chunks[c];
+    const int j = threadIdx.x;
+    const int64_t HD = (int64_t)H * D;
+    float acc[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc[i] = 0.f;
+    for (int t0 = 0; t0 < ce.len; t0 += TILE) {
+        const int n = min(TILE, ce.len - t0);
+        for (int a = 0; a < TILE; ++a) {
+            const int64_t idx = (ce.start + t0 + a) * HD + (int64_t)h * D + j;
+            xs[a][j] = a < n ? X[idx] : 0.f;
+            ys[a][j] = a < n ? Y[idx] : 0.f;
+        }
+        __syncthreads();
+        for (int a = 0; a < n; ++a) {
+            const float yj = ys[a][j];
+#pragma unroll
+            for (int i = 0; i < D; ++i) acc[i] += xs[a][i] * yj;
+        }
+        __syncthreads();
+    }
+    float* dst = states + ((int64_t)c * H + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) dst[i * D + j] = acc[i];
+}
+
+// Reverse exclusive scan per (sequence, head): each chunk sum B_c is replaced
+// by G_exit(c) = dS_final + sum_{c' > c} B_c'; dS0 = dS_final + sum_c B_c.
+constexpr int RSCAN_THREADS = 256;
+__global__ __launch_bounds__(RSCAN_THREADS) void reverse_scan_kernel(
+    float* __restrict__ states, const SegEntry* __restrict__ segs, const float* d_final,
+    float* d_init, int H, int DD, int tiles) {
+    const int pair = blockIdx.x / tiles;
+    const int tile = blockIdx.x - pair * tiles;
+    const int e = (tile * RSCAN_THREADS + threadIdx.x) * 4;
+    if (e >= DD) return;
+    const int s = pair / H, h = pair - s * H;
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    if (d_final != nullptr) run = *reinterpret_cast<const f32x4*>(d_final + (int64_t)pair * DD + e);
+    const SegEntry se = segs[s];
+    for (int c = se.first + se.count - 1; c >= se.first; --c) {
+        f32x4* p = reinterpret_cast<f32x4*>(states + ((int64_t)c * H + h) * DD + e);
+        const f32x4 sum = *p;
+        *p = run;
+        run += sum;
+    }
+    if (d_init != nullptr) *reinterpret_cast<f32x4*>(d_init + (int64_t)pair * DD + e) = run;
+}
+
+// One linear-attention walk per (chunk, head), a workgroup of D threads;
+// thread j owns column j of the D x D fp32 running state R (D registers).
+// REV: anti-causal (blocks last to first, u >= t); TRS: R starts as the
+// transpose of the chunk's state.  EPI = 0: Y to yout (fp32); EPI = 1:
+// gout = Y * SiLU'(raw) in TT.
+template <class TT, int D, int BK, bool REV, bool TRS, int EPI>
+__global__ __launch_bounds__(D) void lin_walk_kernel(
+    const float* __restrict__ Xm, const float* __restrict__ Km, const float* __restrict__ Vm,
+    const PlanHeader* __restrict__ hdr, const ChunkEntry* __restrict__ chunks,
+    const float* __restrict__ states, float* __restrict__ yout, const TT* __restrict__ raw,
+    TT* __restrict__ gout, int H) {
+    extern __shared__ float lds[];
+    float* xs = lds;              // [BK][D]
+    float* ks = xs + BK * D;      // [BK][D]
+    float* vs = ks + BK * D;      // [BK][D]
+    float* sc = vs + BK * D;      // [BK][BK] scores X_a . K_b
+    const int c = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    if (c >= hdr->n_chunks) return;
+    const ChunkEntry ce = chunks[c];
+    const int j = threadIdx.x;
+    const int64_t HD = (int64_t)H * D;
+    float R[D];
+    const float* src = states + ((int64_t)c * H + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) R[i] = TRS ? src[j * D + i] : src[i * D + j];
+    const int nblk = (ce.len + BK - 1) / BK;
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int t0 = (REV ? nblk - 1 - bi : bi) * BK;
+        const int n = min(BK, ce.len - t0);
+        for (int a = 0; a < BK; ++a) {
+            const int64_t idx = (ce.start + t0 + a) * HD + (int64_t)h * D + j;
+            const bool ok = a < n;
+            xs[a * D + j] = ok ? Xm[idx] : 0.f;
+            ks[a * D + j] = ok ? Km[idx] : 0.f;
+            vs[a * D + j] = ok ? Vm[idx] : 0.f;
+        }
+        __syncthreads();
+        // scores inside the window (entries outside it are never read)
+        for (int p = j; p < BK * BK; p += D) {
+            const int a = p / BK, b = p - (p / BK) * BK;
+            float s = 0.f;
+            if ((REV ? b >= a : b <= a) && a < n && b < n) {
+                for (int i = 0; i < D; ++i) s += xs[a * D + i] * ks[b * D + i];
+            }
+            sc[p] = s;
+        }
+        __syncthreads();
+        for (int a = 0; a < n; ++a) {
+            float y = 0.f;
+#pragma unroll
+            for (int i = 0; i < D; ++i) y += xs[a * D + i] * R[i];  // the state entering the block
+            if (REV) {
+                for (int b = a; b < n; ++b) y += sc[a * BK + b] * vs[b * D + j];
+            } else {
+                for (int b = 0; b <= a; ++b) y += sc[a * BK + b] * vs[b * D + j];
+            }
+            const int64_t idx = (ce.start + t0 + a) * HD + (int64_t)h * D + j;
+            if (EPI == 0) yout[idx] = y;
+            else gout[idx] = from_f32<TT>(y * silu_grad_f(to_f32(raw[idx])));
+        }
+        // the block's contribution, after its outputs used the state before it
+        for (int a = 0; a < n; ++a) {
+            const float vj = vs[a * D + j];
+#pragma unroll
+            for (int i = 0; i < D; ++i) R[i] += ks[a * D + i] * vj;
+        }
+        __syncthreads();
+    }
+}
+
+// Norm backward: one workgroup per NB_TOKENS consecutive tokens.  Per token:
+// r and <a, yhat> by block reductions, then dy (fp32) and dgate; dw is
+// accumulated over the workgroup's tokens and written as a partial sum.
+template <class TT>
+__global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
+    const float* __restrict__ y, const TT* __restrict__ g, const TT* __restrict__ w,
+    const TT* __restrict__ dout, float* __restrict__ dy, TT* __restrict__ dg,
+    float* __restrict__ dw_part, int64_t T, int HD, float eps) {
+    __shared__ float red[2][EW_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t t_begin = (int64_t)blockIdx.x * NB_TOKENS;
+    const int64_t t_end = min(T, t_begin + NB_TOKENS);
+    float* part = dw_part + (int64_t)blockIdx.x * HD;
+    for (int i = tid; i < HD; i += EW_THREADS) part[i] = 0.f;
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int64_t base = t * HD;
+        float ss = 0.f, ay = 0.f;
+        for (int i = tid; i < HD; i += EW_THREADS) {
+            const float yi = y[base + i];
+            ss += yi * yi;
+            ay += to_f32(dout[base + i]) * to_f32(w[i]) * sigmoid_f(to_f32(g[base + i])) * yi;
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            ss += __shfl_xor(ss, off);
+            ay += __shfl_xor(ay, off);
+        }
+        if (lane == 0) {
+            red[0][wv] = ss;
+            red[1][wv] = ay;
+        }
+        __syncthreads();
+        ss = 0.f;
+        ay = 0.f;
+#pragma unroll
+        for (int i = 0; i < EW_THREADS / 64; ++i) {
+            ss += red[0][i];
+            ay += red[1][i];
+        }
+        __syncthreads();
+        const float r = __builtin_amdgcn_rsqf(ss / (float)HD + eps);
+        const float m = ay * r / (float)HD;  // <a, yhat> / HD
+        for (int i = tid; i < HD; i += EW_THREADS) {
+            const float yh = y[base + i] * r;
+            const float sg = sigmoid_f(to_f32(g[base + i]));
+            const float go = to_f32(dout[base + i]);
+            const float wi = to_f32(w[i]);
+            dy[base + i] = r * (go * wi * sg - yh * m);
+            dg[base + i] = from_f32<TT>(go * yh * wi * sg * (1.0f - sg));
+            part[i] += go * yh * sg;
+        }
+    }
+}
+
+// dw[i] = sum of the partial sums in workgroup order (deterministic)
+__global__ __launch_bounds__(EW_THREADS) void dw_reduce_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ dw, int nparts,
+                                                               int HD) {
+    const int i = blockIdx.x * EW_THREADS + threadIdx.x;
+    if (i >= HD) return;
+    float acc = 0.f;
+    for (int p = 0; p < nparts; ++p) acc += part[(int64_t)p * HD + i];
+    dw[i] = acc;
+}
+
+// Walk block: 16 tokens whatever the forward's block (the result does not
+// depend on it beyond rounding); the small LDS footprint lets several
+// workgroups share a CU.
+constexpr int WALK_BK = 16;
+
+unsigned ew_grid(int64_t n) {
+    int64_t b = (n + EW_THREADS - 1) / EW_THREADS;
+    return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
+}
+
+template <class TT, int D, int BK, bool REV, bool TRS, int EPI>
+hipError_t walk(const BackwardArgs& a, const float* X, const float* K, const float* V,
+                const float* states, float* yout, const void* raw, void* gout) {
+    const dim3 grid((unsigned)((int64_t)a.p.max_chunks * a.p.H));
+    const size_t lds = sizeof(float) * (3 * BK * D + BK * BK);
+    auto* fn = &lin_walk_kernel<TT, D, BK, REV, TRS, EPI>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, grid, dim3(D), lds, a.stream, X, K, V, a.p.hdr, a.p.chunks, states,
+                       yout, (const TT*)raw, (TT*)gout, a.p.H);
+    return hipGetLastError();
+}
+
+template <class TT, int D, int BK>
+hipError_t backward_db(const BackwardArgs& a) {
+    const PrefillArgs& p = a.p;
+    hipStream_t st = a.stream;
+    const int64_t n = p.total * p.H * D;
+    const int HD = p.H * D;
+    const dim3 cgrid((unsigned)((int64_t)p.max_chunks * p.H));
+    hipError_t e = hipSuccess;
+    // q~, k~, v~; forward chunk sums and the states entering the chunks
+    hipLaunchKernelGGL((silu3_kernel<TT>), dim3(ew_grid(n)), dim3(EW_THREADS), 0, st,
+                       (const TT*)p.q, (const TT*)p.k, (const TT*)p.v, a.qs, a.ks, a.vs, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_sum_kernel<D>), cgrid, dim3(D), 0, st, a.ks, a.vs, p.hdr, p.chunks,
+                       p.states, p.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        PrefillArgs s = p;
+        s.final_state = nullptr;
+        s.skip_last = false;
+        if ((e = launch_state_scan(s, st)) != hipSuccess) return e;
+    }
+    // y, then the norm backward: dy, dgate, dw
+    if ((e = walk<TT, D, BK, false, false, 0>(a, a.qs, a.ks, a.vs, p.states, a.y, nullptr,
+                                               nullptr)) != hipSuccess)
+        return e;
+    if (a.n_tb > 0) {
+        hipLaunchKernelGGL((norm_backward_kernel<TT>), dim3((unsigned)a.n_tb), dim3(EW_THREADS), 0,
+                           st, a.y, (const TT*)p.g, (const TT*)p.w, (const TT*)a.dout, a.dy,
+                           (TT*)a.dg, a.dw_part, p.total, HD, p.eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((HD + EW_THREADS - 1) / EW_THREADS)),
+                       dim3(EW_THREADS), 0, st, a.dw_part, a.dw, a.n_tb, HD);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // reverse chunk sums of q~^T dy, G_exit and dS0
+    hipLaunchKernelGGL((chunk_sum_kernel<D>), cgrid, dim3(D), 0, st, a.qs, a.dy, p.hdr, p.chunks,
+                       a.gstates, p.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        const int DD = D * D;
+        const int tiles = (DD / 4 + RSCAN_THREADS - 1) / RSCAN_THREADS;
+        const int64_t grid = (int64_t)p.nseq * p.H * tiles;
+        if (grid > 0) {
+            hipLaunchKernelGGL(reverse_scan_kernel, dim3((unsigned)grid), dim3(RSCAN_THREADS), 0,
+                               st, a.gstates, p.segs, a.d_final, a.d_init, p.H, DD, tiles);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    // the three input gradients
+    if ((e = walk<TT, D, BK, false, true, 1>(a, a.dy, a.vs, a.ks, p.states, nullptr, p.q, a.dq)) !=
+        hipSuccess)
+        return e;
+    if ((e = walk<TT, D, BK, true, true, 1>(a, a.vs, a.dy, a.qs, a.gstates, nullptr, p.k, a.dk)) !=
+        hipSuccess)
+        return e;
+    return walk<TT, D, BK, true, false, 1>(a, a.ks, a.qs, a.dy, a.gstates, nullptr, p.v, a.dv);
+}
+
+template <class TT>
+hipError_t backward_t(const BackwardArgs& a) {
+    switch (a.p.D) {
+        case 16: return backward_db<TT, 16, WALK_BK>(a);
+        case 32: return backward_db<TT, 32, WALK_BK>(a);
+        case 64: return backward_db<TT, 64, WALK_BK>(a);
+        case 128: return backward_db<TT, 128, WALK_BK>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int backward_norm_tokens() { return NB_TOKENS; }
+
+// After the plan: every kernel of the backward.  With no token at all the
+// token kernels find no chunk (or no token block) and return, dw comes out
+// zero and dS0 = dS_final (or zero).
+hipError_t launch_backward(const BackwardArgs& a) {
+    if (a.p.max_chunks == 0) return hipSuccess;
+    return a.p.bf16 ? backward_t<__bf16>(a) : backward_t<float>(a);
+}
+
+}  // namespace la

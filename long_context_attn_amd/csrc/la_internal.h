@@ -120,6 +120,24 @@ int lane_group_size();
 int lane_slices();
 hipError_t launch_prefill_lane(const PrefillArgs& a, hipStream_t st);
 
+// backward pass (portable fp32 kernels, any supported shape); the plan runs
+// first with the chunk table
+struct BackwardArgs {
+    PrefillArgs p;            // forward inputs, plan, chunk states (forward sums / S_entry)
+    hipStream_t stream;
+    const void* dout;         // [T][H][D] gradient w.r.t. the output
+    const float* d_final;     // [nseq][H][D][D] gradient w.r.t. the final states, or null
+    void *dq, *dk, *dv, *dg;  // [T][H][D] outputs
+    float* dw;                // [H*D] gradient w.r.t. the norm weight
+    float* d_init;            // [nseq][H][D][D] gradient w.r.t. the initial states, or null
+    // workspace: q~, k~, v~, y, dy [T][H][D] fp32; reverse chunk sums / G_exit
+    // [max_chunks][H][D][D]; dw partial sums [n_tb][H*D]
+    float *qs, *ks, *vs, *y, *dy, *gstates, *dw_part;
+    int n_tb;
+};
+int backward_norm_tokens();
+hipError_t launch_backward(const BackwardArgs& a);
+
 struct DecodeArgs {
     const void *q, *k, *v, *g, *w;
     void* out;

@@ -7,6 +7,7 @@ include/lightning_attn.h:
     prefill(q, k, v, gate, weight, ...)            q: [B, N, H, D]
     prefill_varlen(q, k, v, gate, weight, cu, ...) q: [T, H, D], cu: int32 [nseq+1]
     state(k, v, ...) / state_varlen(k, v, cu, ...) final states only, [nseq, H, D, D]
+    backward(q, k, v, gate, weight, dout, ...)     gradients of a prefill (and _varlen)
     decode(q, k, v, gate, weight, state, ...)      q: [S, H, D], state updated in place
 
 The layer is the Lightning Attention Mechanism of "Diving into MiniMax01 405B
@@ -65,6 +66,14 @@ def library():
         lib.lightning_attn_state_varlen.argtypes = [_P, _P, _P, _I, _I64, _P, _P, _I, _I, _I, _I,
                                                     _I, _P, _SZ, _P]
         lib.lightning_attn_state_varlen.restype = _I
+        lib.lightning_attn_backward_workspace_size.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        lib.lightning_attn_backward_workspace_size.restype = _SZ
+        lib.lightning_attn_backward.argtypes = [_P] * 14 + [_I, _I64, _I, _I, _I, _I, _F, _I, _P,
+                                                            _SZ, _P]
+        lib.lightning_attn_backward.restype = _I
+        lib.lightning_attn_backward_varlen.argtypes = ([_P] * 7 + [_I, _I64] + [_P] * 8 +
+                                                       [_I, _I, _I, _I, _F, _I, _P, _SZ, _P])
+        lib.lightning_attn_backward_varlen.restype = _I
         lib.lightning_attn_decode_workspace_size.argtypes = [_I, _I, _I]
         lib.lightning_attn_decode_workspace_size.restype = _SZ
         lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
@@ -266,6 +275,79 @@ def state_varlen(k, v, cu_seqlens, *, block=64, initial_state=None, final_state=
         _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, T, _ptr(init), _ptr(fs), H, D, int(block),
         int(chunk_tokens), _dtype(k), _ptr(ws), ws_bytes, _stream(dev)))
     return fs
+
+
+def backward_workspace_size(total_tokens, nseq, heads, head_dim, block=64, chunk_tokens=0,
+                            dtype=torch.bfloat16) -> int:
+    return int(library().lightning_attn_backward_workspace_size(
+        int(total_tokens), int(nseq), int(heads), int(head_dim), int(block), int(chunk_tokens),
+        LA_DTYPE[dtype]))
+
+
+def _backward_outputs(q, nseq, H, D, want_d_init):
+    dev = q.device
+    grads = [torch.empty_like(q) for _ in range(4)]
+    dw = torch.empty(H * D, dtype=torch.float32, device=dev)
+    d_init = torch.empty(nseq, H, D, D, dtype=torch.float32, device=dev) if want_d_init else None
+    return grads, dw, d_init
+
+
+def backward(q, k, v, gate, weight, dout, *, block=64, eps=1e-6, initial_state=None,
+             d_final_state=None, return_d_initial_state=False, chunk_tokens=0, workspace=None):
+    """Gradients of `prefill` for a loss with gradient `dout` w.r.t. the output (and
+    `d_final_state` w.r.t. the final states).  q, k, v, gate, dout: [B, N, H, D].
+    Returns (dq, dk, dv, dgate, dweight, d_initial_state or None); dweight and
+    d_initial_state are float32."""
+    _same(q, q, k, v, gate, weight, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, gate, dout)):
+        raise ValueError("q, k, v, gate, dout must share one [B, N, H, D] shape")
+    B, N, H, D = q.shape
+    if weight.numel() != H * D:
+        raise ValueError("weight must have H*D elements")
+    dev = q.device
+    init = _state(initial_state, (B, H, D, D), dev, "initial_state")
+    dfin = _state(d_final_state, (B, H, D, D), dev, "d_final_state")
+    (dq, dk, dv, dg), dw, d_init = _backward_outputs(q, B, H, D, return_d_initial_state)
+    ws_bytes = backward_workspace_size(B * N, B, H, D, block, chunk_tokens, q.dtype)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(init), _ptr(dfin),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), B, N, H, D, int(block),
+        int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    return dq, dk, dv, dg, dw, d_init
+
+
+def backward_varlen(q, k, v, gate, weight, dout, cu_seqlens, *, block=64, eps=1e-6,
+                    initial_state=None, d_final_state=None, return_d_initial_state=False,
+                    chunk_tokens=0, workspace=None):
+    """Gradients of `prefill_varlen`; q, k, v, gate, dout: [T, H, D], cu_seqlens int32."""
+    _same(q, q, k, v, gate, weight, dout)
+    if q.dim() != 3 or any(t.shape != q.shape for t in (k, v, gate, dout)):
+        raise ValueError("q, k, v, gate, dout must share one [T, H, D] shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector on the activations' device")
+    T, H, D = q.shape
+    nseq = cu_seqlens.numel() - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if weight.numel() != H * D:
+        raise ValueError("weight must have H*D elements")
+    dev = q.device
+    init = _state(initial_state, (nseq, H, D, D), dev, "initial_state")
+    dfin = _state(d_final_state, (nseq, H, D, D), dev, "d_final_state")
+    (dq, dk, dv, dg), dw, d_init = _backward_outputs(q, nseq, H, D, return_d_initial_state)
+    ws_bytes = backward_workspace_size(T, nseq, H, D, block, chunk_tokens, q.dtype)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_backward_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(cu_seqlens), nseq, T,
+        _ptr(init), _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), H,
+        D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    return dq, dk, dv, dg, dw, d_init
 
 
 def decode(q, k, v, gate, weight, state, *, eps=1e-6, out=None, workspace=None):

@@ -43,7 +43,7 @@ def demangle(name: str) -> str:
 
 def short_name(name: str) -> str:
     n = demangle(name).replace("void ", "")
-    m = re.match(r"_ZN2la(\d+)", n)
+    m = re.match(r"_ZN2la(?:12_GLOBAL__N_1)?(\d+)", n)
     if m:  # still mangled (bf16 template arguments): keep namespace and identifier
         k = int(m.group(1))
         ident = n[m.end():m.end() + k]

@@ -38,9 +38,10 @@ def test_header_declares_the_three_calls():
         assert n in names
     for n in ("lightning_attn_prefill_profiled", "lightning_attn_decode_profiled",
               "lightning_attn_state", "lightning_attn_state_varlen",
-              "lightning_attn_state_workspace_size"):
+              "lightning_attn_state_workspace_size", "lightning_attn_backward",
+              "lightning_attn_backward_varlen", "lightning_attn_backward_workspace_size"):
         assert n in names
-    assert len(names) == 15
+    assert len(names) == 18
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -190,6 +191,55 @@ def test_state_validation(lib):
     assert vcall(total=1 << 31) == SHAPE
     assert vcall(ws_bytes=8) == WS
     assert vcall(nseq=0, total=0, k=None, cu=None, fin=None) == OK
+
+
+def test_backward_workspace_size(lib):
+    # plan + two states per chunk + q~, k~, v~, y, dy in fp32 + dw partial sums per
+    # 32 tokens; automatic chunks give about 8 (chunk, head) walks per CU
+    T, H, D = 8192, 64, 128
+    act = 5 * T * H * D * 4
+    ws = ops.backward_workspace_size(T, 1, H, D, 64, 256)
+    need = act + 2 * (T // 256 + 1) * H * D * D * 4 + (T // 32) * H * D * 4
+    assert need <= ws < need + 65536
+    assert ops.backward_workspace_size(T, 1, H, D, 64, 0) > act
+    assert ops.backward_workspace_size(T, 1, H, 96, 64, 0) == 0
+    assert ops.backward_workspace_size(T, 1, H, D, 64, 100) == 0
+    assert ops.backward_workspace_size(T, 1, H, D, 64, -1) == 0
+    assert ops.backward_workspace_size(0, 0, H, D, 64, 0) > 0
+
+
+def test_backward_validation(lib):
+    def call(q=A, dq=A, dw=A, init=None, dfin=None, dinit=None, batch=2, seqlen=100, heads=2,
+             d=64, block=32, chunk=0, eps=1e-6, dtype=F32, ws=A, ws_bytes=1 << 40):
+        return lib.lightning_attn_backward(q, A, A, A, A, A, init, dfin, dq, A, A, A, dw, dinit,
+                                           batch, seqlen, heads, d, block, chunk, eps, dtype, ws,
+                                           ws_bytes, None)
+    assert call(q=None) == NULLP
+    assert call(dq=None) == NULLP
+    assert call(dw=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(q=A + 8) == MISAL
+    assert call(dfin=A + 4) == MISAL
+    assert call(dinit=A + 4) == MISAL
+    assert call(d=96) == UNSUP
+    assert call(block=48) == UNSUP
+    assert call(chunk=48) == UNSUP
+    assert call(dtype=9) == UNSUP
+    assert call(chunk=-1) == SHAPE
+    assert call(batch=-1) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(ws_bytes=64) == WS
+    assert call(batch=0, q=None, dq=None, dw=None) == OK
+
+    def vcall(cu=A, nseq=2, total=100, ws_bytes=1 << 40):
+        return lib.lightning_attn_backward_varlen(A, A, A, A, A, A, cu, nseq, total, None, None, A,
+                                                  A, A, A, A, None, 2, 64, 32, 0, 1e-6, F32, A,
+                                                  ws_bytes, None)
+    assert vcall(cu=None) == NULLP
+    assert vcall(cu=A + 2) == MISAL
+    assert vcall(nseq=0, total=5) == SHAPE
+    assert vcall(total=1 << 31) == SHAPE
+    assert vcall(ws_bytes=8) == WS
 
 
 def test_decode_validation(lib):

@@ -1,0 +1,156 @@
+"""Backward pass on the GPU against the oracle's gradient (needs an MI355X).
+
+Every gradient (dq, dk, dv, dgate, dweight, and the gradient w.r.t. the
+initial states) is compared with oracle.backward on the same seeded inputs,
+with a gradient reaching the final states as well as the output.  Metric:
+the layer's e_max / e_mean, relative to the largest reference magnitude of
+each tensor.  Arithmetic is fp32 on both sizes of the comparison (the oracle
+in fp64), so fp32 outputs meet the fp32 bar; bf16 outputs are rounded once
+to bf16 and meet the bf16 bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, check, dev, host, inputs, say
+import long_context_attn_amd as la
+from long_context_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = TOL[torch.float32][0]
+
+
+def rnd(seed, shape, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+def compare(grads, ref, dtype, what):
+    dq, dk, dv, dg, dw, d_init = grads
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
+        check(host(got).reshape(ref[name].shape), ref[name], dtype, "%s %s" % (what, name))
+    # fp32 outputs: the fp32 bar whatever the input dtype
+    for name, got in (("dw", dw), ("d_init", d_init)):
+        if got is None:
+            continue
+        emax, _ = oracle.compare(host(got), ref[name])
+        say("%s %s e_max=%.3e" % (what, name, emax))
+        assert emax <= F32_TOL, (what, name, emax)
+
+
+def batch_case(B, N, H, D, dtype, dist, key, with_states=True):
+    T = B * N
+    q, k, v, g, w = inputs(T, H, D, dist, bf16=dtype == torch.bfloat16, key=key)
+    dout = rnd(key + 100, (T, H, D))
+    if dtype == torch.bfloat16:
+        dout = host(dev(dout, torch.bfloat16))
+    init = rnd(key + 101, (B, H, D, D), 0.5) if with_states else None
+    dfin = rnd(key + 102, (B, H, D, D), 0.1) if with_states else None
+    seg = np.arange(B + 1) * N
+    ref = oracle.backward(q, k, v, g, w, dout, cu_seqlens=seg, init_state=init, d_final_state=dfin)
+    return (q, k, v, g, w, dout, init, dfin), ref
+
+
+def run_batch(args, B, N, H, D, dtype, block, chunk):
+    q, k, v, g, w, dout, init, dfin = args
+    x = [dev(a, dtype).view(B, N, H, D) for a in (q, k, v, g)]
+    gd = dev(dout, dtype).view(B, N, H, D)
+    st = lambda a: None if a is None else torch.from_numpy(a).cuda()
+    grads = la.backward(*x, dev(w, dtype), gd, block=block, initial_state=st(init),
+                        d_final_state=st(dfin), return_d_initial_state=True, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    dq, dk, dv, dg, dw, d_init = grads
+    T = B * N
+    return tuple(t.view(T, H, D) for t in (dq, dk, dv, dg)) + (dw, d_init)
+
+
+@pytest.mark.parametrize("D,block", [(16, 16), (32, 32), (64, 64), (128, 32), (128, 64)])
+def test_backward_fp32_shapes(D, block):
+    B, N, H = 2, 301, 3
+    args, ref = batch_case(B, N, H, D, torch.float32, "unit", 21)
+    for chunk in (0, block, 4 * block):
+        say("backward fp32 D", D, "block", block, "chunk", chunk)
+        grads = run_batch(args, B, N, H, D, torch.float32, block, chunk)
+        compare(grads, ref, torch.float32, "fp32 D=%d chunk=%d" % (D, chunk))
+
+
+@pytest.mark.parametrize("D,block,dist", [(128, 64, "minimax"), (128, 64, "unit"), (64, 32, "unit")])
+def test_backward_bf16(D, block, dist):
+    B, N, H = 2, 700, 4
+    args, ref = batch_case(B, N, H, D, torch.bfloat16, dist, 22)
+    for chunk in (0, 2 * block):
+        say("backward bf16 D", D, dist, "chunk", chunk)
+        grads = run_batch(args, B, N, H, D, torch.bfloat16, block, chunk)
+        compare(grads, ref, torch.bfloat16, "bf16 D=%d %s chunk=%d" % (D, dist, chunk))
+
+
+def test_backward_without_states():
+    B, N, H, D = 1, 200, 2, 64
+    args, ref = batch_case(B, N, H, D, torch.float32, "unit", 23, with_states=False)
+    say("backward without initial / final states")
+    q, k, v, g, w, dout, _, _ = args
+    x = [dev(a, torch.float32).view(B, N, H, D) for a in (q, k, v, g, dout)]
+    dq, dk, dv, dg, dw, d_init = la.backward(*x[:4], dev(w, torch.float32), x[4], block=32)
+    torch.cuda.synchronize()
+    assert d_init is None
+    compare((dq.view(N, H, D), dk.view(N, H, D), dv.view(N, H, D), dg.view(N, H, D), dw, None),
+            ref, torch.float32, "no states")
+
+
+@pytest.mark.parametrize("dtype,D,block", [(torch.float32, 64, 32), (torch.bfloat16, 128, 64)])
+def test_backward_varlen(dtype, D, block):
+    lens = [0, 1, 63, 64, 65, 300, 0, 3, 2 * block + 7]
+    seg = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, H, nseq = int(seg[-1]), 3, len(lens)
+    q, k, v, g, w = inputs(T, H, D, "unit", bf16=dtype == torch.bfloat16, key=24)
+    dout = rnd(124, (T, H, D))
+    if dtype == torch.bfloat16:
+        dout = host(dev(dout, torch.bfloat16))
+    init = rnd(125, (nseq, H, D, D), 0.5)
+    dfin = rnd(126, (nseq, H, D, D), 0.1)
+    ref = oracle.backward(q, k, v, g, w, dout, cu_seqlens=seg, init_state=init, d_final_state=dfin)
+    cu = torch.from_numpy(seg.astype(np.int32)).cuda()
+    for chunk in (0, block):
+        say("backward varlen", dtype, "chunk", chunk)
+        grads = la.backward_varlen(*(dev(a, dtype) for a in (q, k, v, g, w, dout)), cu,
+                                   block=block, initial_state=torch.from_numpy(init).cuda(),
+                                   d_final_state=torch.from_numpy(dfin).cuda(),
+                                   return_d_initial_state=True, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        compare(grads, ref, dtype, "varlen chunk=%d" % chunk)
+        # an empty sequence passes the final-state gradient through unchanged
+        d_init = host(grads[5])
+        for s, L in enumerate(lens):
+            if L == 0:
+                assert np.array_equal(d_init[s], dfin[s])
+
+
+def test_backward_empty():
+    H, D = 2, 32
+    x = torch.empty(3, 0, H, D, device="cuda")
+    w = torch.randn(H * D, device="cuda")
+    dfin = torch.randn(3, H, D, D, device="cuda")
+    say("backward with no tokens")
+    dq, dk, dv, dg, dw, d_init = la.backward(x, x, x, x, w, x, block=32, d_final_state=dfin,
+                                             return_d_initial_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw) == 0
+    assert torch.equal(d_init, dfin)
+
+
+@pytest.mark.slow
+def test_backward_8k_workload():
+    """The full 8192-token x 64-head bf16 workload, every gradient against the oracle."""
+    N, H, D = 8192, 64, 128
+    q, k, v, g, w = synth.layer_inputs(synth.PREFILL_8K, N, H, D, "minimax", threads=16)
+    dout = host(dev(rnd(8192, (N, H, D)), torch.bfloat16))
+    say("backward 8K: inputs ready")
+    x = [dev(a, torch.bfloat16).view(1, N, H, D) for a in (q, k, v, g, dout)]
+    grads = la.backward(*x[:4], dev(w, torch.bfloat16), x[4], return_d_initial_state=True)
+    torch.cuda.synchronize()
+    say("backward 8K: GPU done")
+    ref = oracle.backward(q, k, v, g, w, dout)
+    dq, dk, dv, dg, dw, d_init = grads
+    compare(tuple(t.view(N, H, D) for t in (dq, dk, dv, dg)) + (dw, d_init), ref, torch.bfloat16,
+            "backward 8K x 64 heads")
