@@ -173,7 +173,9 @@ LA_API la_status lightning_attn_state_varlen(const void* k, const void* v,
  * the workspace holds fp32 copies of q~, k~, v~, y and dy (20 bytes per
  * element of q) plus two states per chunk.  chunk_tokens: 0 = automatic, or
  * a multiple of `block` (the result does not depend on it beyond rounding).
- * Outputs must not alias inputs.  Errors as for the prefill.
+ * heads * head_dim must be at most 32768 (else the workspace size is 0 and
+ * the call returns LA_ERR_UNSUPPORTED).  Outputs must not alias inputs.
+ * Errors as for the prefill.
  */
 LA_API size_t lightning_attn_backward_workspace_size(int64_t total_tokens, int nseq, int heads,
                                                      int head_dim, int block, int chunk_tokens,

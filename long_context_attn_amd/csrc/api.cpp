@@ -129,23 +129,33 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
 
 // Backward workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks],
 // the forward chunk states and the reverse ones [max_chunks][H][D][D] fp32,
-// q~, k~, v~, y, dy [total][H][D] fp32 and the dw partial sums
-// [ceil(total / norm tokens)][H*D] fp32.  Automatic chunks: the longest
-// power of two (at least the block) that gives about 8 (chunk, head) walks
-// per CU, since each walk is a workgroup of only head_dim threads.
+// y [total][H][D] fp32, dy [total][H][D] (bf16 on the MFMA path, else
+// fp32), on the portable path q~, k~, v~ [total][H][D] fp32, and the dw
+// partial sums [ceil(total / norm tokens) + slices][H*D] fp32.  Automatic chunks: the
+// MFMA walks (a 512-thread workgroup per CU) take the prefill's choice; the
+// portable walks, a workgroup of only head_dim threads each, the longest
+// power of two (at least the block) that gives about 8 walks per CU.
+bool backward_mfma_path(int head_dim, la_dtype dtype) {
+    return dtype == LA_DTYPE_BF16 && head_dim == 128;
+}
+
 struct BwdLayout {
+    bool mfma = false;
     int chunk = 0, max_chunks = 0, n_tb = 0;
     size_t off_segs = 0, off_chunks = 0, off_states = 0, off_gstates = 0, off_qs = 0, off_ks = 0,
            off_vs = 0, off_y = 0, off_dy = 0, off_dw = 0, bytes = 0;
 };
 
 bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
-                     BwdLayout* L) {
+                     la_dtype dtype, BwdLayout* L) {
     if (total < 0 || nseq < 0 || heads < 1 || chunk_tokens < 0 || !supported_dim(head_dim) ||
-        !supported_block(block))
+        !supported_block(block) || (int64_t)heads * head_dim > la::backward_max_hd())
         return false;
+    L->mfma = backward_mfma_path(head_dim, dtype);
     int chunk = chunk_tokens;
-    if (chunk == 0) {
+    if (chunk == 0 && L->mfma) {
+        chunk = auto_chunk(total, nseq, heads, block);
+    } else if (chunk == 0) {
         const int64_t per = total * heads / (8 * (int64_t)la::device_cu_count());
         int64_t c = block;
         while (c * 2 <= per && c < 8192) c *= 2;
@@ -170,13 +180,19 @@ bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block
     off = align_up(off + sizeof(float) * (size_t)maxc * heads * DD);
     L->off_gstates = off;
     off = align_up(off + sizeof(float) * (size_t)maxc * heads * DD);
-    size_t* acts[5] = {&L->off_qs, &L->off_ks, &L->off_vs, &L->off_y, &L->off_dy};
-    for (size_t* o : acts) {
-        *o = off;
-        off = align_up(off + act);
+    L->off_y = off;
+    off = align_up(off + act);
+    L->off_dy = off;
+    off = align_up(off + (L->mfma ? act / 2 : act));
+    if (!L->mfma) {
+        size_t* acts[3] = {&L->off_qs, &L->off_ks, &L->off_vs};
+        for (size_t* o : acts) {
+            *o = off;
+            off = align_up(off + act);
+        }
     }
     L->off_dw = off;
-    off = align_up(off + sizeof(float) * (size_t)ntb * heads * head_dim);
+    off = align_up(off + sizeof(float) * (size_t)(ntb + la::backward_dw_slices()) * heads * head_dim);
     L->bytes = off;
     return true;
 }
@@ -527,7 +543,8 @@ size_t lightning_attn_backward_workspace_size(int64_t total_tokens, int nseq, in
                                               la_dtype dtype) {
     if (check_dtype(dtype) != LA_OK) return 0;
     BwdLayout L;
-    if (!backward_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, &L)) return 0;
+    if (!backward_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, dtype, &L))
+        return 0;
     return L.bytes;
 }
 
@@ -555,7 +572,7 @@ static la_status backward_impl(const void* q, const void* k, const void* v, cons
     if (d_final_state && !aligned16(d_final_state)) return LA_ERR_MISALIGNED;
     if (d_initial_state && !aligned16(d_initial_state)) return LA_ERR_MISALIGNED;
     BwdLayout L;
-    if (!backward_layout(total, nseq, heads, head_dim, block, chunk_tokens, &L))
+    if (!backward_layout(total, nseq, heads, head_dim, block, chunk_tokens, dtype, &L))
         return LA_ERR_UNSUPPORTED;
     if (!workspace) return LA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
@@ -585,12 +602,15 @@ static la_status backward_impl(const void* q, const void* k, const void* v, cons
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dgate;
     a.dw = dweight;
     a.d_init = d_initial_state;
+    a.mfma = L.mfma;
     a.gstates = reinterpret_cast<float*>(ws + L.off_gstates);
-    a.qs = reinterpret_cast<float*>(ws + L.off_qs);
-    a.ks = reinterpret_cast<float*>(ws + L.off_ks);
-    a.vs = reinterpret_cast<float*>(ws + L.off_vs);
+    if (!L.mfma) {
+        a.qs = reinterpret_cast<float*>(ws + L.off_qs);
+        a.ks = reinterpret_cast<float*>(ws + L.off_ks);
+        a.vs = reinterpret_cast<float*>(ws + L.off_vs);
+    }
     a.y = reinterpret_cast<float*>(ws + L.off_y);
-    a.dy = reinterpret_cast<float*>(ws + L.off_dy);
+    a.dy = ws + L.off_dy;
     a.dw_part = reinterpret_cast<float*>(ws + L.off_dw);
     a.n_tb = L.n_tb;
     hipError_t e = la::launch_plan(p, stream);

@@ -1,5 +1,7 @@
-// Backward pass of the Lightning Attention layer: portable fp32 vector-ALU
-// kernels (any supported head_dim / block, fp32 or bf16 storage).
+// Backward pass of the Lightning Attention layer: the portable fp32 vector-ALU
+// kernels (any supported head_dim / block, fp32 or bf16 storage), the norm
+// backward and scans shared with the bf16 MFMA path (backward_mfma.hip), and
+// the launch sequence of both.
 //
 // The forward is Mechanism steps 2-4 of "Diving into MiniMax01 405B MoE"
 // (section "Hybrid Modeling"): q~, k~, v~ = SiLU(q, k, v), S_t = S0 +
@@ -27,7 +29,7 @@ namespace la {
 namespace {
 
 constexpr int EW_THREADS = 256;  // elementwise and norm kernels
-constexpr int NB_TOKENS = 32;    // tokens per workgroup of the norm backward
+constexpr int NB_TOKENS = 8;     // tokens per workgroup of the norm backward
 
 __device__ __forceinline__ float silu_grad_f(float x) {
     const float s = sigmoid_f(x);
@@ -181,27 +183,74 @@ __global__ __launch_bounds__(D) void lin_walk_kernel(
     }
 }
 
-// Norm backward: one workgroup per NB_TOKENS consecutive tokens.  Per token:
-// r and <a, yhat> by block reductions, then dy (fp32) and dgate; dw is
-// accumulated over the workgroup's tokens and written as a partial sum.
-template <class TT>
+// 8 consecutive elements as fp32, and back
+__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[i] = a[i];
+        o[4 + i] = b[i];
+    }
+}
+__device__ __forceinline__ void load8(const __bf16* p, float (&o)[8]) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+__device__ __forceinline__ void store8(__bf16* p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
+    *reinterpret_cast<bf16x8*>(p) = v;
+}
+
+// Norm backward: one workgroup per NB_TOKENS consecutive tokens.  Thread t
+// holds the 8-element pieces t, t + 256, ... (CPT of them) of a token's H*D
+// values in registers: one pass loads y, gate and dout, two block
+// reductions give r and <a, yhat>, and the same registers give dy (DYT:
+// fp32, or bf16 as an MFMA operand) and dgate.  dw is accumulated over the
+// workgroup's tokens and written as one partial sum row.
+template <class TT, class DYT, int CPT>
 __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
     const float* __restrict__ y, const TT* __restrict__ g, const TT* __restrict__ w,
-    const TT* __restrict__ dout, float* __restrict__ dy, TT* __restrict__ dg,
+    const TT* __restrict__ dout, DYT* __restrict__ dy, TT* __restrict__ dg,
     float* __restrict__ dw_part, int64_t T, int HD, float eps) {
     __shared__ float red[2][EW_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nch = HD >> 3;
     const int64_t t_begin = (int64_t)blockIdx.x * NB_TOKENS;
     const int64_t t_end = min(T, t_begin + NB_TOKENS);
-    float* part = dw_part + (int64_t)blockIdx.x * HD;
-    for (int i = tid; i < HD; i += EW_THREADS) part[i] = 0.f;
+    float wt[CPT][8], dwp[CPT][8];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int ch = tid + EW_THREADS * c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dwp[c][i] = 0.f;
+        if (ch < nch) load8(w + 8 * ch, wt[c]);
+    }
     for (int64_t t = t_begin; t < t_end; ++t) {
         const int64_t base = t * HD;
+        float yv[CPT][8], sg[CPT][8], go[CPT][8];
         float ss = 0.f, ay = 0.f;
-        for (int i = tid; i < HD; i += EW_THREADS) {
-            const float yi = y[base + i];
-            ss += yi * yi;
-            ay += to_f32(dout[base + i]) * to_f32(w[i]) * sigmoid_f(to_f32(g[base + i])) * yi;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int ch = tid + EW_THREADS * c;
+            if (ch < nch) {
+                load8(y + base + 8 * ch, yv[c]);
+                load8(g + base + 8 * ch, sg[c]);
+                load8(dout + base + 8 * ch, go[c]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    sg[c][i] = sigmoid_f(sg[c][i]);
+                    ss += yv[c][i] * yv[c][i];
+                    ay += go[c][i] * wt[c][i] * sg[c][i] * yv[c][i];
+                }
+            }
         }
         for (int off = 32; off > 0; off >>= 1) {
             ss += __shfl_xor(ss, off);
@@ -222,26 +271,54 @@ __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
         __syncthreads();
         const float r = __builtin_amdgcn_rsqf(ss / (float)HD + eps);
         const float m = ay * r / (float)HD;  // <a, yhat> / HD
-        for (int i = tid; i < HD; i += EW_THREADS) {
-            const float yh = y[base + i] * r;
-            const float sg = sigmoid_f(to_f32(g[base + i]));
-            const float go = to_f32(dout[base + i]);
-            const float wi = to_f32(w[i]);
-            dy[base + i] = r * (go * wi * sg - yh * m);
-            dg[base + i] = from_f32<TT>(go * yh * wi * sg * (1.0f - sg));
-            part[i] += go * yh * sg;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int ch = tid + EW_THREADS * c;
+            if (ch < nch) {
+                float d1[8], d2[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float yh = yv[c][i] * r;
+                    d1[i] = r * (go[c][i] * wt[c][i] * sg[c][i] - yh * m);
+                    d2[i] = go[c][i] * yh * wt[c][i] * sg[c][i] * (1.0f - sg[c][i]);
+                    dwp[c][i] += go[c][i] * yh * sg[c][i];
+                }
+                store8(dy + base + 8 * ch, d1);
+                store8(dg + base + 8 * ch, d2);
+            }
         }
+    }
+    float* part = dw_part + (int64_t)blockIdx.x * HD;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int ch = tid + EW_THREADS * c;
+        if (ch < nch) store8(part + 8 * ch, dwp[c]);
     }
 }
 
-// dw[i] = sum of the partial sums in workgroup order (deterministic)
-__global__ __launch_bounds__(EW_THREADS) void dw_reduce_kernel(const float* __restrict__ part,
-                                                               float* __restrict__ dw, int nparts,
-                                                               int HD) {
+// dw from the partial sum rows in two fixed-order levels: slice s of
+// DW_SLICES adds rows [s n / S, (s + 1) n / S) into row n + s, then the
+// slices are added in order.
+constexpr int DW_SLICES = 32;
+__global__ __launch_bounds__(EW_THREADS) void dw_slice_kernel(float* __restrict__ part, int nparts,
+                                                              int HD) {
+    const int i = blockIdx.x * EW_THREADS + threadIdx.x;
+    const int s = blockIdx.y;
+    if (i >= HD) return;
+    const int p0 = (int)((int64_t)s * nparts / DW_SLICES);
+    const int p1 = (int)((int64_t)(s + 1) * nparts / DW_SLICES);
+    float acc = 0.f;
+    for (int p = p0; p < p1; ++p) acc += part[(int64_t)p * HD + i];
+    part[(int64_t)(nparts + s) * HD + i] = acc;
+}
+__global__ __launch_bounds__(EW_THREADS) void dw_final_kernel(const float* __restrict__ part,
+                                                              float* __restrict__ dw, int nparts,
+                                                              int HD) {
     const int i = blockIdx.x * EW_THREADS + threadIdx.x;
     if (i >= HD) return;
     float acc = 0.f;
-    for (int p = 0; p < nparts; ++p) acc += part[(int64_t)p * HD + i];
+#pragma unroll
+    for (int s = 0; s < DW_SLICES; ++s) acc += part[(int64_t)(nparts + s) * HD + i];
     dw[i] = acc;
 }
 
@@ -271,10 +348,77 @@ hipError_t walk(const BackwardArgs& a, const float* X, const float* K, const flo
     return hipGetLastError();
 }
 
+hipError_t dw_reduce(const BackwardArgs& a, int HD) {
+    const unsigned cols = (unsigned)((HD + EW_THREADS - 1) / EW_THREADS);
+    hipLaunchKernelGGL(dw_slice_kernel, dim3(cols, DW_SLICES), dim3(EW_THREADS), 0, a.stream,
+                       a.dw_part, a.n_tb, HD);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dw_final_kernel, dim3(cols), dim3(EW_THREADS), 0, a.stream, a.dw_part, a.dw,
+                       a.n_tb, HD);
+    return hipGetLastError();
+}
+
+// norm backward launch: CPT pieces of 8 per thread cover H*D <= 2048 CPT
+template <class TT, class DYT>
+hipError_t norm_backward(const BackwardArgs& a, DYT* dy) {
+    if (a.n_tb == 0) return hipSuccess;
+    const PrefillArgs& p = a.p;
+    const int HD = p.H * p.D;
+    const int per = (HD / 8 + EW_THREADS - 1) / EW_THREADS;
+    const dim3 grid((unsigned)a.n_tb), block(EW_THREADS);
+#define LA_NB(C)                                                                                \
+    hipLaunchKernelGGL((norm_backward_kernel<TT, DYT, C>), grid, block, 0, a.stream, a.y,       \
+                       (const TT*)p.g, (const TT*)p.w, (const TT*)a.dout, dy, (TT*)a.dg,        \
+                       a.dw_part, p.total, HD, p.eps)
+    if (per <= 1) LA_NB(1);
+    else if (per <= 2) LA_NB(2);
+    else if (per <= 4) LA_NB(4);
+    else if (per <= 8) LA_NB(8);
+    else if (per <= 16) LA_NB(16);
+    else return hipErrorInvalidValue;
+#undef LA_NB
+    return hipGetLastError();
+}
+
+hipError_t reverse_scan(const BackwardArgs& a) {
+    const int DD = a.p.D * a.p.D;
+    const int tiles = (DD / 4 + RSCAN_THREADS - 1) / RSCAN_THREADS;
+    const int64_t grid = (int64_t)a.p.nseq * a.p.H * tiles;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(reverse_scan_kernel, dim3((unsigned)grid), dim3(RSCAN_THREADS), 0, a.stream,
+                       a.gstates, a.p.segs, a.d_final, a.d_init, a.p.H, DD, tiles);
+    return hipGetLastError();
+}
+
+// bf16 MFMA path (bf16, head_dim 128): chunk sums and walks on MFMA, the
+// operands read from the activations with SiLU applied on load; dy is bf16.
+hipError_t backward_mfma(const BackwardArgs& a) {
+    const PrefillArgs& p = a.p;
+    hipStream_t st = a.stream;
+    const int HD = p.H * p.D;
+    hipError_t e = launch_chunk_sums_mfma(p, p.k, p.v, true, p.states, true, st);
+    if (e != hipSuccess) return e;
+    {
+        PrefillArgs s = p;
+        s.final_state = nullptr;
+        s.skip_last = true;
+        if ((e = launch_state_scan(s, st)) != hipSuccess) return e;
+    }
+    if ((e = launch_backward_walk_y(a)) != hipSuccess) return e;
+    if ((e = norm_backward<__bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
+    if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
+    if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, false, a.gstates, false, st)) != hipSuccess)
+        return e;
+    if ((e = reverse_scan(a)) != hipSuccess) return e;
+    return launch_backward_walks_grad(a);
+}
+
 template <class TT, int D, int BK>
 hipError_t backward_db(const BackwardArgs& a) {
     const PrefillArgs& p = a.p;
     hipStream_t st = a.stream;
+    float* dy = static_cast<float*>(a.dy);
     const int64_t n = p.total * p.H * D;
     const int HD = p.H * D;
     const dim3 cgrid((unsigned)((int64_t)p.max_chunks * p.H));
@@ -296,37 +440,21 @@ hipError_t backward_db(const BackwardArgs& a) {
     if ((e = walk<TT, D, BK, false, false, 0>(a, a.qs, a.ks, a.vs, p.states, a.y, nullptr,
                                                nullptr)) != hipSuccess)
         return e;
-    if (a.n_tb > 0) {
-        hipLaunchKernelGGL((norm_backward_kernel<TT>), dim3((unsigned)a.n_tb), dim3(EW_THREADS), 0,
-                           st, a.y, (const TT*)p.g, (const TT*)p.w, (const TT*)a.dout, a.dy,
-                           (TT*)a.dg, a.dw_part, p.total, HD, p.eps);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((HD + EW_THREADS - 1) / EW_THREADS)),
-                       dim3(EW_THREADS), 0, st, a.dw_part, a.dw, a.n_tb, HD);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = norm_backward<TT, float>(a, dy)) != hipSuccess) return e;
+    if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
     // reverse chunk sums of q~^T dy, G_exit and dS0
-    hipLaunchKernelGGL((chunk_sum_kernel<D>), cgrid, dim3(D), 0, st, a.qs, a.dy, p.hdr, p.chunks,
+    hipLaunchKernelGGL((chunk_sum_kernel<D>), cgrid, dim3(D), 0, st, a.qs, dy, p.hdr, p.chunks,
                        a.gstates, p.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    {
-        const int DD = D * D;
-        const int tiles = (DD / 4 + RSCAN_THREADS - 1) / RSCAN_THREADS;
-        const int64_t grid = (int64_t)p.nseq * p.H * tiles;
-        if (grid > 0) {
-            hipLaunchKernelGGL(reverse_scan_kernel, dim3((unsigned)grid), dim3(RSCAN_THREADS), 0,
-                               st, a.gstates, p.segs, a.d_final, a.d_init, p.H, DD, tiles);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-    }
+    if ((e = reverse_scan(a)) != hipSuccess) return e;
     // the three input gradients
-    if ((e = walk<TT, D, BK, false, true, 1>(a, a.dy, a.vs, a.ks, p.states, nullptr, p.q, a.dq)) !=
+    if ((e = walk<TT, D, BK, false, true, 1>(a, dy, a.vs, a.ks, p.states, nullptr, p.q, a.dq)) !=
         hipSuccess)
         return e;
-    if ((e = walk<TT, D, BK, true, true, 1>(a, a.vs, a.dy, a.qs, a.gstates, nullptr, p.k, a.dk)) !=
+    if ((e = walk<TT, D, BK, true, true, 1>(a, a.vs, dy, a.qs, a.gstates, nullptr, p.k, a.dk)) !=
         hipSuccess)
         return e;
-    return walk<TT, D, BK, true, false, 1>(a, a.ks, a.qs, a.dy, a.gstates, nullptr, p.v, a.dv);
+    return walk<TT, D, BK, true, false, 1>(a, a.ks, a.qs, dy, a.gstates, nullptr, p.v, a.dv);
 }
 
 template <class TT>
@@ -343,12 +471,15 @@ hipError_t backward_t(const BackwardArgs& a) {
 }  // namespace
 
 int backward_norm_tokens() { return NB_TOKENS; }
+int backward_dw_slices() { return DW_SLICES; }
+int backward_max_hd() { return 16 * 8 * EW_THREADS; }
 
 // After the plan: every kernel of the backward.  With no token at all the
 // token kernels find no chunk (or no token block) and return, dw comes out
 // zero and dS0 = dS_final (or zero).
 hipError_t launch_backward(const BackwardArgs& a) {
     if (a.p.max_chunks == 0) return hipSuccess;
+    if (a.mfma) return backward_mfma(a);
     return a.p.bf16 ? backward_t<__bf16>(a) : backward_t<float>(a);
 }
 

@@ -110,6 +110,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
 // first pass of the two-pass prefill
 bool state_mfma_supported(const PrefillArgs& a);
 hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
+// states[c][h] = sum over chunk c of SiLU(x)^T SiLU(y) (or SiLU(x)^T y)
+hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_y,
+                                  float* states, bool skip_last, hipStream_t st);
 // lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,
 // 32-column state slice) walks every sequence whole; needs heads * 4 <= cus
 // (all lanes resident at once).  The plan runs first with chunk = 64 and no
@@ -130,13 +133,23 @@ struct BackwardArgs {
     void *dq, *dk, *dv, *dg;  // [T][H][D] outputs
     float* dw;                // [H*D] gradient w.r.t. the norm weight
     float* d_init;            // [nseq][H][D][D] gradient w.r.t. the initial states, or null
-    // workspace: q~, k~, v~, y, dy [T][H][D] fp32; reverse chunk sums / G_exit
-    // [max_chunks][H][D][D]; dw partial sums [n_tb][H*D]
-    float *qs, *ks, *vs, *y, *dy, *gstates, *dw_part;
+    // workspace: y [T][H][D] fp32; dy [T][H][D] (fp32, bf16 on the MFMA
+    // path); q~, k~, v~ [T][H][D] fp32 (portable path only); reverse chunk
+    // sums / G_exit [max_chunks][H][D][D]; dw partial sums
+    // [n_tb + backward_dw_slices()][H*D]
+    float *qs, *ks, *vs, *y, *gstates, *dw_part;
+    void* dy;
     int n_tb;
+    bool mfma;
 };
-int backward_norm_tokens();
+int backward_norm_tokens();   // tokens per dw partial sum row
+int backward_dw_slices();     // extra dw rows for the second reduction level
+int backward_max_hd();        // largest heads * head_dim of the norm backward
 hipError_t launch_backward(const BackwardArgs& a);
+// bf16 MFMA walks of the backward (bf16, head_dim 128)
+bool backward_mfma_supported(const PrefillArgs& a);
+hipError_t launch_backward_walk_y(const BackwardArgs& a);
+hipError_t launch_backward_walks_grad(const BackwardArgs& a);
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *w;

@@ -21,6 +21,10 @@ struct StateLds {
     __bf16 v[2][TILE];
 };
 
+// The same kernel gives the backward's chunk sums of q~^T dy: its operands
+// are any two bf16 activations, the first always through SiLU, the second
+// through SiLU when SB (k, v) and as it is otherwise (dy).
+//
 // One workgroup per (chunk, head), state written at states[c][h].  With
 // skip_last, the last chunk of each sequence is left out (the prefill does
 // not need its sum: its walk forms the final state).  Thread t loads rows
@@ -30,6 +34,7 @@ struct StateLds {
 // dv in [32 (w % 4), +32).  Every wave takes part in the SiLU: it is a chain
 // of dependent transcendental operations, and two waves per SIMD hide its
 // latency where one could not.
+template <bool SB>
 __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
@@ -90,7 +95,8 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 *reinterpret_cast<bf16x8*>(sK + swz(rg + 32 * j, 8 * cc)) = silu8(tk[i].r[j]);
-                *reinterpret_cast<bf16x8*>(sV + swz(rg + 32 * j, 8 * cc)) = silu8(tv[i].r[j]);
+                *reinterpret_cast<bf16x8*>(sV + swz(rg + 32 * j, 8 * cc)) =
+                    SB ? silu8(tv[i].r[j]) : tv[i].r[j];
             }
             load_rows(k, b + SPF, tk[i]);
             load_rows(v, b + SPF, tv[i]);
@@ -124,12 +130,23 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
 
 bool state_mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.block == MB; }
 
-hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_y,
+                                  float* states, bool skip_last, hipStream_t st) {
     if (a.max_chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H));
-    hipLaunchKernelGGL(chunk_state_mfma_kernel, grid, dim3(ST_THREADS), 0, st, (const __bf16*)a.k,
-                       (const __bf16*)a.v, a.hdr, a.segs, a.chunks, a.states, a.H, a.skip_last);
+    if (silu_y)
+        hipLaunchKernelGGL(chunk_state_mfma_kernel<true>, grid, dim3(ST_THREADS), 0, st,
+                           (const __bf16*)x, (const __bf16*)y, a.hdr, a.segs, a.chunks, states, a.H,
+                           skip_last);
+    else
+        hipLaunchKernelGGL(chunk_state_mfma_kernel<false>, grid, dim3(ST_THREADS), 0, st,
+                           (const __bf16*)x, (const __bf16*)y, a.hdr, a.segs, a.chunks, states, a.H,
+                           skip_last);
     return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st) {
+    return launch_chunk_sums_mfma(a, a.k, a.v, true, a.states, a.skip_last, st);
 }
 
 }  // namespace la

@@ -4,23 +4,22 @@ Every gradient (dq, dk, dv, dgate, dweight, and the gradient w.r.t. the
 initial states) is compared with oracle.backward on the same seeded inputs,
 with a gradient reaching the final states as well as the output.  Metric:
 the layer's e_max / e_mean, relative to the largest reference magnitude of
-each tensor.  Arithmetic is fp32 on both sizes of the comparison (the oracle
-in fp64), so fp32 outputs meet the fp32 bar; bf16 outputs are rounded once
-to bf16 and meet the bf16 bar.
+each tensor, against the bar of the input dtype.  fp32 inputs take the
+portable fp32 kernels (every tensor within 1e-4).  bf16 inputs at head_dim
+128 take the MFMA walks, whose operands (SiLU outputs, dy, the running
+state) are bf16 as in the forward: every gradient, including the fp32
+dweight and initial-state gradient, is then held to the bf16 bar.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, check, dev, host, inputs, say
+from gpu_util import check, dev, host, inputs, say
 import long_context_attn_amd as la
 from long_context_attn_amd import synth
 
 pytestmark = pytest.mark.gpu
-
-F32_TOL = TOL[torch.float32][0]
-
 
 def rnd(seed, shape, scale=1.0):
     return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
@@ -30,13 +29,9 @@ def compare(grads, ref, dtype, what):
     dq, dk, dv, dg, dw, d_init = grads
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
         check(host(got).reshape(ref[name].shape), ref[name], dtype, "%s %s" % (what, name))
-    # fp32 outputs: the fp32 bar whatever the input dtype
     for name, got in (("dw", dw), ("d_init", d_init)):
-        if got is None:
-            continue
-        emax, _ = oracle.compare(host(got), ref[name])
-        say("%s %s e_max=%.3e" % (what, name, emax))
-        assert emax <= F32_TOL, (what, name, emax)
+        if got is not None:
+            check(host(got), ref[name], dtype, "%s %s" % (what, name))
 
 
 def batch_case(B, N, H, D, dtype, dist, key, with_states=True):
