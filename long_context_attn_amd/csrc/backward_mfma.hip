@@ -53,7 +53,7 @@ __device__ __forceinline__ float silu_grad_f(float x) {
 // Buffer resource over the fp32 rows 0 .. n-1 of one head (rows HD floats
 // apart); stores past the last row are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, int n, int HD) {
-    const int bytes = n > 0 ? ((n - 1) * HD + MD) * 4 : 0;
+    const int bytes = __builtin_amdgcn_readfirstlane(n > 0 ? ((n - 1) * HD + MD) * 4 : 0);
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 

@@ -93,7 +93,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     if (tid == 0) L.item = atomicAdd(&hdr->ticket, 1);
     __syncthreads();
-    const int64_t item = L.item;
+    // uniform across the workgroup: read into a scalar register, so that
+    // everything derived from it (chunk, head, buffer resources) is scalar too
+    // (an LDS value is otherwise taken as divergent, and every buffer access
+    // built from it becomes a loop over lanes)
+    const int64_t item = __builtin_amdgcn_readfirstlane(L.item);
     const int64_t n_items = (int64_t)hdr->n_chunks * H;
     const int64_t DD = (int64_t)MD * MD;
     if (item >= n_items) {

@@ -75,8 +75,11 @@ struct Tile {
 // apart.  The hardware range check makes loads beyond the last row return
 // zeros and drops stores there, which handles a chunk's ragged last block
 // without branches.
+// The byte count is read back into a scalar register: a clamp of a uniform
+// value can be computed in a vector register, and a resource built from one
+// is taken as divergent (every access then loops over the lanes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int n, int HD) {
-    const int bytes = n > 0 ? ((n - 1) * HD + MD) * 2 : 0;
+    const int bytes = __builtin_amdgcn_readfirstlane(n > 0 ? ((n - 1) * HD + MD) * 2 : 0);
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
