@@ -2,6 +2,7 @@
 """Benchmark of the Lightning Attention layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long]
+                    [--no-backward] [--no-layer]
 
 Prints ONE JSON line.  A step is one call of the library's prefill on the
 MiniMax-shaped workload: batch 1, 8192 tokens, 64 heads x head_dim 128
@@ -18,7 +19,8 @@ kernels on the stream they run on: the plan, the chunk sums, the scan of the
 states entering the chunks, and the walk with the RMSNorm fused), the
 roofline of the walk kernel, the state-only pass on the same K and V, the
 backward pass on the same inputs (time per call against its HBM bytes), the
-decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
+layer with its projections (hidden 6144: four input GEMMs with SiLU in the
+epilogue, the attention, the output GEMM) as time per call, the decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
 as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores.
 """
@@ -47,6 +49,8 @@ DECODE_256 = dict(workload="decode_256seq_64h_d128_fp32state", nseq=256, heads=6
 # 1M-token workloads: timed beside the main line, parity in tests/test_gpu_workloads.py
 PREFILL_1M = dict(workload="prefill_1m_64h_d128_bf16", batch=1, seqlen=1 << 20, heads=64,
                   head_dim=128, block=64)
+# the layer with its projections: hidden size of the model
+LAYER_HIDDEN = 6144
 VARLEN_1M = dict(workload="varlen_1m_64h_d128_bf16", total=1 << 20, heads=64, head_dim=128,
                  block=64)
 
@@ -268,6 +272,50 @@ def bench_backward(args, la, torch, inputs):
     return res
 
 
+def bench_layer(args, la, torch):
+    """The layer with its projections on the 8K workload: hidden 6144 (the
+    model's hidden size) projected up to q, k, v and gate (64 heads x 128),
+    SiLU applied in the q/k/v GEMM epilogue, the attention as in the main
+    line, and the 8192 -> 6144 output projection.  Weights are synthetic,
+    N(0, 1/fan_in) in bf16.  The five GEMMs hold 5 x 2 x 8192 x 6144 x 8192
+    FLOPs; the attention's share is the main line's time."""
+    cfg = PREFILL_8K
+    B, N, H, D = cfg["batch"], cfg["seqlen"], cfg["heads"], cfg["head_dim"]
+    hidden, HD = LAYER_HIDDEN, cfg["heads"] * cfg["head_dim"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2025 * 1000 + 61)
+    rn = lambda *shape: torch.randn(*shape, device="cuda", generator=gen)
+    x = rn(B, N, hidden).to(torch.bfloat16)
+    wq = (rn(4, hidden, HD) / math.sqrt(hidden)).to(torch.bfloat16)
+    w = (1 + 0.02 * rn(HD)).to(torch.bfloat16)
+    wo = (rn(HD, hidden) / math.sqrt(HD)).to(torch.bfloat16)
+    out = torch.empty_like(x)
+    ws = torch.empty(la.layer_workspace_size(B * N, B, hidden, H, D), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: la.layer_prefill(x, wq, w, wo, eps=cfg["eps"], out=out, workspace=ws)
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    n = 20
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    gemm_flops = 5 * 2 * B * N * hidden * HD
+    res = dict(workload="layer_8k_hidden6144_64h_d128_bf16", us_per_call=round(us, 1),
+               tokens_per_s=round(B * N / (us * 1e-6), 1), gemm_flops=gemm_flops,
+               gemm_tflops_overall=round(gemm_flops / (us * 1e-6) / 1e12, 1),
+               mfma_frac_overall=round(gemm_flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+    log("layer with projections: %.1f us/call, %.0f TFLOP/s over the whole call"
+        % (us, res["gemm_tflops_overall"]))
+    del x, wq, wo, out, ws
+    return res
+
+
 def bench_decode(args, la, torch, hip):
     from long_context_attn_amd import synth
     cfg = DECODE_256
@@ -457,6 +505,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-long", action="store_true", help="skip the 1M-token workloads")
+    ap.add_argument("--no-layer", action="store_true", help="skip the layer with its projections")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter-collection run: a 1 GiB device copy (calibrates FETCH_SIZE / "
@@ -480,6 +529,7 @@ def main():
     hip = Hip()
     pre = bench_prefill(args, la, torch, hip)
     bwd = None if args.no_backward else bench_backward(args, la, torch, pre["inputs"])
+    layer = None if args.no_layer else bench_layer(args, la, torch)
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)
     long_ctx = None if args.no_long else bench_long(args, la, torch)
     cpu = None
@@ -510,6 +560,7 @@ def main():
         "roofline": pre["roofline"],
         "state_only": pre["state_only"],
         "backward": bwd,
+        "layer_with_projections": layer,
         "decode": dec,
         "long_context": long_ctx,
         "cpu_baseline": cpu,

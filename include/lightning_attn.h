@@ -21,8 +21,9 @@
  *     accumulation for bf16 inputs); out is rounded to the input dtype.
  *   - All pointers are device pointers (hipMalloc'd or from a framework
  *     allocator) and must be 16-byte aligned.  The caller owns all memory;
- *     the library allocates nothing and keeps no global mutable state, so
- *     calls are reentrant and thread-safe.
+ *     the library allocates nothing and keeps no global mutable state (but
+ *     a per-device cache of the CU count and, for the layer call, one
+ *     hipBLASLt handle per device), so calls are reentrant and thread-safe.
  *   - Work is enqueued asynchronously on `stream`; calls do not synchronize.
  *   - Errors: arguments are validated on the host before any HIP call; on a
  *     validation error nothing is enqueued.  A launch failure reported by
@@ -196,6 +197,38 @@ LA_API la_status lightning_attn_backward_varlen(
     void* dgate, float* dweight, float* d_initial_state, int heads, int head_dim, int block,
     int chunk_tokens, float eps, la_dtype dtype, void* workspace, size_t workspace_bytes,
     hipStream_t stream);
+
+/*
+ * The whole layer on a batch of B rows of N tokens, with the projections on
+ * either side of the attention (Mechanism step 1: q, k, v and the gate are
+ * linear maps of the layer input; the output is mapped back to the hidden
+ * size):
+ *     q~, k~, v~ = SiLU(x Wq), SiLU(x Wk), SiLU(x Wv);  g = x Wg
+ *     out        = (RMSNorm(q~ S) * w * sigmoid(g)) Wo  (as lightning_attn_prefill)
+ * The four input projections and the output projection are bf16 GEMMs with
+ * fp32 accumulation on hipBLASLt.  SiLU is applied by the epilogue of the q,
+ * k, v GEMMs to the fp32 accumulators before rounding to bf16, and the
+ * attention kernels then read the activated q, k, v (the gate's sigmoid is
+ * applied by the attention, as in lightning_attn_prefill).
+ *   x:           [batch][seqlen][hidden] bf16
+ *   w_qkvg:      [4][hidden][heads*head_dim] bf16 (Wq, Wk, Wv, Wg; y = x W)
+ *   norm_weight: [heads*head_dim] bf16
+ *   w_out:       [heads*head_dim][hidden] bf16
+ *   out:         [batch][seqlen][hidden] bf16
+ *   initial_state / final_state: as for lightning_attn_prefill
+ * bf16 only, head_dim 128 (LA_ERR_UNSUPPORTED otherwise).  The first call on
+ * a device creates that device's hipBLASLt handle, kept until the process
+ * ends; the GEMMs use a slice of the caller's workspace.
+ */
+LA_API size_t lightning_attn_layer_workspace_size(int64_t total_tokens, int nseq, int hidden,
+                                                  int heads, int head_dim);
+LA_API la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg,
+                                              const void* norm_weight, const void* w_out,
+                                              void* out, const float* initial_state,
+                                              float* final_state, int batch, int64_t seqlen,
+                                              int hidden, int heads, int head_dim, float eps,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
 
 /* Workspace bytes needed by lightning_attn_decode. */
 LA_API size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim);

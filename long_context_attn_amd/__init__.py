@@ -8,10 +8,11 @@ tensors into it.  There is no CPU fallback: if the library is not built the
 calls raise.
 """
 from .ops import (LightningAttnError, backward, backward_varlen,  # noqa: F401
-                  backward_workspace_size, decode, decode_workspace_size, library, prefill,
-                  prefill_varlen, prefill_workspace_size, state, state_varlen,
-                  state_workspace_size, status_string)
+                  backward_workspace_size, decode, decode_workspace_size, layer_prefill,
+                  layer_workspace_size, library, prefill, prefill_varlen, prefill_workspace_size,
+                  state, state_varlen, state_workspace_size, status_string)
 
 __all__ = ["prefill", "prefill_varlen", "state", "state_varlen", "backward", "backward_varlen",
-           "decode", "prefill_workspace_size", "state_workspace_size", "backward_workspace_size",
-           "decode_workspace_size", "library", "status_string", "LightningAttnError"]
+           "layer_prefill", "decode", "prefill_workspace_size", "state_workspace_size",
+           "backward_workspace_size", "layer_workspace_size", "decode_workspace_size", "library",
+           "status_string", "LightningAttnError"]

@@ -20,8 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning_attn.so")
 SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "lane.hip", "state_mfma.hip",
-           "decode.hip", "backward.hip", "backward_mfma.hip"]
+           "decode.hip", "backward.hip", "backward_mfma.hip", "gemm.cpp"]
 ARCH = "gfx950"
+# hipBLASLt: the projection GEMMs of the layer entry point
+LIBS = ["-L" + os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib"), "-lhipblaslt"]
 
 
 def source_sha() -> str:
@@ -66,7 +68,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + LIBS
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))

@@ -651,6 +651,97 @@ la_status lightning_attn_backward_varlen(
                          workspace_bytes, stream);
 }
 
+// Layer workspace: the prefill's (automatic chunks), then SiLU(q), SiLU(k),
+// SiLU(v), the gate projection and the attention output [total][H*D] bf16
+// each, then the GEMM workspace.
+struct LayerLayout {
+    Layout pre;
+    size_t off_act = 0, off_attn = 0, off_gemm = 0, bytes = 0;
+};
+
+static bool layer_layout(int64_t total, int nseq, int hidden, int heads, int head_dim,
+                         LayerLayout* L) {
+    if (hidden < 1 || head_dim != 128) return false;
+    if (!plan_layout(total, nseq, heads, head_dim, 64, 0, true, &L->pre)) return false;
+    const size_t act = sizeof(uint16_t) * (size_t)total * heads * head_dim;
+    size_t off = align_up(L->pre.bytes);
+    L->off_act = off;
+    off = align_up(off + 4 * act);
+    L->off_attn = off;
+    off = align_up(off + act);
+    L->off_gemm = off;
+    off = align_up(off + la::gemm_workspace_bytes());
+    L->bytes = off;
+    return true;
+}
+
+size_t lightning_attn_layer_workspace_size(int64_t total_tokens, int nseq, int hidden, int heads,
+                                           int head_dim) {
+    LayerLayout L;
+    if (total_tokens < 0 || nseq < 0 || heads < 1 ||
+        !layer_layout(total_tokens, nseq, hidden, heads, head_dim, &L))
+        return 0;
+    return L.bytes;
+}
+
+la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg, const void* norm_weight,
+                                       const void* w_out, void* out, const float* initial_state,
+                                       float* final_state, int batch, int64_t seqlen, int hidden,
+                                       int heads, int head_dim, float eps, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    if (batch < 0 || seqlen < 0 || heads < 1 || hidden < 1 || !(eps >= 0.0f))
+        return LA_ERR_BAD_SHAPE;
+    if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
+    if (head_dim != 128) return LA_ERR_UNSUPPORTED;
+    const int64_t total = (int64_t)batch * seqlen;
+    if (total > 0) {
+        la_status s = check_ptrs(x, w_qkvg, w_out, norm_weight, out, out);
+        if (s != LA_OK) return s;
+    }
+    if (initial_state && !aligned16(initial_state)) return LA_ERR_MISALIGNED;
+    if (final_state && !aligned16(final_state)) return LA_ERR_MISALIGNED;
+    LayerLayout L;
+    if (!layer_layout(total, batch, hidden, heads, head_dim, &L)) return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (batch == 0) return LA_OK;
+    char* ws = static_cast<char*>(workspace);
+    const int HD = heads * head_dim;
+    const size_t act = sizeof(uint16_t) * (size_t)total * HD;
+    char* acts = ws + L.off_act;
+    void* attn = ws + L.off_attn;
+    void* gws = ws + L.off_gemm;
+    const size_t gbytes = la::gemm_workspace_bytes();
+    const size_t wmat = sizeof(uint16_t) * (size_t)hidden * HD;
+    // SiLU in the epilogue of the q, k, v projections; the gate stays raw (its
+    // sigmoid is applied by the attention when it finalises the outputs)
+    const la::GemmAct acts_of[4] = {la::GemmAct::silu, la::GemmAct::silu, la::GemmAct::silu,
+                                   la::GemmAct::none};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 4 && e == hipSuccess; ++i)
+        e = la::gemm_bf16(x, static_cast<const char*>(w_qkvg) + i * wmat, acts + i * act, total, HD,
+                          hidden, acts_of[i], gws, gbytes, stream);
+    if (e != hipSuccess) return LA_ERR_HIP;
+    la::PrefillArgs a{};
+    a.q = acts; a.k = acts + act; a.v = acts + 2 * act; a.g = acts + 3 * act;
+    a.w = norm_weight; a.out = attn;
+    a.init_state = initial_state;
+    a.final_state = final_state;
+    a.cu = nullptr;
+    a.nseq = batch;
+    a.seqlen = seqlen;
+    a.total = total;
+    a.H = heads; a.D = head_dim; a.block = 64;
+    a.eps = eps;
+    a.bf16 = true;
+    a.preact = true;
+    la_status s = run_prefill(a, L.pre, workspace, stream);
+    if (s != LA_OK) return s;
+    e = la::gemm_bf16(attn, w_out, out, total, hidden, HD, la::GemmAct::none, gws, gbytes, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {
     if (nseq < 0 || heads < 1 || !supported_dim(head_dim)) return 0;
     return align_up(sizeof(float) * (size_t)nseq * heads * head_dim) +

@@ -397,7 +397,7 @@ hipError_t backward_mfma(const BackwardArgs& a) {
     const PrefillArgs& p = a.p;
     hipStream_t st = a.stream;
     const int HD = p.H * p.D;
-    hipError_t e = launch_chunk_sums_mfma(p, p.k, p.v, true, p.states, true, st);
+    hipError_t e = launch_chunk_sums_mfma(p, p.k, p.v, true, true, p.states, true, st);
     if (e != hipSuccess) return e;
     {
         PrefillArgs s = p;
@@ -408,7 +408,7 @@ hipError_t backward_mfma(const BackwardArgs& a) {
     if ((e = launch_backward_walk_y(a)) != hipSuccess) return e;
     if ((e = norm_backward<__bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
     if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
-    if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, false, a.gstates, false, st)) != hipSuccess)
+    if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, true, false, a.gstates, false, st)) != hipSuccess)
         return e;
     if ((e = reverse_scan(a)) != hipSuccess) return e;
     return launch_backward_walks_grad(a);

@@ -77,6 +77,9 @@ struct PrefillArgs {
     // neither computed nor read by the scan, and the scan writes no final
     // state: the MFMA walk forms it)
     bool skip_last;
+    // MFMA path: q, k, v hold SiLU(q), SiLU(k), SiLU(v) already (applied by
+    // the projection's epilogue); the gate is raw either way
+    bool preact;
     // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
     // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block.
     // Each word holds a float in its low half and 1 in its high half once
@@ -110,9 +113,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
 // first pass of the two-pass prefill
 bool state_mfma_supported(const PrefillArgs& a);
 hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
-// states[c][h] = sum over chunk c of SiLU(x)^T SiLU(y) (or SiLU(x)^T y)
-hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_y,
-                                  float* states, bool skip_last, hipStream_t st);
+// states[c][h] = sum over chunk c of f(x)^T g(y), f and g SiLU or the identity
+hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_x,
+                                  bool silu_y, float* states, bool skip_last, hipStream_t st);
 // lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,
 // 32-column state slice) walks every sequence whole; needs heads * 4 <= cus
 // (all lanes resident at once).  The plan runs first with chunk = 64 and no
@@ -150,6 +153,13 @@ hipError_t launch_backward(const BackwardArgs& a);
 bool backward_mfma_supported(const PrefillArgs& a);
 hipError_t launch_backward_walk_y(const BackwardArgs& a);
 hipError_t launch_backward_walks_grad(const BackwardArgs& a);
+
+// bf16 projection GEMMs on hipBLASLt: row-major y [rows][n] =
+// act(x [rows][k] w [k][n]), the activation applied to the fp32 accumulators
+enum class GemmAct { none, silu };
+size_t gemm_workspace_bytes();
+hipError_t gemm_bf16(const void* x, const void* w, void* y, int64_t rows, int n, int k, GemmAct act,
+                     void* workspace, size_t workspace_bytes, hipStream_t st);
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *w;

@@ -81,6 +81,10 @@ struct WalkLds {
     int item;
 };
 
+// ACT: apply SiLU to q, k, v on load; without it they arrive activated (a
+// projection whose epilogue applied SiLU).  The gate's sigmoid is always
+// applied here, when the outputs are finalised.
+template <bool ACT>
 __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ gate, const __bf16* __restrict__ wgt, __bf16* __restrict__ out,
@@ -182,8 +186,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                 bf16x8 qs[4], ks[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    qs[r] = silu8(tq.r[r]);
-                    ks[r] = silu8(tk.r[r]);
+                    qs[r] = act8<ACT>(tq.r[r]);
+                    ks[r] = act8<ACT>(tk.r[r]);
                 }
                 store_rows(qs, L.q[buf], cc, rg);
                 store_rows(ks, L.k[buf], cc, rg);
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
             if (b < nblk) {
                 bf16x8 vs[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) vs[r] = silu8(tv.r[r]);
+                for (int r = 0; r < 4; ++r) vs[r] = act8<ACT>(tv.r[r]);
                 store_rows(vs, L.v[buf], cc, rg);
             }
             load(v, it + 2, tv);
@@ -435,11 +439,11 @@ bool mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.bloc
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
     if (a.max_chunks == 0 && a.nseq == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H + a.nseq));
-    hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(NTHREADS), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.g,
-                       (const __bf16*)a.w, (__bf16*)a.out, a.hdr, a.segs, a.chunks, a.init_state,
-                       a.final_state, a.states, a.part, a.rsub, a.H, a.nseq, a.chunk / MB,
-                       a.eps);
+    auto* fn = a.preact ? &prefill_mfma_kernel<false> : &prefill_mfma_kernel<true>;
+    hipLaunchKernelGGL(fn, grid, dim3(NTHREADS), 0, st, (const __bf16*)a.q, (const __bf16*)a.k,
+                       (const __bf16*)a.v, (const __bf16*)a.g, (const __bf16*)a.w, (__bf16*)a.out,
+                       a.hdr, a.segs, a.chunks, a.init_state, a.final_state, a.states, a.part,
+                       a.rsub, a.H, a.nseq, a.chunk / MB, a.eps);
     return hipGetLastError();
 }
 

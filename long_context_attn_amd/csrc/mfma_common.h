@@ -58,11 +58,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// SiLU when ACT, else the value as it is (operands already activated)
+template <bool ACT>
+__device__ __forceinline__ bf16x8 act8(bf16x8 x);
 __device__ __forceinline__ bf16x8 silu8(bf16x8 x) {
     bf16x8 o;
 #pragma unroll
     for (int u = 0; u < 8; ++u) o[u] = (__bf16)silu_f((float)x[u]);
     return o;
+}
+template <bool ACT>
+__device__ __forceinline__ bf16x8 act8(bf16x8 x) {
+    if constexpr (ACT) return silu8(x);
+    else return x;
 }
 
 // One 64 x 128 tile as loaded by a producer thread (cc = ptid % 16,

@@ -22,8 +22,9 @@ struct StateLds {
 };
 
 // The same kernel gives the backward's chunk sums of q~^T dy: its operands
-// are any two bf16 activations, the first always through SiLU, the second
-// through SiLU when SB (k, v) and as it is otherwise (dy).
+// are any two bf16 activations, the first through SiLU when SA, the second
+// when SB (k, v: both; q, dy: the first; operands a projection already
+// activated: neither).
 //
 // One workgroup per (chunk, head), state written at states[c][h].  With
 // skip_last, the last chunk of each sequence is left out (the prefill does
@@ -34,7 +35,7 @@ struct StateLds {
 // dv in [32 (w % 4), +32).  Every wave takes part in the SiLU: it is a chain
 // of dependent transcendental operations, and two waves per SIMD hide its
 // latency where one could not.
-template <bool SB>
+template <bool SA, bool SB>
 __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
@@ -94,9 +95,9 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
             __bf16* sV = L.v[b & 1];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                *reinterpret_cast<bf16x8*>(sK + swz(rg + 32 * j, 8 * cc)) = silu8(tk[i].r[j]);
+                *reinterpret_cast<bf16x8*>(sK + swz(rg + 32 * j, 8 * cc)) = act8<SA>(tk[i].r[j]);
                 *reinterpret_cast<bf16x8*>(sV + swz(rg + 32 * j, 8 * cc)) =
-                    SB ? silu8(tv[i].r[j]) : tv[i].r[j];
+                    act8<SB>(tv[i].r[j]);
             }
             load_rows(k, b + SPF, tk[i]);
             load_rows(v, b + SPF, tv[i]);
@@ -130,23 +131,21 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
 
 bool state_mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.block == MB; }
 
-hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_y,
-                                  float* states, bool skip_last, hipStream_t st) {
+hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_x,
+                                  bool silu_y, float* states, bool skip_last, hipStream_t st) {
     if (a.max_chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H));
-    if (silu_y)
-        hipLaunchKernelGGL(chunk_state_mfma_kernel<true>, grid, dim3(ST_THREADS), 0, st,
-                           (const __bf16*)x, (const __bf16*)y, a.hdr, a.segs, a.chunks, states, a.H,
-                           skip_last);
-    else
-        hipLaunchKernelGGL(chunk_state_mfma_kernel<false>, grid, dim3(ST_THREADS), 0, st,
-                           (const __bf16*)x, (const __bf16*)y, a.hdr, a.segs, a.chunks, states, a.H,
-                           skip_last);
+    auto* fn = silu_x ? (silu_y ? &chunk_state_mfma_kernel<true, true>
+                                : &chunk_state_mfma_kernel<true, false>)
+                      : (silu_y ? &chunk_state_mfma_kernel<false, true>
+                                : &chunk_state_mfma_kernel<false, false>);
+    hipLaunchKernelGGL(fn, grid, dim3(ST_THREADS), 0, st, (const __bf16*)x, (const __bf16*)y,
+                       a.hdr, a.segs, a.chunks, states, a.H, skip_last);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st) {
-    return launch_chunk_sums_mfma(a, a.k, a.v, true, a.states, a.skip_last, st);
+    return launch_chunk_sums_mfma(a, a.k, a.v, !a.preact, !a.preact, a.states, a.skip_last, st);
 }
 
 }  // namespace la

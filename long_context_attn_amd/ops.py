@@ -8,6 +8,7 @@ include/lightning_attn.h:
     prefill_varlen(q, k, v, gate, weight, cu, ...) q: [T, H, D], cu: int32 [nseq+1]
     state(k, v, ...) / state_varlen(k, v, cu, ...) final states only, [nseq, H, D, D]
     backward(q, k, v, gate, weight, dout, ...)     gradients of a prefill (and _varlen)
+    layer_prefill(x, w_qkvg, weight, w_out, ...)   projections + attention, x: [B, N, hidden]
     decode(q, k, v, gate, weight, state, ...)      q: [S, H, D], state updated in place
 
 The layer is the Lightning Attention Mechanism of "Diving into MiniMax01 405B
@@ -74,6 +75,11 @@ def library():
         lib.lightning_attn_backward_varlen.argtypes = ([_P] * 7 + [_I, _I64] + [_P] * 8 +
                                                        [_I, _I, _I, _I, _F, _I, _P, _SZ, _P])
         lib.lightning_attn_backward_varlen.restype = _I
+        lib.lightning_attn_layer_workspace_size.argtypes = [_I64, _I, _I, _I, _I]
+        lib.lightning_attn_layer_workspace_size.restype = _SZ
+        lib.lightning_attn_layer_prefill.argtypes = [_P] * 7 + [_I, _I64, _I, _I, _I, _F, _P, _SZ,
+                                                                _P]
+        lib.lightning_attn_layer_prefill.restype = _I
         lib.lightning_attn_decode_workspace_size.argtypes = [_I, _I, _I]
         lib.lightning_attn_decode_workspace_size.restype = _SZ
         lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
@@ -348,6 +354,43 @@ def backward_varlen(q, k, v, gate, weight, dout, cu_seqlens, *, block=64, eps=1e
         _ptr(init), _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), H,
         D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
     return dq, dk, dv, dg, dw, d_init
+
+
+def layer_workspace_size(total_tokens, nseq, hidden, heads, head_dim=128) -> int:
+    return int(library().lightning_attn_layer_workspace_size(
+        int(total_tokens), int(nseq), int(hidden), int(heads), int(head_dim)))
+
+
+def layer_prefill(x, w_qkvg, weight, w_out, *, eps=1e-6, initial_state=None,
+                  return_final_state=False, out=None, final_state=None, workspace=None):
+    """The layer with its projections.  x: [B, N, hidden] bf16; w_qkvg: [4, hidden, H*D]
+    (Wq, Wk, Wv, Wg, y = x W); weight: [H*D]; w_out: [H*D, hidden].  Head dim 128."""
+    _same(x, x, w_qkvg, weight, w_out)
+    if x.dim() != 3 or w_qkvg.dim() != 3 or w_qkvg.shape[0] != 4 or w_qkvg.shape[1] != x.shape[2]:
+        raise ValueError("x must be [B, N, hidden] and w_qkvg [4, hidden, H*D]")
+    B, N, hidden = x.shape
+    HD = w_qkvg.shape[2]
+    D = 128
+    if HD % D != 0 or weight.numel() != HD or tuple(w_out.shape) != (HD, hidden):
+        raise ValueError("weight must be [H*D] and w_out [H*D, hidden], head_dim 128")
+    H = HD // D
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    _same(x, out)
+    init = _state(initial_state, (B, H, D, D), dev, "initial_state")
+    fs = final_state
+    if return_final_state and fs is None:
+        fs = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    _state(fs, (B, H, D, D), dev, "final_state")
+    ws_bytes = layer_workspace_size(B * N, B, hidden, H, D)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, dev, workspace)
+    _check(library().lightning_attn_layer_prefill(
+        _ptr(x), _ptr(w_qkvg), _ptr(weight), _ptr(w_out), _ptr(out), _ptr(init), _ptr(fs), B, N,
+        hidden, H, D, float(eps), _ptr(ws), ws_bytes, _stream(dev)))
+    return (out, fs) if return_final_state else out
 
 
 def decode(q, k, v, gate, weight, state, *, eps=1e-6, out=None, workspace=None):

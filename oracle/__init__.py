@@ -208,6 +208,24 @@ def backward(q, k, v, g, w, dout, cu_seqlens=None, eps=1e-6, init_state=None,
     return res
 
 
+def layer(x, w_qkvg, w, w_out, head_dim=128, cu_seqlens=None, eps=1e-6, init_state=None,
+          return_state=False):
+    """The layer with its projections (Mechanism step 1: q, k, v and the gate are
+    linear maps of the input; the output is mapped back to the hidden size):
+    out = prefill(x Wq, x Wk, x Wv, x Wg) Wo, the matrix products in float64.
+    x: [T, hidden]; w_qkvg: [4, hidden, H*D]; w: [H*D]; w_out: [H*D, hidden]."""
+    x, w_qkvg, w_out = _f64(x), _f64(w_qkvg), _f64(w_out)
+    T = x.shape[0]
+    HD = w_qkvg.shape[2]
+    D = int(head_dim)
+    q, k, v, g = ((x @ w_qkvg[i]).reshape(T, HD // D, D) for i in range(4))
+    res = prefill(q, k, v, g, w, cu_seqlens=cu_seqlens, eps=eps, init_state=init_state,
+                  return_state=return_state)
+    attn, fs = (res if return_state else (res, None))
+    out = attn.reshape(T, HD) @ w_out
+    return (out, fs) if return_state else out
+
+
 def compare(out_dev, out_ref):
     """Error metrics measured after the epilogue, relative to max|out_ref|:
     (e_max, e_mean) = (max|d|, mean|d|) / max|out_ref| over the compared elements."""

@@ -325,6 +325,25 @@ def pin_backward_final_state_only(orc):
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_autograd,
                  pin_backward_final_state_only]
 
+
+def pin_layer_composition(orc):
+    """The layer with distinct scaled-identity projections (Wq = I, Wk = 2 I,
+    Wv = -I, Wg = I / 2) and a permutation for Wo equals the prefill of
+    (x, 2x, -x, x/2) with its outputs permuted: any mix-up of the four
+    projections or of the output map changes the result."""
+    T, H, D, seg = 12, 2, 3, [0, 5, 12]
+    HD = H * D
+    x = rnd(131, (T, HD))
+    w = rnd(132, (HD,), 0.3) + 1.0
+    eye = np.eye(HD)
+    wq = np.stack([eye, 2 * eye, -eye, 0.5 * eye])
+    perm = np.random.default_rng(133).permutation(HD)
+    wo = eye[:, perm]
+    got = orc.layer(x, wq, w, wo, head_dim=D, cu_seqlens=seg)
+    xs = x.reshape(T, H, D)
+    ref = orc.prefill(xs, 2 * xs, -xs, 0.5 * xs, w, cu_seqlens=seg).reshape(T, HD)[:, perm]
+    assert rel(got, ref) < TIGHT
+
 ALL_PINS = [pin_elementwise, pin_brute_force, pin_first_token, pin_constant_closed_form,
             pin_rmsnorm_invariant, pin_causality, pin_head_permutation, pin_blocked,
-            pin_decode_after_prefill, pin_segments_and_resume] + BACKWARD_PINS
+            pin_decode_after_prefill, pin_segments_and_resume] + BACKWARD_PINS + [pin_layer_composition]

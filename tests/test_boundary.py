@@ -39,9 +39,10 @@ def test_header_declares_the_three_calls():
     for n in ("lightning_attn_prefill_profiled", "lightning_attn_decode_profiled",
               "lightning_attn_state", "lightning_attn_state_varlen",
               "lightning_attn_state_workspace_size", "lightning_attn_backward",
-              "lightning_attn_backward_varlen", "lightning_attn_backward_workspace_size"):
+              "lightning_attn_backward_varlen", "lightning_attn_backward_workspace_size",
+              "lightning_attn_layer_prefill", "lightning_attn_layer_workspace_size"):
         assert n in names
-    assert len(names) == 18
+    assert len(names) == 20
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -249,6 +250,32 @@ def test_backward_validation(lib):
     assert vcall(nseq=0, total=5) == SHAPE
     assert vcall(total=1 << 31) == SHAPE
     assert vcall(ws_bytes=8) == WS
+
+
+def test_layer_workspace_and_validation(lib):
+    # the prefill's workspace, 5 bf16 activations of T x H*D, 64 MiB for the GEMMs
+    T, H, D, hidden = 8192, 64, 128, 6144
+    ws = ops.layer_workspace_size(T, 1, hidden, H, D)
+    pre = ops.prefill_workspace_size(T, 1, H, D, 64, 0)
+    need = pre + 5 * T * H * D * 2 + (64 << 20)
+    assert need <= ws < need + 65536
+    assert ops.layer_workspace_size(T, 1, hidden, H, 64) == 0   # head_dim 128 only
+    assert ops.layer_workspace_size(T, 1, 0, H, D) == 0
+
+    def call(x=A, w=A, out=A, batch=2, seqlen=100, hidden=256, heads=2, d=128, eps=1e-6, ws=A,
+             ws_bytes=1 << 40):
+        return lib.lightning_attn_layer_prefill(x, w, A, A, out, None, None, batch, seqlen, hidden,
+                                                heads, d, eps, ws, ws_bytes, None)
+    assert call(x=None) == NULLP
+    assert call(out=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(w=A + 8) == MISAL
+    assert call(d=64) == UNSUP
+    assert call(batch=-1) == SHAPE
+    assert call(hidden=0) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(ws_bytes=1024) == WS
+    assert call(batch=0, x=None, w=None, out=None) == OK
 
 
 def test_decode_validation(lib):
