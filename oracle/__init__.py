@@ -7,6 +7,11 @@ may import this package; the GPU library never does.  It shares no code with
 the HIP path: the arithmetic lives in ``la_oracle.c`` (plain C, built with gcc,
 no fast-math) and this module only marshals numpy arrays.
 
+It also states the hybrid's other attention, the softmax layer (same page,
+"1/8 Softmax Attention"; the model card's Positional Encoding: rotary
+embedding on half of the head dimension, base 10,000,000): ``rope`` and
+``softmax_attention``.
+
 All functions take numpy arrays of any float dtype and compute in float64
 (bf16 and fp32 values convert to float64 exactly).  Layout is token-major:
 activations [T, H, D]; states [nseq, H, D, D] with row = key dimension.
@@ -54,6 +59,11 @@ def _bind(path):
     lib.la_oracle_backward.argtypes = [_D, _D, _D, _D, _D, _D, _I64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _D, _D,
                                        _D, _D, _D, _D, _D, _D]
+    lib.la_oracle_rope.argtypes = [_D, _D, _I64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_double]
+    lib.la_oracle_softmax_attention.argtypes = [_D, _D, _D, _I64, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                                ctypes.c_double, _I64, ctypes.c_int64, _D]
     lib.la_oracle_sigmoid.argtypes = [ctypes.c_double]
     lib.la_oracle_sigmoid.restype = ctypes.c_double
     lib.la_oracle_silu.argtypes = [ctypes.c_double]
@@ -61,7 +71,8 @@ def _bind(path):
     lib.la_oracle_set_threads.argtypes = [ctypes.c_int]
     lib.la_oracle_max_threads.restype = ctypes.c_int
     for f in ("la_oracle_prefill", "la_oracle_prefill_blocked", "la_oracle_decode",
-              "la_oracle_state", "la_oracle_backward"):
+              "la_oracle_state", "la_oracle_backward", "la_oracle_rope",
+              "la_oracle_softmax_attention"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -224,6 +235,50 @@ def layer(x, w_qkvg, w, w_out, head_dim=128, cu_seqlens=None, eps=1e-6, init_sta
     attn, fs = (res if return_state else (res, None))
     out = attn.reshape(T, HD) @ w_out
     return (out, fs) if return_state else out
+
+
+ROPE_BASE = 1e7  # the model card: RoPE base frequency 10,000,000
+
+
+def rope(x, cu_seqlens=None, rope_dim=None, base=ROPE_BASE):
+    """Rotary embedding of x [T, H, D] at each token's position within its
+    sequence, on the first rope_dim features (default D/2, half of the head
+    dimension) in adjacent pairs."""
+    x = _f64(x)
+    T, H, D = x.shape
+    seg = _segments(T, cu_seqlens)
+    rd = D // 2 if rope_dim is None else int(rope_dim)
+    if rd < 0 or rd > D or rd % 2:
+        raise ValueError("rope_dim must be even and at most head_dim")
+    y = np.empty_like(x)
+    _load().la_oracle_rope(_p(x), _p(y), seg.ctypes.data_as(_I64), len(seg) - 1, H, D, rd,
+                           float(base))
+    return y
+
+
+def softmax_attention(q, k, v, cu_seqlens=None, rope_dim=None, base=ROPE_BASE, scale=None,
+                      rows=None):
+    """The hybrid's softmax attention layer: causal softmax attention per
+    sequence, q and k rotated at their positions (rope_dim default D/2, base
+    10M), logits scaled by `scale` (default 1/sqrt(D)).  q, k, v: [T, H, D].
+    rows: optional token indices to compute (the rest of the result is NaN)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, D = q.shape
+    seg = _segments(T, cu_seqlens)
+    rd = D // 2 if rope_dim is None else int(rope_dim)
+    if rd < 0 or rd > D or rd % 2:
+        raise ValueError("rope_dim must be even and at most head_dim")
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.full((T, H, D), np.nan)
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if r is not None and (np.any(r < 0) or np.any(r >= T)):
+        raise ValueError("rows out of range")
+    rc = _load().la_oracle_softmax_attention(
+        _p(q), _p(k), _p(v), seg.ctypes.data_as(_I64), len(seg) - 1, H, D, rd, float(base), sc,
+        None if r is None else r.ctypes.data_as(_I64), 0 if r is None else len(r), _p(out))
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return out
 
 
 def compare(out_dev, out_ref):

@@ -21,6 +21,9 @@
  *    square root, then the weight w[h*D+d], then the elementwise sigmoid gate;
  *  - the state S is D_k x D_v, row = key dimension: S[i][j] += k~_i v~_j.
  *
+ * The file ends with the hybrid's softmax attention layer (rotary embedding
+ * and causal softmax attention), stated the same way.
+ *
  * Layouts: activations token-major [T][H][D]; states [nseq][H][D][D].
  * Segments (batch rows or packed varlen sequences) are given by seg[0..nseq],
  * seg[0] = 0, nondecreasing, seg[nseq] = T; each starts from its own state.
@@ -341,6 +344,101 @@ int la_oracle_backward(const double* q, const double* k, const double* v, const 
 }
 
 /* thread control for the timed baseline (OpenMP over segments x heads) */
+/*
+ * ------------------------------------------------ the softmax attention layer
+ * The hybrid's other attention: one softmax attention layer after every
+ * seven Lightning layers ("Diving into MiniMax01 405B MoE", section "Hybrid
+ * Modeling", 1/8 Softmax Attention: rotary embedding on half of the head
+ * dimension; the model card, "2. Model Architecture": RoPE on half of the
+ * head dimension with base frequency 10,000,000).
+ *
+ * Readings taken where the pages are silent (listed in the design doc):
+ *  - rotary embedding as first defined (RoFormer): features (2i, 2i+1) of the
+ *    first rope_dim ones form a plane rotated by the angle pos * theta_i,
+ *    theta_i = base^(-2i / rope_dim); the other features pass unchanged;
+ *  - pos = the token's index within its own sequence (0 at each start);
+ *  - causal softmax attention, the current token included, logits scaled by
+ *    `scale` (1/sqrt(head_dim) unless the caller says otherwise), as many
+ *    key/value heads as query heads.
+ */
+static void rope_vec(const double* x, double* y, int64_t D, int64_t rope_dim, double base,
+                     double pos) {
+    for (int64_t i = 0; i < rope_dim / 2; ++i) {
+        const double theta = pow(base, -2.0 * (double)i / (double)rope_dim);
+        const double c = cos(pos * theta), s = sin(pos * theta);
+        const double a = x[2 * i], b = x[2 * i + 1];
+        y[2 * i] = a * c - b * s;
+        y[2 * i + 1] = a * s + b * c;
+    }
+    for (int64_t j = rope_dim; j < D; ++j) y[j] = x[j];
+}
+
+/* rotary embedding of every head vector of x [T][H][D] at its position */
+int la_oracle_rope(const double* x, double* y, const int64_t* seg, int64_t nseq, int64_t H,
+                   int64_t D, int64_t rope_dim, double base) {
+    for (int64_t s = 0; s < nseq; ++s)
+        for (int64_t t = seg[s]; t < seg[s + 1]; ++t)
+            for (int64_t h = 0; h < H; ++h) {
+                const int64_t e = (t * H + h) * D;
+                rope_vec(x + e, y + e, D, rope_dim, base, (double)(t - seg[s]));
+            }
+    return 0;
+}
+
+/*
+ * out_t = sum_{u <= t} softmax_u(scale * <q^_t, k^_u>) v_u over the keys u of
+ * t's own sequence, q^ and k^ rotated at their positions.  rows (optional,
+ * nrows entries): compute only these tokens (others are left untouched).
+ */
+int la_oracle_softmax_attention(const double* q, const double* k, const double* v,
+                                const int64_t* seg, int64_t nseq, int64_t H, int64_t D,
+                                int64_t rope_dim, double base, double scale, const int64_t* rows,
+                                int64_t nrows, double* out) {
+    const int64_t T = seg[nseq];
+    const int64_t n = rows ? nrows : T;
+    int bad = 0;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t t = rows ? rows[r] : r;
+            int64_t s = 0;
+            while (s < nseq && seg[s + 1] <= t) ++s;
+            const int64_t s0 = seg[s];
+            double* qh = malloc(sizeof(double) * D);
+            double* kh = malloc(sizeof(double) * D);
+            double* p = malloc(sizeof(double) * (t - s0 + 1));
+            if (!qh || !kh || !p) {
+                bad = 1;
+            } else {
+                rope_vec(q + (t * H + h) * D, qh, D, rope_dim, base, (double)(t - s0));
+                const int64_t last = t; /* causal: the current token is its own last key */
+                double m = -INFINITY;
+                for (int64_t u = s0; u <= last; ++u) {
+                    rope_vec(k + (u * H + h) * D, kh, D, rope_dim, base, (double)(u - s0));
+                    double dot = 0.0;
+                    for (int64_t j = 0; j < D; ++j) dot += qh[j] * kh[j];
+                    p[u - s0] = scale * dot;
+                    if (p[u - s0] > m) m = p[u - s0];
+                }
+                double z = 0.0;
+                for (int64_t u = s0; u <= last; ++u) {
+                    p[u - s0] = exp(p[u - s0] - m);
+                    z += p[u - s0];
+                }
+                double* o = out + (t * H + h) * D;
+                for (int64_t j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int64_t u = s0; u <= last; ++u) acc += p[u - s0] * v[(u * H + h) * D + j];
+                    o[j] = acc / z;
+                }
+            }
+            free(qh);
+            free(kh);
+            free(p);
+        }
+    return bad ? -1 : 0;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 void la_oracle_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }

@@ -347,3 +347,119 @@ def pin_layer_composition(orc):
 ALL_PINS = [pin_elementwise, pin_brute_force, pin_first_token, pin_constant_closed_form,
             pin_rmsnorm_invariant, pin_causality, pin_head_permutation, pin_blocked,
             pin_decode_after_prefill, pin_segments_and_resume] + BACKWARD_PINS + [pin_layer_composition]
+# (the softmax pins are appended below, once defined)
+
+
+# ------------------------------------------------------------ softmax layer
+# The hybrid's softmax attention layer ("Diving into MiniMax01 405B MoE",
+# section "Hybrid Modeling", 1/8 Softmax Attention; model card "2. Model
+# Architecture", Positional Encoding): rotary embedding on half of the head
+# dimension, base 10,000,000, causal softmax attention.
+
+def _rope_complex(x, seg, rope_dim, base):
+    """Rotary embedding written as complex multiplication (its form in the
+    RoFormer paper): feature pairs (2i, 2i+1) read as z = x_2i + j x_2i+1,
+    multiplied by exp(j pos base^(-2i/d)); a different formulation from the
+    oracle's plane rotation."""
+    y = np.array(x, np.float64, copy=True)
+    pos = np.concatenate([np.arange(b - a) for a, b in zip(seg[:-1], seg[1:])]).astype(np.float64)
+    z = y[..., 0:rope_dim:2] + 1j * y[..., 1:rope_dim:2]
+    freq = np.exp(-np.log(base) * np.arange(0, rope_dim, 2) / rope_dim)
+    z = z * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    y[..., 0:rope_dim:2] = z.real
+    y[..., 1:rope_dim:2] = z.imag
+    return y
+
+
+def pin_rope(orc):
+    """Rotary embedding: the page's base and fraction; equal to the complex
+    form; position 0 and the unrotated half pass unchanged; each pair keeps its
+    norm; <rope(q, m), rope(k, n)> depends only on m - n."""
+    import json, os
+    facts = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                        "page_facts.json")))
+    assert orc.ROPE_BASE == facts["rope_base"]
+    T, H, D = 13, 2, 16
+    seg = np.array([0, 5, 5, 13])
+    x = rnd(151, (T, H, D))
+    y = orc.rope(x, cu_seqlens=seg)  # default: half of the head dimension
+    assert rel(y, _rope_complex(x, seg, D // 2, facts["rope_base"])) < TIGHT
+    assert np.array_equal(y[:, :, D // 2:], x[:, :, D // 2:])
+    assert rel(y[[0, 5]], x[[0, 5]]) < TIGHT
+    pn = lambda a: a[..., 0:D // 2:2] ** 2 + a[..., 1:D // 2:2] ** 2
+    assert rel(pn(y), pn(x)) < TIGHT
+    for rd, base in ((D, 10000.0), (4, 500.0)):
+        assert rel(orc.rope(x, cu_seqlens=seg, rope_dim=rd, base=base),
+                   _rope_complex(x, seg, rd, base)) < TIGHT
+    # relative positions: the same q and k vectors at every position of one sequence
+    L = 40
+    qv, kv = rnd(152, (1, 1, D)), rnd(153, (1, 1, D))
+    rq = orc.rope(np.repeat(qv, L, 0), rope_dim=D, base=50.0)[:, 0]
+    rk = orc.rope(np.repeat(kv, L, 0), rope_dim=D, base=50.0)[:, 0]
+    for m, n, c in ((7, 3, 11), (3, 7, 20), (0, 0, 39), (12, 30, 5)):
+        assert abs(rq[m] @ rk[n] - rq[m + c] @ rk[n + c]) < 1e-10
+
+
+def pin_softmax_closed_forms(orc):
+    """The first token of every sequence returns its own value; with q = 0 all
+    logits are equal, so token t returns the mean of v over its sequence's
+    tokens up to and including t."""
+    T, H, D = 17, 3, 8
+    seg = np.array([0, 1, 9, 9, 17])
+    q, k, v = rnd(161, (T, H, D)), rnd(162, (T, H, D)), rnd(163, (T, H, D))
+    out = orc.softmax_attention(q, k, v, cu_seqlens=seg)
+    for a in (0, 1, 9):
+        assert rel(out[a], v[a]) < TIGHT
+    out0 = orc.softmax_attention(np.zeros_like(q), k, v, cu_seqlens=seg)
+    ref = np.empty_like(v)
+    for a, b in zip(seg[:-1], seg[1:]):
+        for t in range(a, b):
+            ref[t] = v[a:t + 1].mean(axis=0)
+    assert rel(out0, ref) < TIGHT
+
+
+def pin_softmax_library(orc):
+    """With the rotation switched off, each sequence equals torch's causal
+    scaled_dot_product_attention in float64 (default scale 1/sqrt(D), and an
+    explicit one)."""
+    import torch
+    T, H, D = 23, 2, 16
+    seg = np.array([0, 10, 23])
+    q, k, v = rnd(171, (T, H, D)), rnd(172, (T, H, D)), rnd(173, (T, H, D))
+    for scale in (None, 0.37):
+        out = orc.softmax_attention(q, k, v, cu_seqlens=seg, rope_dim=0, scale=scale)
+        for a, b in zip(seg[:-1], seg[1:]):
+            tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x[a:b].transpose(1, 0, 2)))
+                          for x in (q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                                   scale=scale)
+            assert rel(out[a:b], ref.numpy().transpose(1, 0, 2)) < 1e-12
+
+
+def pin_softmax_rope_composition(orc):
+    """Attention with the rotation equals attention without it on inputs
+    rotated beforehand (complex form, positions restarting in every sequence);
+    packing sequences together changes nothing; rows computed alone match."""
+    T, H, D = 29, 2, 16
+    seg = np.array([0, 11, 11, 29])
+    q, k, v = rnd(181, (T, H, D), 2.0), rnd(182, (T, H, D), 2.0), rnd(183, (T, H, D))
+    base = 30.0  # a small base, so that every pair turns noticeably over a few tokens
+    out = orc.softmax_attention(q, k, v, cu_seqlens=seg, base=base)
+    ref = orc.softmax_attention(_rope_complex(q, seg, D // 2, base),
+                                _rope_complex(k, seg, D // 2, base), v, cu_seqlens=seg,
+                                rope_dim=0)
+    assert rel(out, ref) < 1e-12
+    for a, b in zip(seg[:-1], seg[1:]):
+        if b > a:
+            alone = orc.softmax_attention(q[a:b], k[a:b], v[a:b], base=base)
+            assert rel(out[a:b], alone) < TIGHT
+    rows = [28, 0, 11, 17]
+    part = orc.softmax_attention(q, k, v, cu_seqlens=seg, base=base, rows=rows)
+    assert rel(part[rows], out[rows]) < TIGHT
+    assert np.isnan(part[1]).all()
+
+
+SOFTMAX_PINS = [pin_rope, pin_softmax_closed_forms, pin_softmax_library,
+                pin_softmax_rope_composition]
+
+ALL_PINS = ALL_PINS + SOFTMAX_PINS

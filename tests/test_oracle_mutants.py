@@ -17,6 +17,20 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "la_oracle.c")
 
 # (name, original text, mutated text): each must occur exactly once
 MUTANTS = [
+    # softmax attention layer
+    ("sm_diagonal_excluded", "const int64_t last = t;", "const int64_t last = t - 1;"),
+    ("sm_rope_direction", "y[2 * i + 1] = a * s + b * c;", "y[2 * i + 1] = -a * s + b * c;"),
+    ("sm_rope_frequency", "pow(base, -2.0 * (double)i / (double)rope_dim)",
+     "pow(base, -(double)i / (double)rope_dim)"),
+    ("sm_rope_query_position_global",
+     "rope_vec(q + (t * H + h) * D, qh, D, rope_dim, base, (double)(t - s0));",
+     "rope_vec(q + (t * H + h) * D, qh, D, rope_dim, base, (double)t);"),
+    ("sm_scale_missing", "p[u - s0] = scale * dot;", "p[u - s0] = dot;"),
+    ("sm_normaliser_missing", "o[j] = acc / z;", "o[j] = acc;"),
+    ("sm_passthrough_dropped", "for (int64_t j = rope_dim; j < D; ++j) y[j] = x[j];",
+     "for (int64_t j = rope_dim; j < D; ++j) y[j] = 0.0;"),
+    ("sm_keys_across_sequences", "const int64_t s0 = seg[s];\n            double* qh",
+     "const int64_t s0 = 0;\n            double* qh"),
     ("diagonal_excluded",
      "                /* state update first: the current token attends to itself */\n"
      "                for (int64_t i = 0; i < D; ++i)\n"
