@@ -230,6 +230,40 @@ LA_API la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg,
                                               void* workspace, size_t workspace_bytes,
                                               hipStream_t stream);
 
+/*
+ * The hybrid's softmax attention layer (one after every seven Lightning
+ * layers: "Diving into MiniMax01 405B MoE", section "Hybrid Modeling", 1/8
+ * Softmax Attention; the model card, "2. Model Architecture", Positional
+ * Encoding: rotary embedding on half of the head dimension, base frequency
+ * 10,000,000).  Per sequence and head, with pos counted from 0 in every
+ * sequence:
+ *     q^_t = rope(q_t, t), k^_u = rope(k_u, u): features (2i, 2i+1), i <
+ *            rope_dim / 2, turned by the angle pos * rope_base^(-2i / rope_dim);
+ *            features >= rope_dim unchanged
+ *     out_t = sum_{u <= t} softmax_u(scale * <q^_t, k^_u>) v_u      (causal)
+ * as many key/value heads as query heads.
+ *   q, k, v, out: [batch][seqlen][heads][head_dim] bf16, or packed
+ *                 [total_tokens][heads][head_dim] with device cu_seqlens int32
+ *                 [nseq+1] (as for lightning_attn_prefill_varlen)
+ *   rope_dim:     rotated features, a multiple of 8 in 0..head_dim (the model:
+ *                 head_dim / 2 = 64); rope_base > 0 (the model: 1e7)
+ *   scale:        logit scale > 0 (usually 1 / sqrt(head_dim))
+ * bf16 and head_dim 128 only (LA_ERR_UNSUPPORTED otherwise).  The workspace
+ * holds the query-tile plan and, when rope_dim > 0, the rotated q and k
+ * (2 x total_tokens x heads x head_dim bf16).
+ */
+LA_API size_t lightning_attn_softmax_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                                    int head_dim, int rope_dim);
+LA_API la_status lightning_attn_softmax_prefill(const void* q, const void* k, const void* v,
+                                                void* out, int batch, int64_t seqlen, int heads,
+                                                int head_dim, int rope_dim, double rope_base,
+                                                float scale, la_dtype dtype, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream);
+LA_API la_status lightning_attn_softmax_prefill_varlen(
+    const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens, int nseq,
+    int64_t total_tokens, int heads, int head_dim, int rope_dim, double rope_base, float scale,
+    la_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by lightning_attn_decode. */
 LA_API size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim);
 

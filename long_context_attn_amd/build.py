@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning_attn.so")
 SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "lane.hip", "state_mfma.hip",
-           "decode.hip", "backward.hip", "backward_mfma.hip", "gemm.cpp"]
+           "decode.hip", "backward.hip", "backward_mfma.hip", "gemm.cpp", "softmax_attn.hip"]
 ARCH = "gfx950"
 # hipBLASLt: the projection GEMMs of the layer entry point
 LIBS = ["-L" + os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib"), "-lhipblaslt"]

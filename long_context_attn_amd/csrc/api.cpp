@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "la_internal.h"
 
 namespace {
@@ -285,6 +287,93 @@ la_status check_ptrs(const void* q, const void* k, const void* v, const void* g,
         !aligned16(out))
         return LA_ERR_MISALIGNED;
     return LA_OK;
+}
+
+// Softmax attention workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x
+// max_tiles] (128-token query tiles), then the rotated q and k (bf16
+// [total][H][D] each) when rope_dim > 0.
+struct SoftmaxLayout {
+    int max_tiles = 0;
+    size_t off_segs = 0, off_tiles = 0, off_qr = 0, off_kr = 0, bytes = 0;
+};
+
+bool softmax_layout(int64_t total, int nseq, int heads, int head_dim, int rope_dim,
+                    SoftmaxLayout* L) {
+    if (total < 0 || nseq < 0 || heads < 1 || head_dim != 128) return false;
+    if (rope_dim < 0 || rope_dim > head_dim || rope_dim % 8 != 0) return false;
+    const int64_t tiles = total / la::SOFTMAX_TILE + nseq;
+    // one workgroup per (tile, head), counted in 32 bits
+    if (tiles * heads > (int64_t)0x7fffffff) return false;
+    L->max_tiles = (int)tiles;
+    size_t off = align_up(sizeof(la::PlanHeader));
+    L->off_segs = off;
+    off = align_up(off + sizeof(la::SegEntry) * (size_t)nseq);
+    L->off_tiles = off;
+    off = align_up(off + sizeof(la::ChunkEntry) * (size_t)tiles);
+    const size_t act = rope_dim > 0 ? sizeof(uint16_t) * (size_t)total * heads * head_dim : 0;
+    L->off_qr = off;
+    off = align_up(off + act);
+    L->off_kr = off;
+    off = align_up(off + act);
+    L->bytes = off;
+    return true;
+}
+
+la_status softmax_checks(const void* q, const void* k, const void* v, const void* out,
+                         int64_t total, int heads, int head_dim, int rope_dim, double rope_base,
+                         float scale, la_dtype dtype) {
+    if (heads < 1 || !(scale > 0.0f) || !std::isfinite(scale)) return LA_ERR_BAD_SHAPE;
+    if (rope_dim > 0 && (!(rope_base > 0.0) || !std::isfinite(rope_base))) return LA_ERR_BAD_SHAPE;
+    if (dtype != LA_DTYPE_BF16 || head_dim != 128 || rope_dim < 0 || rope_dim > head_dim ||
+        rope_dim % 8 != 0)
+        return LA_ERR_UNSUPPORTED;
+    if (total > 0) {
+        if (!q || !k || !v || !out) return LA_ERR_NULL_POINTER;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+            return LA_ERR_MISALIGNED;
+    }
+    return LA_OK;
+}
+
+// plan (query tiles of SOFTMAX_TILE tokens) -> rotate q, k -> attention
+la_status run_softmax(const void* q, const void* k, const void* v, void* out, const int32_t* cu,
+                      int nseq, int64_t seqlen, int64_t total, int heads, int rope_dim,
+                      double rope_base, float scale, const SoftmaxLayout& L, void* workspace,
+                      hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    la::PrefillArgs p{};
+    p.cu = cu;
+    p.nseq = nseq;
+    p.seqlen = seqlen;
+    p.total = total;
+    p.H = heads;
+    p.D = 128;
+    p.chunk = la::SOFTMAX_TILE;
+    p.max_chunks = L.max_tiles;
+    p.hdr = reinterpret_cast<la::PlanHeader*>(ws);
+    p.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
+    p.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_tiles);
+    p.clear = nullptr;
+    p.clear_words = 0;
+    la::SoftmaxArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.H = heads;
+    a.rope_dim = rope_dim;
+    a.rope_base = rope_base;
+    a.scale = scale;
+    a.max_tiles = L.max_tiles;
+    a.hdr = p.hdr;
+    a.segs = p.segs;
+    a.tiles = p.chunks;
+    a.qr = reinterpret_cast<__bf16*>(ws + L.off_qr);
+    a.kr = reinterpret_cast<__bf16*>(ws + L.off_kr);
+    hipError_t e = la::launch_plan(p, stream);
+    if (e == hipSuccess && rope_dim > 0) e = la::launch_softmax_rope(a, stream);
+    if (e == hipSuccess) e = la::launch_softmax_fwd(a, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 }  // namespace
@@ -740,6 +829,57 @@ la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg, const 
     if (s != LA_OK) return s;
     e = la::gemm_bf16(attn, w_out, out, total, hidden, HD, la::GemmAct::none, gws, gbytes, stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+size_t lightning_attn_softmax_workspace_size(int64_t total_tokens, int nseq, int heads,
+                                             int head_dim, int rope_dim) {
+    SoftmaxLayout L;
+    if (!softmax_layout(total_tokens, nseq, heads, head_dim, rope_dim, &L)) return 0;
+    return L.bytes;
+}
+
+la_status lightning_attn_softmax_prefill(const void* q, const void* k, const void* v, void* out,
+                                         int batch, int64_t seqlen, int heads, int head_dim,
+                                         int rope_dim, double rope_base, float scale,
+                                         la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+    if (batch < 0 || seqlen < 0) return LA_ERR_BAD_SHAPE;
+    if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
+    const int64_t total = (int64_t)batch * seqlen;
+    la_status s = softmax_checks(q, k, v, out, total, heads, head_dim, rope_dim, rope_base, scale,
+                                 dtype);
+    if (s != LA_OK) return s;
+    SoftmaxLayout L;
+    if (!softmax_layout(total, batch, heads, head_dim, rope_dim, &L)) return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (total == 0) return LA_OK;
+    return run_softmax(q, k, v, out, nullptr, batch, seqlen, total, heads, rope_dim, rope_base,
+                       scale, L, workspace, stream);
+}
+
+la_status lightning_attn_softmax_prefill_varlen(const void* q, const void* k, const void* v,
+                                                void* out, const int32_t* cu_seqlens, int nseq,
+                                                int64_t total_tokens, int heads, int head_dim,
+                                                int rope_dim, double rope_base, float scale,
+                                                la_dtype dtype, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream) {
+    if (nseq < 0 || total_tokens < 0 || total_tokens > ((int64_t)1 << 40)) return LA_ERR_BAD_SHAPE;
+    if (nseq == 0 && total_tokens != 0) return LA_ERR_BAD_SHAPE;
+    la_status s = softmax_checks(q, k, v, out, total_tokens, heads, head_dim, rope_dim, rope_base,
+                                 scale, dtype);
+    if (s != LA_OK) return s;
+    if (!cu_seqlens) return LA_ERR_NULL_POINTER;
+    SoftmaxLayout L;
+    if (!softmax_layout(total_tokens, nseq, heads, head_dim, rope_dim, &L))
+        return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (total_tokens == 0 || nseq == 0) return LA_OK;
+    return run_softmax(q, k, v, out, cu_seqlens, nseq, 0, total_tokens, heads, rope_dim, rope_base,
+                       scale, L, workspace, stream);
 }
 
 size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {

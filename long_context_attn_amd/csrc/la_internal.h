@@ -174,4 +174,25 @@ struct DecodeArgs {
 hipError_t launch_decode_state(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_norm(const DecodeArgs& a, hipStream_t st);
 
+// --------------------------------------------- softmax attention layer
+// The hybrid's softmax layer: rotary embedding on the first rope_dim features,
+// then causal softmax attention per sequence (bf16, head_dim 128).  The plan
+// cuts the sequences into query tiles of SOFTMAX_TILE tokens.
+constexpr int SOFTMAX_TILE = 128;
+struct SoftmaxArgs {
+    const void *q, *k, *v;
+    void* out;
+    int H, rope_dim;
+    double rope_base;
+    float scale;
+    int max_tiles;
+    PlanHeader* hdr;
+    SegEntry* segs;
+    ChunkEntry* tiles;   // query tiles, from the plan
+    __bf16* qr;          // rotated q and k [total][H][128] (rope_dim > 0)
+    __bf16* kr;
+};
+hipError_t launch_softmax_rope(const SoftmaxArgs& a, hipStream_t st);
+hipError_t launch_softmax_fwd(const SoftmaxArgs& a, hipStream_t st);
+
 }  // namespace la

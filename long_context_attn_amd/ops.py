@@ -18,6 +18,7 @@ a running fp32 state, then RMSNorm(Y) * sigmoid(gate).
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -80,6 +81,15 @@ def library():
         lib.lightning_attn_layer_prefill.argtypes = [_P] * 7 + [_I, _I64, _I, _I, _I, _F, _P, _SZ,
                                                                 _P]
         lib.lightning_attn_layer_prefill.restype = _I
+        lib.lightning_attn_softmax_workspace_size.argtypes = [_I64, _I, _I, _I, _I]
+        lib.lightning_attn_softmax_workspace_size.restype = _SZ
+        _D = ctypes.c_double
+        lib.lightning_attn_softmax_prefill.argtypes = [_P] * 4 + [_I, _I64, _I, _I, _I, _D, _F, _I,
+                                                                 _P, _SZ, _P]
+        lib.lightning_attn_softmax_prefill.restype = _I
+        lib.lightning_attn_softmax_prefill_varlen.argtypes = [_P] * 5 + [_I, _I64, _I, _I, _I, _D,
+                                                                        _F, _I, _P, _SZ, _P]
+        lib.lightning_attn_softmax_prefill_varlen.restype = _I
         lib.lightning_attn_decode_workspace_size.argtypes = [_I, _I, _I]
         lib.lightning_attn_decode_workspace_size.restype = _SZ
         lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
@@ -410,4 +420,73 @@ def decode(q, k, v, gate, weight, state, *, eps=1e-6, out=None, workspace=None):
     _check(library().lightning_attn_decode(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(state), S, H, D,
         float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    return out
+
+
+ROPE_BASE = 1e7  # the model card's rotary base frequency
+
+
+def softmax_workspace_size(total_tokens, nseq, heads, head_dim=128, rope_dim=64) -> int:
+    return int(library().lightning_attn_softmax_workspace_size(
+        int(total_tokens), int(nseq), int(heads), int(head_dim), int(rope_dim)))
+
+
+def _softmax_args(q, k, v, rope_dim, scale):
+    _same(q, k, v)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape")
+    D = q.shape[-1]
+    rd = D // 2 if rope_dim is None else int(rope_dim)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    return rd, sc
+
+
+def softmax_prefill(q, k, v, *, rope_dim=None, rope_base=ROPE_BASE, scale=None, out=None,
+                    workspace=None):
+    """The hybrid's softmax attention layer on B rows of N tokens: q and k
+    rotated on their first rope_dim features (default head_dim / 2, base 1e7),
+    then causal softmax attention with logits scaled by `scale` (default
+    1/sqrt(head_dim)).  q, k, v: [B, N, H, D] bf16, D = 128."""
+    rd, sc = _softmax_args(q, k, v, rope_dim, scale)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, N, H, D]")
+    B, N, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _same(q, out)
+    ws_bytes = softmax_workspace_size(B * N, B, H, D, rd)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, q.device, workspace)
+    _check(library().lightning_attn_softmax_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, rd, float(rope_base), sc, _dtype(q),
+        _ptr(ws), ws_bytes, _stream(q.device)))
+    return out
+
+
+def softmax_prefill_varlen(q, k, v, cu_seqlens, *, rope_dim=None, rope_base=ROPE_BASE, scale=None,
+                           out=None, workspace=None):
+    """softmax_prefill on sequences packed back to back: q, k, v [T, H, D] bf16,
+    cu_seqlens int32 [nseq+1] on the same device; positions restart at 0 in
+    every sequence."""
+    rd, sc = _softmax_args(q, k, v, rope_dim, scale)
+    if q.dim() != 3:
+        raise ValueError("q, k, v must be [T, H, D]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector on the activations' device")
+    T, H, D = q.shape
+    nseq = cu_seqlens.numel() - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if out is None:
+        out = torch.empty_like(q)
+    _same(q, out)
+    ws_bytes = softmax_workspace_size(T, nseq, H, D, rd)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, q.device, workspace)
+    _check(library().lightning_attn_softmax_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), nseq, T, H, D, rd,
+        float(rope_base), sc, _dtype(q), _ptr(ws), ws_bytes, _stream(q.device)))
     return out

@@ -40,9 +40,11 @@ def test_header_declares_the_three_calls():
               "lightning_attn_state", "lightning_attn_state_varlen",
               "lightning_attn_state_workspace_size", "lightning_attn_backward",
               "lightning_attn_backward_varlen", "lightning_attn_backward_workspace_size",
-              "lightning_attn_layer_prefill", "lightning_attn_layer_workspace_size"):
+              "lightning_attn_layer_prefill", "lightning_attn_layer_workspace_size",
+              "lightning_attn_softmax_prefill", "lightning_attn_softmax_prefill_varlen",
+              "lightning_attn_softmax_workspace_size"):
         assert n in names
-    assert len(names) == 20
+    assert len(names) == 23
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -276,6 +278,47 @@ def test_layer_workspace_and_validation(lib):
     assert call(eps=-1.0) == SHAPE
     assert call(ws_bytes=1024) == WS
     assert call(batch=0, x=None, w=None, out=None) == OK
+
+
+def test_softmax_workspace_and_validation(lib):
+    # plan (header, sequences, 128-token query tiles) + rotated q and k
+    T, H, D = 8192, 64, 128
+    ws = ops.softmax_workspace_size(T, 1, H, D, 64)
+    assert 2 * T * H * D * 2 <= ws < 2 * T * H * D * 2 + 65536
+    assert ops.softmax_workspace_size(T, 1, H, D, 0) < 65536   # no rotation: no copies
+    assert ops.softmax_workspace_size(T, 1, H, 64, 32) == 0    # head_dim 128 only
+    assert ops.softmax_workspace_size(T, 1, H, D, 12) == 0     # rope_dim a multiple of 8
+    assert ops.softmax_workspace_size(T, 1, H, D, 136) == 0    # rope_dim <= head_dim
+    D64 = ctypes.c_double
+
+    def call(q=A, out=A, batch=2, seqlen=100, heads=2, d=128, rd=64, base=1e7, scale=0.088,
+             dtype=BF16, ws=A, ws_bytes=1 << 40):
+        return lib.lightning_attn_softmax_prefill(q, A, A, out, batch, seqlen, heads, d, rd,
+                                                  D64(base), scale, dtype, ws, ws_bytes, None)
+    assert call(q=None) == NULLP
+    assert call(out=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(q=A + 8) == MISAL
+    assert call(d=64) == UNSUP
+    assert call(dtype=F32) == UNSUP
+    assert call(rd=12) == UNSUP
+    assert call(batch=-1) == SHAPE
+    assert call(heads=0) == SHAPE
+    assert call(scale=0.0) == SHAPE
+    assert call(scale=float("nan")) == SHAPE
+    assert call(base=0.0) == SHAPE
+    assert call(base=0.0, rd=0, ws_bytes=16) == WS  # the base is unused without rotation
+    assert call(ws_bytes=1024) == WS
+    assert call(batch=0, q=None, out=None) == OK
+
+    def vcall(cu=A, nseq=3, total=100, ws_bytes=1 << 40):
+        return lib.lightning_attn_softmax_prefill_varlen(A, A, A, A, cu, nseq, total, 2, 128, 64,
+                                                         D64(1e7), 0.088, BF16, A, ws_bytes, None)
+    assert vcall(cu=None) == NULLP
+    assert vcall(nseq=-1) == SHAPE
+    assert vcall(nseq=0) == SHAPE
+    assert vcall(ws_bytes=10) == WS
+    assert vcall(nseq=0, total=0) == OK
 
 
 def test_decode_validation(lib):

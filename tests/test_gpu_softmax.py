@@ -1,0 +1,101 @@
+"""The softmax attention layer on the GPU against the oracle (needs an MI355X).
+
+The hybrid's softmax layer: rotary embedding on half of the head dimension
+(base 1e7 by default), causal softmax attention per sequence.  Outputs are
+compared with oracle.softmax_attention on the same bf16 inputs, to the bf16 bar
+(e_max relative to the largest reference magnitude).  Shapes span several
+128-query tiles and 64-key blocks with ragged tails; varlen packs include
+empty and one-token sequences; the full 8192-token x 64-head workload is
+checked on sampled tokens (every head), which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check, dev, host, say
+import long_context_attn_amd as la
+from long_context_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+BF = torch.bfloat16
+
+
+def qkv(T, H, D, key, scale=1.0):
+    """Seeded bf16 q, k, v [T, H, D] (the values the oracle sees are the bf16 ones)."""
+    return [synth.normal((synth.SEED, 95, key, i), (T, H, D), scale=scale, bf16=True)
+            for i in range(3)]
+
+
+@pytest.mark.parametrize("B,N,H,rope_dim,base,scale", [
+    (2, 300, 3, 64, 1e7, 1.0),      # the model's rotation; ragged last tile and block
+    (1, 700, 2, 128, 100.0, 1.0),   # all features turned, a fast-turning base
+    (2, 129, 2, 0, 1e7, 1.0),       # no rotation
+    (1, 1000, 2, 64, 1e4, 3.0),     # peaked logits: the running maximum moves often
+    (3, 1, 1, 64, 1e7, 1.0),        # one token per row
+])
+def test_softmax_batch(B, N, H, rope_dim, base, scale):
+    D = 128
+    T = B * N
+    q, k, v = qkv(T, H, D, key=B * 1000 + N, scale=scale)
+    seg = np.arange(B + 1) * N
+    say("softmax B", B, "N", N, "H", H, "rope_dim", rope_dim, "base", base)
+    ref = oracle.softmax_attention(q, k, v, cu_seqlens=seg, rope_dim=rope_dim, base=base)
+    out = la.softmax_prefill(*(dev(a, BF).view(B, N, H, D) for a in (q, k, v)),
+                             rope_dim=rope_dim, rope_base=base)
+    torch.cuda.synchronize()
+    check(host(out).reshape(T, H, D), ref, BF,
+          "softmax B=%d N=%d H=%d rope_dim=%d base=%g" % (B, N, H, rope_dim, base))
+
+
+def test_softmax_varlen():
+    D, H = 128, 2
+    lens = [0, 1, 127, 128, 129, 300, 0, 5, 700]
+    seg = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(seg[-1])
+    q, k, v = qkv(T, H, D, key=77)
+    ref = oracle.softmax_attention(q, k, v, cu_seqlens=seg)
+    cu = torch.from_numpy(seg.astype(np.int32)).cuda()
+    say("softmax varlen", lens)
+    out = la.softmax_prefill_varlen(*(dev(a, BF) for a in (q, k, v)), cu)
+    torch.cuda.synchronize()
+    check(out, ref, BF, "softmax varlen")
+    # positions restart in every sequence: each equals its own call
+    for a, b in zip(seg[:-1], seg[1:]):
+        if b - a > 0:
+            alone = la.softmax_prefill(*(dev(x[a:b], BF).view(1, b - a, H, D) for x in (q, k, v)))
+            torch.cuda.synchronize()
+            assert torch.equal(alone.view(b - a, H, D), out[a:b])
+
+
+def test_softmax_empty_and_scale():
+    H, D = 2, 128
+    x = torch.empty(2, 0, H, D, device="cuda", dtype=BF)
+    say("softmax with no tokens")
+    assert la.softmax_prefill(x, x, x).numel() == 0
+    T = 200
+    q, k, v = qkv(T, H, D, key=5)
+    say("softmax explicit scale")
+    ref = oracle.softmax_attention(q, k, v, scale=0.02)
+    out = la.softmax_prefill(*(dev(a, BF).view(1, T, H, D) for a in (q, k, v)), scale=0.02)
+    torch.cuda.synchronize()
+    check(host(out).reshape(T, H, D), ref, BF, "softmax scale 0.02")
+
+
+def test_softmax_8k_workload_sampled():
+    """The 8192-token x 64-head workload (bf16, rotation on 64 of 128 features,
+    base 1e7), in the launch configuration the bench times; the oracle computes
+    sampled tokens (all 64 heads each), including the first and last token and
+    both sides of tile and block boundaries."""
+    N, H, D = 8192, 64, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2025 * 1000 + 95)
+    x = [torch.randn(1, N, H, D, device="cuda", generator=gen).to(BF) for _ in range(3)]
+    say("softmax 8K: inputs ready")
+    out = la.softmax_prefill(*x)
+    torch.cuda.synchronize()
+    say("softmax 8K: GPU done")
+    rows = [0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 4095, 5555, 8063, 8064, 8190, 8191]
+    q, k, v = (host(t).reshape(N, H, D) for t in x)
+    ref = oracle.softmax_attention(q, k, v, rows=rows)
+    check(host(out).reshape(N, H, D)[rows], ref[rows], BF, "softmax 8K x 64 heads, sampled")
