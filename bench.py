@@ -2,7 +2,7 @@
 """Benchmark of the Lightning Attention layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long]
-                    [--no-backward] [--no-layer]
+                    [--no-backward] [--no-layer] [--no-softmax]
 
 Prints ONE JSON line.  A step is one call of the library's prefill on the
 MiniMax-shaped workload: batch 1, 8192 tokens, 64 heads x head_dim 128
@@ -20,7 +20,9 @@ states entering the chunks, and the walk with the RMSNorm fused), the
 roofline of the walk kernel, the state-only pass on the same K and V, the
 backward pass on the same inputs (time per call against its HBM bytes), the
 layer with its projections (hidden 6144: four input GEMMs with SiLU in the
-epilogue, the attention, the output GEMM) as time per call, the decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
+epilogue, the attention, the output GEMM) as time per call, the hybrid's
+softmax attention layer on the same shape (rotary embedding on half of the
+head dimension, causal) as TFLOP/s, the decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
 as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores.
 """
@@ -316,6 +318,42 @@ def bench_layer(args, la, torch):
     return res
 
 
+def bench_softmax(args, la, torch):
+    """The hybrid's softmax attention layer on the 8K workload: 8192 tokens x
+    64 heads x 128, bf16, rotary embedding on 64 of the 128 features (base
+    1e7), causal.  FLOPs: the causal half of 4 N^2 D H (QK^T and PV)."""
+    cfg = PREFILL_8K
+    B, N, H, D = cfg["batch"], cfg["seqlen"], cfg["heads"], cfg["head_dim"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2025 * 1000 + 95)
+    x = [torch.randn(B, N, H, D, device="cuda", generator=gen).to(torch.bfloat16)
+         for _ in range(3)]
+    out = torch.empty_like(x[0])
+    ws = torch.empty(la.softmax_workspace_size(B * N, B, H, D, D // 2), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: la.softmax_prefill(*x, out=out, workspace=ws)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    n = 20
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    flops = 4 * B * N * N / 2 * D * H
+    tf = flops / (us * 1e-6) / 1e12
+    res = dict(workload="softmax_8k_64h_d128_bf16_rope64", us_per_call=round(us, 1),
+               tokens_per_s=round(B * N / (us * 1e-6), 1), flops=int(flops),
+               tflops=round(tf, 1), mfma_frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+    log("softmax layer: %.1f us/call, %.0f TFLOP/s" % (us, tf))
+    del x, out, ws
+    return res
+
+
 def bench_decode(args, la, torch, hip):
     from long_context_attn_amd import synth
     cfg = DECODE_256
@@ -506,6 +544,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-long", action="store_true", help="skip the 1M-token workloads")
     ap.add_argument("--no-layer", action="store_true", help="skip the layer with its projections")
+    ap.add_argument("--no-softmax", action="store_true", help="skip the softmax attention layer")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter-collection run: a 1 GiB device copy (calibrates FETCH_SIZE / "
@@ -530,6 +569,7 @@ def main():
     pre = bench_prefill(args, la, torch, hip)
     bwd = None if args.no_backward else bench_backward(args, la, torch, pre["inputs"])
     layer = None if args.no_layer else bench_layer(args, la, torch)
+    smx = None if args.no_softmax else bench_softmax(args, la, torch)
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)
     long_ctx = None if args.no_long else bench_long(args, la, torch)
     cpu = None
@@ -561,6 +601,7 @@ def main():
         "state_only": pre["state_only"],
         "backward": bwd,
         "layer_with_projections": layer,
+        "softmax_layer": smx,
         "decode": dec,
         "long_context": long_ctx,
         "cpu_baseline": cpu,

@@ -249,8 +249,8 @@ LA_API la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg,
  *                 head_dim / 2 = 64); rope_base > 0 (the model: 1e7)
  *   scale:        logit scale > 0 (usually 1 / sqrt(head_dim))
  * bf16 and head_dim 128 only (LA_ERR_UNSUPPORTED otherwise).  The workspace
- * holds the query-tile plan and, when rope_dim > 0, the rotated q and k
- * (2 x total_tokens x heads x head_dim bf16).
+ * holds the query-tile plan and, when rope_dim > 0, the rotated k
+ * (total_tokens x heads x head_dim bf16).
  */
 LA_API size_t lightning_attn_softmax_workspace_size(int64_t total_tokens, int nseq, int heads,
                                                     int head_dim, int rope_dim);

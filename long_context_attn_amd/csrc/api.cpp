@@ -290,11 +290,11 @@ la_status check_ptrs(const void* q, const void* k, const void* v, const void* g,
 }
 
 // Softmax attention workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x
-// max_tiles] (128-token query tiles), then the rotated q and k (bf16
-// [total][H][D] each) when rope_dim > 0.
+// max_tiles] (128-token query tiles), then the rotated k (bf16 [total][H][D])
+// when rope_dim > 0.
 struct SoftmaxLayout {
     int max_tiles = 0;
-    size_t off_segs = 0, off_tiles = 0, off_qr = 0, off_kr = 0, bytes = 0;
+    size_t off_segs = 0, off_tiles = 0, off_kr = 0, bytes = 0;
 };
 
 bool softmax_layout(int64_t total, int nseq, int heads, int head_dim, int rope_dim,
@@ -311,8 +311,6 @@ bool softmax_layout(int64_t total, int nseq, int heads, int head_dim, int rope_d
     L->off_tiles = off;
     off = align_up(off + sizeof(la::ChunkEntry) * (size_t)tiles);
     const size_t act = rope_dim > 0 ? sizeof(uint16_t) * (size_t)total * heads * head_dim : 0;
-    L->off_qr = off;
-    off = align_up(off + act);
     L->off_kr = off;
     off = align_up(off + act);
     L->bytes = off;
@@ -368,7 +366,6 @@ la_status run_softmax(const void* q, const void* k, const void* v, void* out, co
     a.hdr = p.hdr;
     a.segs = p.segs;
     a.tiles = p.chunks;
-    a.qr = reinterpret_cast<__bf16*>(ws + L.off_qr);
     a.kr = reinterpret_cast<__bf16*>(ws + L.off_kr);
     hipError_t e = la::launch_plan(p, stream);
     if (e == hipSuccess && rope_dim > 0) e = la::launch_softmax_rope(a, stream);

@@ -189,8 +189,7 @@ struct SoftmaxArgs {
     PlanHeader* hdr;
     SegEntry* segs;
     ChunkEntry* tiles;   // query tiles, from the plan
-    __bf16* qr;          // rotated q and k [total][H][128] (rope_dim > 0)
-    __bf16* kr;
+    __bf16* kr;          // rotated k [total][H][128] (rope_dim > 0)
 };
 hipError_t launch_softmax_rope(const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_softmax_fwd(const SoftmaxArgs& a, hipStream_t st);

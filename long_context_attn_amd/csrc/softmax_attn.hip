@@ -10,9 +10,10 @@
 //   out_t  = sum_{u <= t} softmax_u(scale <q^_t, k^_u>) v_u   (causal, per sequence)
 //
 // Two kernels:
-//  - rope_kernel: rotates q and k once into bf16 copies in the workspace
+//  - rope_kernel: rotates k once into a bf16 copy in the workspace
 //    (HBM-bound; the angles are reduced in fp64, so positions up to 2^31 keep
-//    full fp32 accuracy);
+//    full fp32 accuracy); q is rotated the same way as the attention kernel
+//    loads it (once per query tile);
 //  - softmax_fwd_kernel: flash-style causal attention on bf16 MFMA.  A
 //    workgroup of four waves takes a 128-query tile of one head (32 queries per
 //    wave) and walks the key blocks from its sequence's start to the tile's
@@ -25,6 +26,9 @@
 //    permlane32 swap; V^T comes from the transposing LDS read.  Softmax runs
 //    in base 2 with scale * log2(e) folded into the logits.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <type_traits>
 
 #include "la_internal.h"
 #include "mfma_common.h"
@@ -40,12 +44,38 @@ constexpr int ROPE_THREADS = 256;
 constexpr int ROPE_TOKENS = 16;  // tokens per workgroup
 constexpr int ROPE_MAX_PAIRS = 64;
 
+// the rotation frequencies theta_p = base^(-2p / rope_dim), passed by value
+struct RopeTheta {
+    double t[ROPE_MAX_PAIRS];
+};
+RopeTheta rope_theta(const SoftmaxArgs& a) {
+    RopeTheta th{};
+    for (int p = 0; p < a.rope_dim / 2 && p < ROPE_MAX_PAIRS; ++p)
+        th.t[p] = std::pow(a.rope_base, -2.0 * p / a.rope_dim);
+    return th;
+}
+
+// Rotation of one feature pair p (< rope_dim / 2) at position pos: the angle
+// pos * theta_p (theta_p = base^(-2p / rope_dim), computed on the host in
+// fp64) is formed and reduced to [-pi, pi] in fp64, then its cosine and sine
+// are taken in fp32.
+__device__ __forceinline__ float2 rope_cs(int64_t pos, double theta) {
+    const double two_pi = 6.283185307179586476925286766559;
+    const double inv_two_pi = 0.15915494309189533576888376337251;
+    double a = (double)pos * theta;
+    a -= two_pi * rint(a * inv_two_pi);
+    float sn, cn;
+    sincosf((float)a, &sn, &cn);
+    return make_float2(cn, sn);
+}
+
+// K's rotation (the attention kernel turns Q itself as it loads it).
 // Workgroup (tile c, group j): tokens 16 j .. 16 j + 15 of tile c.  Each
 // token's cos / sin table is built once in LDS and serves all of its heads.
 __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, __bf16* __restrict__ qr,
-    __bf16* __restrict__ kr, const PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
-    const ChunkEntry* __restrict__ tiles, int H, int rope_dim, double log2_base) {
+    const __bf16* __restrict__ k, __bf16* __restrict__ kr, const PlanHeader* __restrict__ hdr,
+    const SegEntry* __restrict__ segs, const ChunkEntry* __restrict__ tiles, int H, int rope_dim,
+    const RopeTheta th) {
     __shared__ float2 cs[ROPE_TOKENS][ROPE_MAX_PAIRS];
     constexpr int GROUPS = SOFTMAX_TILE / ROPE_TOKENS;
     const int c = blockIdx.x / GROUPS, grp = blockIdx.x - c * GROUPS;
@@ -57,29 +87,20 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(
     const int64_t first = ce.start + t0;                      // packed index of the first token
     const int64_t pos0 = first - tiles[segs[ce.seg].first].start;  // its position in the sequence
     const int npairs = rope_dim / 2;
-    const double two_pi = 6.283185307179586476925286766559;
     for (int i = threadIdx.x; i < ROPE_TOKENS * npairs; i += ROPE_THREADS) {
         const int t = i / npairs, p = i - t * npairs;
-        // theta_p = base^(-2p / rope_dim); angle reduced to [-pi, pi] in fp64
-        const double theta = exp2(-(2.0 * p / rope_dim) * log2_base);
-        double a = (double)(pos0 + t) * theta;
-        a -= two_pi * rint(a / two_pi);
-        float sn, cn;
-        sincosf((float)a, &sn, &cn);
-        cs[t][p] = make_float2(cn, sn);
+        cs[t][p] = rope_cs(pos0 + t, th.t[p]);
     }
     __syncthreads();
     const int HD = H * MD;
     const int per_token = HD / 8;  // 16-byte pieces of one token
     const int64_t n = (int64_t)nt * per_token;
-    for (int64_t i = threadIdx.x; i < 2 * n; i += ROPE_THREADS) {
-        const bool isk = i >= n;
-        const int64_t e = isk ? i - n : i;
+    for (int64_t e = threadIdx.x; e < n; e += ROPE_THREADS) {
         const int t = (int)(e / per_token);
         const int piece = (int)(e - (int64_t)t * per_token);
         const int f = (piece % (MD / 8)) * 8;  // first feature of the piece within its head
         const int64_t off = (first + t) * HD + (int64_t)piece * 8;
-        bf16x8 x = *reinterpret_cast<const bf16x8*>((isk ? k : q) + off);
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(k + off);
         if (f < rope_dim) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -89,7 +110,7 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(
                 x[2 * u + 1] = (__bf16)(a * r.y + b * r.x);
             }
         }
-        *reinterpret_cast<bf16x8*>((isk ? kr : qr) + off) = x;
+        *reinterpret_cast<bf16x8*>(kr + off) = x;
     }
 }
 
@@ -117,7 +138,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ out, const PlanHeader* __restrict__ hdr,
-    const SegEntry* __restrict__ segs, const ChunkEntry* __restrict__ tiles, int H, float sl2) {
+    const SegEntry* __restrict__ segs, const ChunkEntry* __restrict__ tiles, int H, float sl2,
+    int rope_dim, const RopeTheta th) {
     __shared__ __attribute__((aligned(16))) FaLds L;
     const int ntile = hdr->n_chunks;
     // Workgroups are dealt to the eight XCDs in turn; when the heads divide
@@ -139,7 +161,8 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
     const int64_t qstart = ce.start;
     const int qlen = ce.len;
     const int HD = H * MD;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
     const int64_t qend = qstart + qlen;
     const int nkb = (int)((qend - s0 + MB - 1) / MB);
 
@@ -154,96 +177,173 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
         for (int s = 0; s < MD / 16; ++s)
             qb[s] = __builtin_bit_cast(bf16x8,
                                        __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * s, 0));
+        // rotate the first rope_dim features at the query's position (as
+        // rope_kernel does for K)
+        const int64_t pos = q0w + l32 - s0;
+#pragma unroll
+        for (int s = 0; s < MD / 16; ++s) {
+            const int f0 = 16 * s + 8 * g;
+            if (f0 < rope_dim) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float2 r = rope_cs(pos, th.t[f0 / 2 + u]);
+                    const float a = (float)qb[s][2 * u], b = (float)qb[s][2 * u + 1];
+                    qb[s][2 * u] = (__bf16)(a * r.x - b * r.y);
+                    qb[s][2 * u + 1] = (__bf16)(a * r.y + b * r.x);
+                }
+            }
+        }
     }
 
-    // K / V tiles: thread loads rows 4 rg .. 4 rg + 3, features 8 cc .. + 7
-    const int cc = tid & 15, rg = tid >> 4;
-    const int voff = (4 * rg * HD + 8 * cc) * 2, rstride = HD * 2;
-    auto load_kv = [&](int b, Tile& tk, Tile& tv) {
-        const int64_t kb0 = s0 + (int64_t)min(b, nkb - 1) * MB;
-        const int n = b < nkb ? (int)min((int64_t)MB, qend - kb0) : 0;
-        const int64_t off = kb0 * HD + (int64_t)h * MD;
-        load_tile(tk, tile_rsrc(k + off, n, HD), voff, rstride);
-        load_tile(tv, tile_rsrc(v + off, n, HD), voff, rstride);
+    // K / V tiles go from HBM straight into LDS (buffer loads with the LDS
+    // as destination, no registers): wave w stages rows 16 w .. 16 w + 15 of
+    // a 64-key tile with four 1 KiB loads, lane l of each filling physical
+    // 16-byte chunk l % 16 of row 4 i + l / 16 with the logical chunk that the
+    // swizzle puts there.  Rows past a ragged end repeat the last key: their
+    // scores are always masked, so they only need to be finite.
+    // K runs one block ahead of V: while the exponentials of block b run on
+    // the VALU, the scores of block b + 1 run on the matrix cores.  In
+    // iteration b the LDS holds K(b + 1) and V(b), and the loads of K(b + 2)
+    // and V(b + 1) fill the buffers that K(b) and V(b - 1) left before the
+    // last barrier; each wave waits for its own loads before the next barrier.
+    auto stage = [&](const __bf16* base, int b, __bf16* dst) {
+        const int64_t kb0 = s0 + (int64_t)b * MB;
+        const int n = (int)min((int64_t)MB, qend - kb0);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base + kb0 * HD + (int64_t)h * MD, n, HD);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row0 = 16 * w + 4 * i;
+            const int row = row0 + (lane >> 4);
+            const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+            const int vo = (min(row, n - 1) * HD + 8 * ((lane & 15) ^ f)) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(dst + row0 * MD), 16, vo, 0, 0, 0);
+        }
     };
-    Tile tk, tv;
-    load_kv(0, tk, tv);
-    store_rows(tk.r, L.k[0], cc, rg);
-    store_rows(tv.r, L.v[0], cc, rg);
-    load_kv(1, tk, tv);
+    // vmcnt(0) with the other counters left alone: this wave's tile loads done
+    auto loads_done = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
+    // the last key block this wave's queries reach (-1: no queries)
+    const int last_w = qrows > 0 ? (int)((q0w + qrows - 1 - s0) / MB) : -1;
+    stage(k, 0, L.k[0]);
+    stage(v, 0, L.v[0]);
+    if (nkb > 1) stage(k, 1, L.k[1]);
+    loads_done();
     __syncthreads();
 
     f32x16 O[MD / 32] = {};
-    float mrun = -INFINITY, lsum = 0.f;
+    float mrun = -INFINITY, lsum = 0.f;  // running maximum (raw score units) and sum
+    // The running maximum only moves when a score exceeds it by more than
+    // 8 / sl2, so that probabilities stay below 2^8 and the rescale of the
+    // output is rare.
+    const float tau = 8.f / sl2;
     const int64_t qabs = q0w + l32;  // this lane's query
-    for (int b = 0; b < nkb; ++b) {
-        const __bf16* sK = L.k[b & 1];
-        const __bf16* sV = L.v[b & 1];
-        const int64_t kb0 = s0 + (int64_t)b * MB;
-        // a wave whose queries all precede the block has nothing to add
-        if (qrows > 0 && q0w + qrows - 1 >= kb0) {
-            f32x16 S[2] = {};
+    auto scores = [&](const __bf16* sK, f32x16 (&S)[2]) {
+        S[0] = f32x16{};
+        S[1] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < MD / 16; ++s)
+        for (int s = 0; s < MD / 16; ++s)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                S[m] = mfma32(ld_row_operand(sK, 32 * m + l32, 16 * s + 8 * g), qb[s], S[m]);
+    };
+    f32x16 Sa[2], Sb[2];
+    if (last_w >= 0) scores(L.k[0], Sa);
+    // iteration b (P = b % 2): softmax and O += P V for block b (scores in
+    // Sc), scores of block b + 1 into Sn
+    auto step = [&](auto par, int b, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+        constexpr int P = decltype(par)::value;
+        if (b + 2 < nkb) stage(k, b + 2, L.k[P]);
+        if (b + 1 < nkb) stage(v, b + 1, L.v[1 - P]);
+        if (b <= last_w) {
+            const int64_t kb0 = s0 + (int64_t)b * MB;
+            if (kb0 + MB - 1 > q0w) {  // the block reaches the diagonal: mask keys after the query
+                const int qrel = (int)min((int64_t)MB, qabs - kb0);
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    S[m] = mfma32(ld_row_operand(sK, 32 * m + l32, 16 * s + 8 * g), qb[s], S[m]);
-            // logits in base 2; keys after the query masked out
-            const bool diag = kb0 + MB - 1 > q0w;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * m + 8 * (r >> 2) + 4 * g + (r & 3) > qrel) Sc[m][r] = -INFINITY;
+            }
             float bm = -INFINITY;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = S[m][r] * sl2;
-                    if (diag && kb0 + 32 * m + 8 * (r >> 2) + 4 * g + (r & 3) > qabs) x = -INFINITY;
-                    S[m][r] = x;
-                    bm = fmaxf(bm, x);
-                }
-            const float mnew = fmaxf(mrun, pair_max(bm));
-            const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-            mrun = mnew;
-            float ps = 0.f;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(S[m][r] - mnew);
-                    S[m][r] = p;
-                    ps += p;
-                }
-            lsum = lsum * alpha + ps;
-#pragma unroll
-            for (int n = 0; n < MD / 32; ++n)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) O[n][r] *= alpha;
-            // O^T += V^T P^T, 16 keys at a time: accumulator registers
-            // r0 .. r0 + 7 of tile m hold keys 16 s + 8 (j / 4) + 4 g + j % 4;
-            // one swap between the lane halves makes them keys 16 s + 8 g + j
-#pragma unroll
-            for (int s = 0; s < MB / 16; ++s) {
-                const int m = s >> 1, r0 = 8 * (s & 1);
-                const unsigned p0 = pack_bf16(S[m][r0 + 0], S[m][r0 + 1]);
-                const unsigned p1 = pack_bf16(S[m][r0 + 2], S[m][r0 + 3]);
-                const unsigned p2 = pack_bf16(S[m][r0 + 4], S[m][r0 + 5]);
-                const unsigned p3 = pack_bf16(S[m][r0 + 6], S[m][r0 + 7]);
-                const auto x02 = __builtin_amdgcn_permlane32_swap(p0, p2, false, false);
-                const auto x13 = __builtin_amdgcn_permlane32_swap(p1, p3, false, false);
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{x02[0], x13[0], x02[1], x13[1]});
+                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, Sc[m][r]);
+            bm = pair_max(bm);
+            const bool up = bm > mrun + tau;
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
+                const float mnew = up ? bm : mrun;
+                const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);
+                mrun = mnew;
+                lsum *= alpha;
 #pragma unroll
                 for (int n = 0; n < MD / 32; ++n)
-                    O[n] = mfma32(ld_tr_operand(sV, 16 * s, 32 * n, lane), pb, O[n]);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) O[n][r] *= alpha;
+            }
+            const float msc = mrun * sl2;
+            // Block b + 1's scores on the matrix cores with block b's
+            // exponentials in between: step s issues the two products of
+            // features 16 s .. 16 s + 15 (K operands read one step ahead) and
+            // four of the 32 exponentials; every two steps complete eight, and
+            // they become one P^T operand (accumulator registers r0 .. r0 + 7
+            // of tile m hold keys 16 t + 8 (j / 4) + 4 g + j % 4; one swap
+            // between the lane halves makes them keys 16 t + 8 g + j).  The
+            // fences keep this order.  A wave past its last block computes
+            // scores from whatever the buffer holds and never uses them.
+            const __bf16* sK = L.k[1 - P];
+            Sn[0] = f32x16{};
+            Sn[1] = f32x16{};
+            bf16x8 ka[2][2];
+            ka[0][0] = ld_row_operand(sK, l32, 8 * g);
+            ka[0][1] = ld_row_operand(sK, 32 + l32, 8 * g);
+            float ps = 0.f;
+            float pv[8];
+            bf16x8 pb[MB / 16];
+#pragma unroll
+            for (int st = 0; st < MD / 16; ++st) {
+                if (st + 1 < MD / 16) {
+                    ka[(st + 1) & 1][0] = ld_row_operand(sK, l32, 16 * (st + 1) + 8 * g);
+                    ka[(st + 1) & 1][1] = ld_row_operand(sK, 32 + l32, 16 * (st + 1) + 8 * g);
+                }
+                Sn[0] = mfma32(ka[st & 1][0], qb[st], Sn[0]);
+                Sn[1] = mfma32(ka[st & 1][1], qb[st], Sn[1]);
+                const int t = st >> 1, m = t >> 1, r0 = 8 * (t & 1) + 4 * (st & 1);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[m][r0 + u], sl2, -msc));
+                    pv[4 * (st & 1) + u] = e;
+                    ps += e;
+                }
+                if (st & 1) {
+                    const unsigned p0 = pack_bf16(pv[0], pv[1]), p1 = pack_bf16(pv[2], pv[3]);
+                    const unsigned p2 = pack_bf16(pv[4], pv[5]), p3 = pack_bf16(pv[6], pv[7]);
+                    const auto x02 = __builtin_amdgcn_permlane32_swap(p0, p2, false, false);
+                    const auto x13 = __builtin_amdgcn_permlane32_swap(p1, p3, false, false);
+                    pb[t] = __builtin_bit_cast(bf16x8, u32x4{x02[0], x13[0], x02[1], x13[1]});
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            lsum += ps;
+            // O^T += V^T P^T, V operands read one product ahead
+            const __bf16* sV = L.v[P];
+            bf16x8 va[2];
+            va[0] = ld_tr_operand(sV, 0, 0, lane);
+#pragma unroll
+            for (int i = 0; i < (MB / 16) * (MD / 32); ++i) {
+                const int t = i >> 2, n = i & 3;
+                if (i + 1 < (MB / 16) * (MD / 32))
+                    va[(i + 1) & 1] = ld_tr_operand(sV, 16 * ((i + 1) >> 2), 32 * ((i + 1) & 3), lane);
+                O[n] = mfma32(va[i & 1], pb[t], O[n]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // stage block b + 1 (loaded during block b - 1) and fetch block b + 2;
-        // every wave finished block b - 1, which used the same buffers, before
-        // the last barrier
-        if (b + 1 < nkb) {
-            store_rows(tk.r, L.k[(b + 1) & 1], cc, rg);
-            store_rows(tv.r, L.v[(b + 1) & 1], cc, rg);
-        }
-        load_kv(b + 2, tk, tv);
+        loads_done();
         __syncthreads();
+    };
+    for (int b = 0; b < nkb; b += 2) {
+        step(std::integral_constant<int, 0>{}, b, Sa, Sb);
+        if (b + 1 < nkb) step(std::integral_constant<int, 1>{}, b + 1, Sb, Sa);
     }
 
     // out = O / sum, lane = query l32, features 32 n + 8 jj + 4 g .. + 3
@@ -268,20 +368,18 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
 hipError_t launch_softmax_rope(const SoftmaxArgs& a, hipStream_t st) {
     if (a.max_tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_tiles * (SOFTMAX_TILE / ROPE_TOKENS)));
-    hipLaunchKernelGGL(rope_kernel, grid, dim3(ROPE_THREADS), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, a.qr, a.kr, a.hdr, a.segs, a.tiles, a.H, a.rope_dim,
-                       log2(a.rope_base));
+    hipLaunchKernelGGL(rope_kernel, grid, dim3(ROPE_THREADS), 0, st, (const __bf16*)a.k, a.kr,
+                       a.hdr, a.segs, a.tiles, a.H, a.rope_dim, rope_theta(a));
     return hipGetLastError();
 }
 
 hipError_t launch_softmax_fwd(const SoftmaxArgs& a, hipStream_t st) {
     if (a.max_tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_tiles * a.H));
-    const __bf16* qq = a.rope_dim > 0 ? a.qr : (const __bf16*)a.q;
     const __bf16* kk = a.rope_dim > 0 ? a.kr : (const __bf16*)a.k;
-    hipLaunchKernelGGL(softmax_fwd_kernel, grid, dim3(FA_THREADS), 0, st, qq, kk,
+    hipLaunchKernelGGL(softmax_fwd_kernel, grid, dim3(FA_THREADS), 0, st, (const __bf16*)a.q, kk,
                        (const __bf16*)a.v, (__bf16*)a.out, a.hdr, a.segs, a.tiles, a.H,
-                       a.scale * 1.4426950408889634f);
+                       a.scale * 1.4426950408889634f, a.rope_dim, rope_theta(a));
     return hipGetLastError();
 }
 
