@@ -22,7 +22,8 @@ backward pass on the same inputs (time per call against its HBM bytes), the
 layer with its projections (hidden 6144: four input GEMMs with SiLU in the
 epilogue, the attention, the output GEMM) as time per call, the hybrid's
 softmax attention layer on the same shape (rotary embedding on half of the
-head dimension, causal) as TFLOP/s, the decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
+head dimension, causal) as TFLOP/s and its decode step against a KV cache
+(32 sequences, cache lengths 1K..16K) as KV GB/s, the decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
 as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores.
 """
@@ -354,6 +355,49 @@ def bench_softmax(args, la, torch):
     return res
 
 
+def bench_softmax_decode(args, la, torch):
+    """One decode step of the softmax layer against a KV cache: 32 sequences x
+    64 heads x 128 (bf16), cache lengths drawn uniformly from 1024..16383
+    (seeded), the new token's key rotated at its position.  Algorithmic HBM
+    bytes: the cached keys and values read once, (L + 1) x H x D x 2 x 2 per
+    sequence.  The lengths are not advanced between the timed steps, so every
+    step does the same work."""
+    S, H, D, max_len = 32, 64, 128, 16384
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2025 * 1000 + 96)
+    lens = torch.randint(1024, max_len, (S,), generator=gen, device="cuda", dtype=torch.int32)
+    kc = torch.empty(S, H, max_len, D, device="cuda", dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    for t in (kc, vc):
+        for i in range(S):
+            t[i].normal_(generator=gen)
+    q, k, v = (torch.randn(S, H, D, device="cuda", generator=gen).to(torch.bfloat16)
+               for _ in range(3))
+    out = torch.empty_like(q)
+    ws = torch.empty(la.softmax_decode_workspace_size(S, max_len, H, D), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: la.softmax_decode(q, k, v, kc, vc, lens, out=out, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    n = 10
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    nbytes = int((lens.long() + 1).sum().item()) * H * D * 2 * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = dict(workload="softmax_decode_32seq_64h_d128_bf16_cache1k_16k", us_per_step=round(us, 1),
+               kv_bytes=nbytes, kv_GBps=round(gbs, 1), kv_hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    log("softmax decode: %.1f us/step, KV cache %.0f GB/s" % (us, gbs))
+    del kc, vc, ws
+    return res
+
+
 def bench_decode(args, la, torch, hip):
     from long_context_attn_amd import synth
     cfg = DECODE_256
@@ -570,6 +614,7 @@ def main():
     bwd = None if args.no_backward else bench_backward(args, la, torch, pre["inputs"])
     layer = None if args.no_layer else bench_layer(args, la, torch)
     smx = None if args.no_softmax else bench_softmax(args, la, torch)
+    smd = None if args.no_softmax else bench_softmax_decode(args, la, torch)
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)
     long_ctx = None if args.no_long else bench_long(args, la, torch)
     cpu = None
@@ -602,6 +647,7 @@ def main():
         "backward": bwd,
         "layer_with_projections": layer,
         "softmax_layer": smx,
+        "softmax_decode": smd,
         "decode": dec,
         "long_context": long_ctx,
         "cpu_baseline": cpu,

@@ -264,6 +264,35 @@ LA_API la_status lightning_attn_softmax_prefill_varlen(
     int64_t total_tokens, int heads, int head_dim, int rope_dim, double rope_base, float scale,
     la_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * One decode step of the softmax layer against a KV cache (cached generation:
+ * each new token attends over the keys and values of the tokens before it).
+ * For every sequence s with L = cache_len[s] tokens cached:
+ *     k_cache[s][L] = rope(k[s], L), v_cache[s][L] = v[s]      (appended)
+ *     out[s] = sum_{u <= L} softmax_u(scale <rope(q[s], L), k_cache[s][u]>) v_cache[s][u]
+ * with rope and scale as for lightning_attn_softmax_prefill (the cache holds
+ * rotated keys, rounded to bf16).  cache_len is not changed: the caller
+ * advances it (L + 1) before the next step.
+ *   q, k, v, out:     [nseq][heads][head_dim] bf16, the new token of each sequence
+ *   k_cache, v_cache: [nseq][heads][max_len][head_dim] bf16 (head-major: the keys of
+ *                     one sequence and head are contiguous), updated in place at slot L
+ *   cache_len:        device int32 [nseq]; each 0 <= L < max_len.  A sequence whose L
+ *                     is outside that range is skipped (its cache and out are left
+ *                     untouched) and marked 1 in the workspace's first nseq int32
+ *                     words (0 for the others), written on every call.
+ * bf16 and head_dim 128 only.  Work: the cached keys and values are read once
+ * (split over ranges of 512 keys, then combined).
+ */
+LA_API size_t lightning_attn_softmax_decode_workspace_size(int nseq, int max_len, int heads,
+                                                           int head_dim);
+LA_API la_status lightning_attn_softmax_decode(const void* q, const void* k, const void* v,
+                                               void* k_cache, void* v_cache,
+                                               const int32_t* cache_len, void* out, int nseq,
+                                               int max_len, int heads, int head_dim, int rope_dim,
+                                               double rope_base, float scale, la_dtype dtype,
+                                               void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
+
 /* Workspace bytes needed by lightning_attn_decode. */
 LA_API size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim);
 

@@ -879,6 +879,75 @@ la_status lightning_attn_softmax_prefill_varlen(const void* q, const void* k, co
                        scale, L, workspace, stream);
 }
 
+// Softmax decode workspace: status [S] int32, rotated queries [S][H][128]
+// fp32, partials [S][H][nsplit][130] fp32.
+static bool softmax_decode_layout(int nseq, int max_len, int heads, int head_dim, size_t* off_q,
+                                  size_t* off_part, size_t* bytes, int* nsplit) {
+    if (nseq < 0 || max_len < 1 || heads < 1 || head_dim != 128) return false;
+    const int ns = (max_len + la::SOFTMAX_DEC_SPLIT - 1) / la::SOFTMAX_DEC_SPLIT;
+    if ((int64_t)nseq * heads * ns > (int64_t)0x7fffffff) return false;
+    size_t off = align_up(sizeof(int32_t) * (size_t)nseq);
+    *off_q = off;
+    off = align_up(off + sizeof(float) * (size_t)nseq * heads * head_dim);
+    *off_part = off;
+    off = align_up(off + sizeof(float) * (size_t)nseq * heads * ns * (2 + head_dim));
+    *bytes = off;
+    *nsplit = ns;
+    return true;
+}
+
+size_t lightning_attn_softmax_decode_workspace_size(int nseq, int max_len, int heads,
+                                                    int head_dim) {
+    size_t oq, op, bytes;
+    int ns;
+    if (!softmax_decode_layout(nseq, max_len, heads, head_dim, &oq, &op, &bytes, &ns)) return 0;
+    return bytes;
+}
+
+la_status lightning_attn_softmax_decode(const void* q, const void* k, const void* v,
+                                        void* k_cache, void* v_cache, const int32_t* cache_len,
+                                        void* out, int nseq, int max_len, int heads, int head_dim,
+                                        int rope_dim, double rope_base, float scale,
+                                        la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    if (nseq < 0 || max_len < 1) return LA_ERR_BAD_SHAPE;
+    la_status st = softmax_checks(q, k, v, out, nseq, heads, head_dim, rope_dim, rope_base, scale,
+                                  dtype);
+    if (st != LA_OK) return st;
+    if (nseq > 0) {
+        if (!k_cache || !v_cache || !cache_len) return LA_ERR_NULL_POINTER;
+        if (!aligned16(k_cache) || !aligned16(v_cache)) return LA_ERR_MISALIGNED;
+    }
+    size_t off_q, off_part, bytes;
+    int ns;
+    if (!softmax_decode_layout(nseq, max_len, heads, head_dim, &off_q, &off_part, &bytes, &ns))
+        return LA_ERR_UNSUPPORTED;
+    if (!workspace) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    if (nseq == 0) return LA_OK;
+    char* ws = static_cast<char*>(workspace);
+    la::SoftmaxDecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.len = cache_len;
+    a.out = out;
+    a.nseq = nseq;
+    a.max_len = max_len;
+    a.H = heads;
+    a.rope_dim = rope_dim;
+    a.rope_base = rope_base;
+    a.scale = scale;
+    a.nsplit = ns;
+    a.status = reinterpret_cast<int32_t*>(ws);
+    a.qr = reinterpret_cast<float*>(ws + off_q);
+    a.part = reinterpret_cast<float*>(ws + off_part);
+    return la::launch_softmax_decode(a, stream) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 size_t lightning_attn_decode_workspace_size(int nseq, int heads, int head_dim) {
     if (nseq < 0 || heads < 1 || !supported_dim(head_dim)) return 0;
     return align_up(sizeof(float) * (size_t)nseq * heads * head_dim) +

@@ -194,4 +194,25 @@ struct SoftmaxArgs {
 hipError_t launch_softmax_rope(const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_softmax_fwd(const SoftmaxArgs& a, hipStream_t st);
 
+// One decode step of the softmax layer against a KV cache: the new token's
+// key (rotated at position len[s]) and value are appended at slot len[s], and
+// its query (rotated likewise) attends over the len[s] + 1 keys.  Keys are
+// split into ranges of SOFTMAX_DEC_SPLIT, each a workgroup's partial
+// (max, sum, output); a second kernel combines them.
+constexpr int SOFTMAX_DEC_SPLIT = 512;
+struct SoftmaxDecodeArgs {
+    const void *q, *k, *v;    // [S][H][128] bf16, the new tokens
+    void *k_cache, *v_cache;  // [S][H][max_len][128] bf16 (keys stored rotated)
+    const int32_t* len;       // device [S]: tokens already cached
+    void* out;                // [S][H][128] bf16
+    int nseq, max_len, H, rope_dim;
+    double rope_base;
+    float scale;
+    int nsplit;               // ceil(max_len / SOFTMAX_DEC_SPLIT)
+    int32_t* status;          // device [S]: 1 where len is outside [0, max_len), else 0
+    float* qr;                // [S][H][128] rotated queries, fp32
+    float* part;              // [S][H][nsplit][2 + 128]: max, sum, output
+};
+hipError_t launch_softmax_decode(const SoftmaxDecodeArgs& a, hipStream_t st);
+
 }  // namespace la

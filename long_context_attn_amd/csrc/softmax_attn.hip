@@ -363,7 +363,182 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
     }
 }
 
+// ----------------------------------------------------------------- decode
+// One decode step against a KV cache (bound by HBM: the cached keys and
+// values are read once).  The cache is head-major, [S][H][max_len][128], so
+// the keys of one (sequence, head) are one contiguous stream.  Step 1: per sequence, rotate the new key at
+// position len and store it with the value at slot len; rotate the query
+// (kept in fp32).  Step 2: one 256-thread workgroup per (sequence, head,
+// 512-key range): 16 threads per key (8 features each), 16 keys at a time,
+// each thread keeping a running maximum, sum and 8 output features over the
+// keys it saw; the 16 key slots are merged in LDS into one partial.  Step 3:
+// the partials of a (sequence, head) are merged and normalised.
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_KEYS = DEC_THREADS / 16;  // keys per pass
+constexpr int DEC_UNROLL = 4;               // passes whose loads are in flight together
+
+__global__ __launch_bounds__(DEC_THREADS) void softmax_append_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ kc, __bf16* __restrict__ vc, const int32_t* __restrict__ len,
+    float* __restrict__ qr, int32_t* __restrict__ status, int max_len, int H, int rope_dim,
+    const RopeTheta th) {
+    const int s = blockIdx.x;
+    const int L = len[s];
+    const bool bad = L < 0 || L >= max_len;
+    if (threadIdx.x == 0) status[s] = bad ? 1 : 0;  // written on every call: nothing to clear
+    if (bad) return;
+    const int HD = H * MD;
+    const int64_t src = (int64_t)s * HD;
+    for (int e = threadIdx.x * 2; e < HD; e += DEC_THREADS * 2) {
+        const int h = e / MD, f = e - h * MD;  // head, feature within it (even)
+        const int64_t dst = (((int64_t)s * H + h) * max_len + L) * MD + f;
+        float q0 = (float)q[src + e], q1 = (float)q[src + e + 1];
+        float k0 = (float)k[src + e], k1 = (float)k[src + e + 1];
+        if (f < rope_dim) {
+            const float2 r = rope_cs(L, th.t[f / 2]);
+            const float a = q0, b = q1;
+            q0 = a * r.x - b * r.y;
+            q1 = a * r.y + b * r.x;
+            const float c = k0, d = k1;
+            k0 = c * r.x - d * r.y;
+            k1 = c * r.y + d * r.x;
+        }
+        qr[src + e] = q0;
+        qr[src + e + 1] = q1;
+        kc[dst] = (__bf16)k0;
+        kc[dst + 1] = (__bf16)k1;
+        vc[dst] = v[src + e];
+        vc[dst + 1] = v[src + e + 1];
+    }
+}
+
+__global__ __launch_bounds__(DEC_THREADS) void softmax_split_kernel(
+    const float* __restrict__ qr, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const int32_t* __restrict__ len, float* __restrict__ part, int max_len, int H, int nsplit,
+    float sl2) {
+    __shared__ float sm[DEC_KEYS], sl[DEC_KEYS];
+    __shared__ float so[DEC_KEYS][MD + 4];
+    const int sp = blockIdx.x % nsplit;
+    const int sh = blockIdx.x / nsplit;  // sequence * H + head
+    const int s = sh / H, h = sh - s * H;
+    const int L = len[s];
+    float* pp = part + (int64_t)blockIdx.x * (2 + MD);
+    const int j0 = sp * SOFTMAX_DEC_SPLIT;
+    const int nk = (L < 0 || L >= max_len) ? 0 : min(SOFTMAX_DEC_SPLIT, L + 1 - j0);
+    const int t = threadIdx.x, slot = t >> 4, c = t & 15;
+    if (nk <= 0) {  // no keys in this range
+        if (t == 0) {
+            pp[0] = -INFINITY;
+            pp[1] = 0.f;
+        }
+        return;
+    }
+    float qv[8];
+    {
+        const float* qs = qr + (int64_t)sh * MD + 8 * c;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qv[u] = qs[u] * sl2;  // logits in base 2
+    }
+    const int64_t base = ((int64_t)sh * max_len + j0) * MD + 8 * c;
+    float m = -INFINITY, l = 0.f, o[8] = {};
+    for (int j = slot; j < nk; j += DEC_KEYS * DEC_UNROLL) {
+        bf16x8 kk[DEC_UNROLL], vv[DEC_UNROLL];
+#pragma unroll
+        for (int u = 0; u < DEC_UNROLL; ++u) {
+            const int jj = min(j + u * DEC_KEYS, nk - 1);
+            kk[u] = *reinterpret_cast<const bf16x8*>(kc + base + (int64_t)jj * MD);
+            vv[u] = *reinterpret_cast<const bf16x8*>(vc + base + (int64_t)jj * MD);
+        }
+#pragma unroll
+        for (int u = 0; u < DEC_UNROLL; ++u) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += qv[e] * (float)kk[u][e];
+            // sum over the 16 threads of the key
+            d += __shfl_xor(d, 1, 16);
+            d += __shfl_xor(d, 2, 16);
+            d += __shfl_xor(d, 4, 16);
+            d += __shfl_xor(d, 8, 16);
+            if (j + u * DEC_KEYS < nk) {
+                const float mn = fmaxf(m, d);
+                const float al = __builtin_amdgcn_exp2f(m - mn);
+                const float p = __builtin_amdgcn_exp2f(d - mn);
+                l = l * al + p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = o[e] * al + p * (float)vv[u][e];
+                m = mn;
+            }
+        }
+    }
+    // merge the 16 key slots
+    if (c == 0) {
+        sm[slot] = m;
+        sl[slot] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) so[slot][8 * c + e] = o[e];
+    __syncthreads();
+    if (t < MD) {
+        float M = -INFINITY;
+        for (int i = 0; i < DEC_KEYS; ++i) M = fmaxf(M, sm[i]);
+        float lt = 0.f, ot = 0.f;
+        for (int i = 0; i < DEC_KEYS; ++i) {
+            if (sm[i] == -INFINITY) continue;  // a slot that saw no key
+            const float w = __builtin_amdgcn_exp2f(sm[i] - M);
+            lt += sl[i] * w;
+            ot += so[i][t] * w;
+        }
+        pp[2 + t] = ot;
+        if (t == 0) {
+            pp[0] = M;
+            pp[1] = lt;
+        }
+    }
+}
+
+__global__ __launch_bounds__(MD) void softmax_combine_kernel(const float* __restrict__ part,
+                                                             __bf16* __restrict__ out,
+                                                             const int32_t* __restrict__ len,
+                                                             int max_len, int H, int nsplit) {
+    const int sh = blockIdx.x, s = sh / H, t = threadIdx.x;
+    const int L = len[s];
+    if (L < 0 || L >= max_len) return;  // reported by the append step; out left as it was
+    const float* pp = part + (int64_t)sh * nsplit * (2 + MD);
+    float M = -INFINITY;
+    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, pp[i * (2 + MD)]);
+    float lt = 0.f, ot = 0.f;
+    for (int i = 0; i < nsplit; ++i) {
+        const float mi = pp[i * (2 + MD)];
+        if (mi == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(mi - M);
+        lt += pp[i * (2 + MD) + 1] * w;
+        ot += pp[i * (2 + MD) + 2 + t] * w;
+    }
+    out[(int64_t)sh * MD + t] = (__bf16)(ot / lt);
+}
+
 }  // namespace
+
+hipError_t launch_softmax_decode(const SoftmaxDecodeArgs& a, hipStream_t st) {
+    if (a.nseq == 0) return hipSuccess;
+    SoftmaxArgs ra{};
+    ra.rope_dim = a.rope_dim;
+    ra.rope_base = a.rope_base;
+    hipLaunchKernelGGL(softmax_append_kernel, dim3((unsigned)a.nseq), dim3(DEC_THREADS), 0, st,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (__bf16*)a.k_cache, (__bf16*)a.v_cache, a.len, a.qr, a.status, a.max_len,
+                       a.H, a.rope_dim, rope_theta(ra));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (int64_t)a.nseq * a.H * a.nsplit;
+    hipLaunchKernelGGL(softmax_split_kernel, dim3((unsigned)blocks), dim3(DEC_THREADS), 0, st,
+                       a.qr, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache, a.len, a.part,
+                       a.max_len, a.H, a.nsplit, a.scale * 1.4426950408889634f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(softmax_combine_kernel, dim3((unsigned)(a.nseq * a.H)), dim3(MD), 0, st,
+                       a.part, (__bf16*)a.out, a.len, a.max_len, a.H, a.nsplit);
+    return hipGetLastError();
+}
 
 hipError_t launch_softmax_rope(const SoftmaxArgs& a, hipStream_t st) {
     if (a.max_tiles == 0) return hipSuccess;

@@ -90,6 +90,11 @@ def library():
         lib.lightning_attn_softmax_prefill_varlen.argtypes = [_P] * 5 + [_I, _I64, _I, _I, _I, _D,
                                                                         _F, _I, _P, _SZ, _P]
         lib.lightning_attn_softmax_prefill_varlen.restype = _I
+        lib.lightning_attn_softmax_decode_workspace_size.argtypes = [_I, _I, _I, _I]
+        lib.lightning_attn_softmax_decode_workspace_size.restype = _SZ
+        lib.lightning_attn_softmax_decode.argtypes = [_P] * 7 + [_I, _I, _I, _I, _I, _D, _F, _I,
+                                                                _P, _SZ, _P]
+        lib.lightning_attn_softmax_decode.restype = _I
         lib.lightning_attn_decode_workspace_size.argtypes = [_I, _I, _I]
         lib.lightning_attn_decode_workspace_size.restype = _SZ
         lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
@@ -489,4 +494,40 @@ def softmax_prefill_varlen(q, k, v, cu_seqlens, *, rope_dim=None, rope_base=ROPE
     _check(library().lightning_attn_softmax_prefill_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), nseq, T, H, D, rd,
         float(rope_base), sc, _dtype(q), _ptr(ws), ws_bytes, _stream(q.device)))
+    return out
+
+
+def softmax_decode_workspace_size(nseq, max_len, heads, head_dim=128) -> int:
+    return int(library().lightning_attn_softmax_decode_workspace_size(
+        int(nseq), int(max_len), int(heads), int(head_dim)))
+
+
+def softmax_decode(q, k, v, k_cache, v_cache, cache_len, *, rope_dim=None, rope_base=ROPE_BASE,
+                   scale=None, out=None, workspace=None):
+    """One decode step of the softmax layer: q, k, v [S, H, D] bf16 (the new
+    token of each sequence); k_cache, v_cache [S, H, max_len, D] bf16 (head-major,
+    keys stored rotated), updated in place at slot cache_len[s]; cache_len
+    int32 [S] on the device, not advanced here.  Returns out [S, H, D]."""
+    rd, sc = _softmax_args(q, k, v, rope_dim, scale)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q, k, v must be [S, H, D] and the caches [S, H, max_len, D]")
+    S, H, D = q.shape
+    if k_cache.shape[0] != S or k_cache.shape[1] != H or k_cache.shape[3] != D:
+        raise ValueError("cache shape does not match q")
+    _same(q, k_cache, v_cache)
+    if cache_len.dtype != torch.int32 or cache_len.numel() != S or cache_len.device != q.device \
+            or not cache_len.is_contiguous():
+        raise ValueError("cache_len must be a contiguous int32 vector of S entries on the device")
+    max_len = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _same(q, out)
+    ws_bytes = softmax_decode_workspace_size(S, max_len, H, D)
+    if ws_bytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    ws = _workspace(ws_bytes, q.device, workspace)
+    _check(library().lightning_attn_softmax_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(out), S,
+        max_len, H, D, rd, float(rope_base), sc, _dtype(q), _ptr(ws), ws_bytes,
+        _stream(q.device)))
     return out

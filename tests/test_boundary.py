@@ -42,9 +42,10 @@ def test_header_declares_the_three_calls():
               "lightning_attn_backward_varlen", "lightning_attn_backward_workspace_size",
               "lightning_attn_layer_prefill", "lightning_attn_layer_workspace_size",
               "lightning_attn_softmax_prefill", "lightning_attn_softmax_prefill_varlen",
-              "lightning_attn_softmax_workspace_size"):
+              "lightning_attn_softmax_workspace_size", "lightning_attn_softmax_decode",
+              "lightning_attn_softmax_decode_workspace_size"):
         assert n in names
-    assert len(names) == 23
+    assert len(names) == 25
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -319,6 +320,36 @@ def test_softmax_workspace_and_validation(lib):
     assert vcall(nseq=0) == SHAPE
     assert vcall(ws_bytes=10) == WS
     assert vcall(nseq=0, total=0) == OK
+
+
+def test_softmax_decode_workspace_and_validation(lib):
+    # status words, fp32 rotated queries, (2 + 128)-float partials per 512-key range
+    S, L, H, D = 4, 1000, 8, 128
+    ws = ops.softmax_decode_workspace_size(S, L, H, D)
+    need = S * 4 + S * H * D * 4 + S * H * 2 * (2 + D) * 4
+    assert need <= ws < need + 1024
+    assert ops.softmax_decode_workspace_size(S, 0, H, D) == 0
+    assert ops.softmax_decode_workspace_size(S, L, H, 64) == 0
+    D64 = ctypes.c_double
+
+    def call(q=A, kc=A, ln=A, out=A, nseq=4, max_len=1000, heads=8, d=128, rd=64, scale=0.088,
+             dtype=BF16, ws=A, ws_bytes=1 << 40):
+        return lib.lightning_attn_softmax_decode(q, A, A, kc, A, ln, out, nseq, max_len, heads,
+                                                 d, rd, D64(1e7), scale, dtype, ws, ws_bytes,
+                                                 None)
+    assert call(q=None) == NULLP
+    assert call(kc=None) == NULLP
+    assert call(ln=None) == NULLP
+    assert call(out=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(kc=A + 8) == MISAL
+    assert call(d=64) == UNSUP
+    assert call(dtype=F32) == UNSUP
+    assert call(nseq=-1) == SHAPE
+    assert call(max_len=0) == SHAPE
+    assert call(scale=-1.0) == SHAPE
+    assert call(ws_bytes=100) == WS
+    assert call(nseq=0, q=None, kc=None, ln=None, out=None) == OK
 
 
 def test_decode_validation(lib):

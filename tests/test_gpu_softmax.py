@@ -7,6 +7,9 @@ compared with oracle.softmax_attention on the same bf16 inputs, to the bf16 bar
 128-query tiles and 64-key blocks with ragged tails; varlen packs include
 empty and one-token sequences; the full 8192-token x 64-head workload is
 checked on sampled tokens (every head), which the oracle computes one by one.
+The decode step against a KV cache is checked against the oracle's attention
+row of the new token, against a prefill of the same tokens, and for its
+handling of cache lengths out of range.
 """
 import numpy as np
 import pytest
@@ -99,3 +102,92 @@ def test_softmax_8k_workload_sampled():
     q, k, v = (host(t).reshape(N, H, D) for t in x)
     ref = oracle.softmax_attention(q, k, v, rows=rows)
     check(host(out).reshape(N, H, D)[rows], ref[rows], BF, "softmax 8K x 64 heads, sampled")
+
+
+def _decode_case(lens, H, max_len, key):
+    """Raw q, k, v of L + 1 tokens per sequence.  The caches hold the first L
+    keys rotated (by the oracle, rounded to bf16) and values, and stale values
+    in slot L; the step's expected output is row L of the oracle's attention on
+    the raw tokens, and slot L must end up holding the new key rotated at L."""
+    D = 128
+    S = len(lens)
+    kc = np.zeros((S, max_len, H, D), np.float32)
+    vc = np.zeros((S, max_len, H, D), np.float32)
+    qn, kn, vn = (np.zeros((S, H, D), np.float32) for _ in range(3))
+    ref = np.zeros((S, H, D))
+    new_k, new_v = [], []
+    for s_, L in enumerate(lens):
+        q, k, v = qkv(L + 1, H, D, key=key + s_)
+        kr = host(dev(oracle.rope(k), BF))  # the cache's keys: rotated, bf16
+        kc[s_, :L] = kr[:L]
+        vc[s_, :L] = v[:L]
+        kc[s_, L] = -7.0  # stale contents of the slot the step writes
+        vc[s_, L] = 3.0
+        qn[s_], kn[s_], vn[s_] = q[L], k[L], v[L]
+        ref[s_] = oracle.softmax_attention(q, k, v, rows=[L])[L]
+        new_k.append(kr[L])
+        new_v.append(v[L])
+    # head-major caches [S, H, max_len, D]
+    kc, vc = (np.ascontiguousarray(c.transpose(0, 2, 1, 3)) for c in (kc, vc))
+    return qn, kn, vn, kc, vc, ref, new_k, new_v
+
+
+@pytest.mark.parametrize("lens,H,max_len", [
+    ([0, 1, 511, 512, 513, 1500, 7], 2, 1600),   # empty cache, one key, split edges
+    ([4000, 2048], 4, 4096),
+])
+def test_softmax_decode(lens, H, max_len):
+    qn, kn, vn, kc, vc, ref, new_k, new_v = _decode_case(lens, H, max_len, 300 + len(lens))
+    say("softmax decode lens", lens, "H", H, "max_len", max_len)
+    kcd, vcd = dev(kc, BF), dev(vc, BF)
+    ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = la.softmax_decode(dev(qn, BF), dev(kn, BF), dev(vn, BF), kcd, vcd, ln)
+    torch.cuda.synchronize()
+    check(out, ref, BF, "softmax decode lens=%s" % lens)
+    # the new key (rotated at its position) and value were appended at slot L
+    for s_, L in enumerate(lens):
+        np.testing.assert_allclose(host(kcd[s_, :, L]), new_k[s_], rtol=0,
+                                   atol=2e-2 * np.abs(new_k[s_]).max())
+        assert np.array_equal(host(vcd[s_, :, L]), new_v[s_])
+    assert torch.equal(ln, torch.tensor(lens, dtype=torch.int32, device="cuda"))  # not advanced
+
+
+def test_softmax_decode_steps_match_prefill():
+    """Prefill-free generation: starting from an empty cache, N decode steps
+    (the caller advancing the lengths) give the same outputs as one causal
+    prefill of the N tokens."""
+    H, D, N = 2, 128, 300
+    q, k, v = qkv(N, H, D, key=401)
+    kc = torch.zeros(1, H, N, D, device="cuda", dtype=BF)
+    vc = torch.zeros_like(kc)
+    ln = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qd, kd, vd = (dev(x, BF) for x in (q, k, v))
+    say("softmax decode: 300 steps from an empty cache")
+    outs = []
+    for t in range(N):
+        outs.append(la.softmax_decode(qd[t:t + 1], kd[t:t + 1], vd[t:t + 1], kc, vc, ln))
+        ln += 1
+    torch.cuda.synchronize()
+    dec = torch.cat(outs)
+    pre = la.softmax_prefill(*(x.view(1, N, H, D) for x in (qd, kd, vd))).view(N, H, D)
+    ref = oracle.softmax_attention(q, k, v)
+    check(dec, ref, BF, "softmax decode steps vs oracle")
+    check(dec, host(pre).astype(np.float64), BF, "softmax decode steps vs the GPU prefill")
+
+
+def test_softmax_decode_bad_length_is_reported():
+    H, D, max_len = 2, 128, 64
+    q, k, v = qkv(3, H, D, key=402)
+    kc = torch.zeros(3, H, max_len, D, device="cuda", dtype=BF)
+    vc = torch.zeros_like(kc)
+    ln = torch.tensor([5, max_len, -1], dtype=torch.int32, device="cuda")
+    out = torch.full((3, H, D), 9.0, device="cuda", dtype=BF)
+    ws = torch.empty(la.softmax_decode_workspace_size(3, max_len, H, D), dtype=torch.uint8,
+                     device="cuda")
+    say("softmax decode with out-of-range lengths")
+    la.softmax_decode(*(dev(x, BF) for x in (q, k, v)), kc, vc, ln, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    status = ws[:12].view(torch.int32).cpu().tolist()
+    assert status == [0, 1, 1]
+    assert torch.all(out[1:] == 9.0)           # skipped sequences keep their output
+    assert torch.count_nonzero(kc[1:]) == 0    # and their caches
