@@ -15,8 +15,9 @@ value = prefill tokens/s, in steady state: the warm-up (default 200 calls,
 about 45 ms) lets the clocks settle first; the first few dozen calls on an
 idle GPU run ~20% slower.  Also reported: TFLOP/s on the block-tiled FLOP
 count, the per-kernel split (HIP events recorded between the library's
-kernels on the stream they run on: the plan, the chunk sums, the scan of the
-states entering the chunks, and the walk with the RMSNorm fused), the
+kernels on the stream they run on: the plan (no kernel for uniform rows: the
+chunk-sum kernel writes it), the chunk sums, the scan of the states entering
+the chunks, and the walk with the RMSNorm fused), the
 roofline of the walk kernel, the state-only pass on the same K and V, the
 backward pass on the same inputs (time per call against its HBM bytes), the
 layer with its projections (hidden 6144: four input GEMMs with SiLU in the
@@ -199,9 +200,10 @@ def bench_prefill(args, la, torch, hip):
     res = dict(
         ms_per_step=ms, tokens_per_s=tok_s, tflops=fl / (ms * 1e-3) / 1e12,
         layer_hbm_frac=layer_bytes_per_token(H, D) * tokens / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        # stage marks: plan, chunk_state (chunk sums), state_scan, walk (the
+        # stage marks: plan (empty for uniform rows: the chunk-sum kernel
+        # writes the plan), chunk_state (chunk sums), state_scan, walk (the
         # walk kernel with the RMSNorm fused; the norm_gate mark stays empty)
-        kernels_us={"plan_kernel": round(per["plan"] * 1e3, 2),
+        kernels_us={"plan": round(per["plan"] * 1e3, 2),
                     "chunk_state_mfma_kernel": round(per["chunk_state"] * 1e3, 2),
                     "state_scan_kernel": round(per["state_scan"] * 1e3, 2),
                     "prefill_mfma_kernel": round(per["walk"] * 1e3, 2)},

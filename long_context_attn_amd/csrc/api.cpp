@@ -254,8 +254,10 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
         a.clear = a.part;
         a.clear_words = (int64_t)((L.off_clear_end - L.off_part) / sizeof(uint64_t));
     }
+    // uniform rows on the MFMA path: the chunk-sum kernel writes the plan
+    a.inline_plan = mfma && a.cu == nullptr && a.seqlen > 0;
     hipError_t e = marks.mark(stream);
-    if (e == hipSuccess) e = la::launch_plan(a, stream);
+    if (e == hipSuccess && !a.inline_plan) e = la::launch_plan(a, stream);
     if (e == hipSuccess) e = marks.mark(stream);
     if (mfma) {
         // chunk sums (every chunk but each sequence's last), the scan of the

@@ -80,6 +80,11 @@ struct PrefillArgs {
     // MFMA path: q, k, v hold SiLU(q), SiLU(k), SiLU(v) already (applied by
     // the projection's epilogue); the gate is raw either way
     bool preact;
+    // MFMA prefill of uniform rows (cu == null): no plan kernel; the chunk-sum
+    // kernel computes its chunks from (nseq, seqlen, chunk), and extra
+    // workgroups of it write the plan tables, reset the header and clear the
+    // exchange words for the kernels after it
+    bool inline_plan;
     // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
     // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block.
     // Each word holds a float in its low half and 1 in its high half once

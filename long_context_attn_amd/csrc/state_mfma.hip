@@ -35,19 +35,70 @@ struct StateLds {
 // dv in [32 (w % 4), +32).  Every wave takes part in the SiLU: it is a chain
 // of dependent transcendental operations, and two waves per SIMD hide its
 // latency where one could not.
+// Uniform rows without a plan kernel: nseq rows of seqlen tokens cut into
+// cps = ceil(seqlen / chunk) chunks each; the last `extra` workgroups of the
+// grid write what the plan kernel would (tables, header, cleared words).
+struct InlinePlan {
+    int extra;  // 0: the plan kernel ran, read its tables
+    int nseq, cps, chunk;
+    int64_t seqlen;
+    PlanHeader* hdr;
+    SegEntry* segs;
+    ChunkEntry* chunks;
+    uint64_t* clear;
+    int64_t clear_words;
+};
+
+__device__ __forceinline__ ChunkEntry uniform_chunk(const InlinePlan& ip, int c) {
+    const int s = c / ip.cps, i = c - s * ip.cps;
+    ChunkEntry ce;
+    ce.start = (int64_t)s * ip.seqlen + (int64_t)i * ip.chunk;
+    ce.len = (int)min((int64_t)ip.chunk, ip.seqlen - (int64_t)i * ip.chunk);
+    ce.seg = s;
+    return ce;
+}
+
+__device__ void write_plan(const InlinePlan& ip, int e, int tid) {
+    const int64_t stride = (int64_t)ip.extra * ST_THREADS;
+    const int64_t i0 = (int64_t)e * ST_THREADS + tid;
+    for (int64_t i = i0; i < ip.clear_words; i += stride) ip.clear[i] = 0;
+    const int64_t nch = (int64_t)ip.nseq * ip.cps;
+    for (int64_t c = i0; c < nch; c += stride) ip.chunks[c] = uniform_chunk(ip, (int)c);
+    for (int64_t s = i0; s < ip.nseq; s += stride)
+        ip.segs[s] = SegEntry{(int32_t)(s * ip.cps), ip.cps};
+    if (e == 0 && tid == 0) {
+        ip.hdr->ticket = 0;
+        ip.hdr->wait_site = ip.hdr->wait_chunk = ip.hdr->wait_head = 0;
+        ip.hdr->error = 0;
+        ip.hdr->n_chunks = (int32_t)nch;
+    }
+}
+
 template <bool SA, bool SB>
 __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
-    const ChunkEntry* __restrict__ chunks, float* __restrict__ states, int H, bool skip_last) {
+    const ChunkEntry* __restrict__ chunks, float* __restrict__ states, int H, bool skip_last,
+    const InlinePlan ip) {
     __shared__ __attribute__((aligned(16))) StateLds L;
-    const int nch = hdr->n_chunks;
+    const int n_sum = (int)gridDim.x - ip.extra;
+    if ((int)blockIdx.x >= n_sum) {
+        write_plan(ip, (int)blockIdx.x - n_sum, threadIdx.x);
+        return;
+    }
     const int c = blockIdx.x / H, h = blockIdx.x - c * H;
-    if (c >= nch) return;
-    const ChunkEntry ce = chunks[c];
-    if (skip_last) {
-        const SegEntry se = segs[ce.seg];
-        if (c == se.first + se.count - 1) return;
+    ChunkEntry ce;
+    if (ip.extra > 0) {
+        if (c >= ip.nseq * ip.cps) return;
+        ce = uniform_chunk(ip, c);
+        if (skip_last && c - ce.seg * ip.cps == ip.cps - 1) return;
+    } else {
+        if (c >= hdr->n_chunks) return;
+        ce = chunks[c];
+        if (skip_last) {
+            const SegEntry se = segs[ce.seg];
+            if (c == se.first + se.count - 1) return;
+        }
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int HD = H * MD;
@@ -134,13 +185,26 @@ bool state_mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && 
 hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_x,
                                   bool silu_y, float* states, bool skip_last, hipStream_t st) {
     if (a.max_chunks == 0) return hipSuccess;
-    const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H));
+    InlinePlan ip{};
+    if (a.inline_plan) {
+        ip.extra = 64;  // on the CUs the chunk sums leave idle
+        ip.nseq = a.nseq;
+        ip.chunk = a.chunk;
+        ip.seqlen = a.seqlen;
+        ip.cps = (int)((a.seqlen + a.chunk - 1) / a.chunk);
+        ip.hdr = a.hdr;
+        ip.segs = a.segs;
+        ip.chunks = a.chunks;
+        ip.clear = a.clear;
+        ip.clear_words = a.clear_words;
+    }
+    const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H + ip.extra));
     auto* fn = silu_x ? (silu_y ? &chunk_state_mfma_kernel<true, true>
                                 : &chunk_state_mfma_kernel<true, false>)
                       : (silu_y ? &chunk_state_mfma_kernel<false, true>
                                 : &chunk_state_mfma_kernel<false, false>);
     hipLaunchKernelGGL(fn, grid, dim3(ST_THREADS), 0, st, (const __bf16*)x, (const __bf16*)y,
-                       a.hdr, a.segs, a.chunks, states, a.H, skip_last);
+                       a.hdr, a.segs, a.chunks, states, a.H, skip_last, ip);
     return hipGetLastError();
 }
 
