@@ -62,7 +62,8 @@ bool lane_path(int heads, int chunk_tokens, bool fused, int cus) {
 //  * otherwise [ChunkEntry x max_chunks], then per-chunk states
 //    [max_chunks][H][D][D] fp32 (chunk sums, then the states entering the
 //    chunks), then
-//  * MFMA path: the words the plan kernel clears on every call, the
+//  * MFMA path: the words cleared on every call before the walk (by the plan
+//    kernel, or for uniform rows by the chunk-sum kernel), the
 //    per-(chunk, block) RMSNorm exchange part [n_slots][H][64] and
 //    rsub [n_slots][ceil(H/16)][64].
 bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,

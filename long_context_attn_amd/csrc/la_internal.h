@@ -88,11 +88,12 @@ struct PrefillArgs {
     // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
     // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block.
     // Each word holds a float in its low half and 1 in its high half once
-    // written (0 = not yet written); the plan kernel clears them.
+    // written (0 = not yet written); cleared on every call by the plan kernel
+    // (or, for uniform rows, by the chunk-sum kernel's extra workgroups).
     int n_slots;
     uint64_t* part;           // [n_slots][H][64] per-head sums of y^2 per token
     uint64_t* rsub;           // [n_slots][ceil(H / 16)][64] sums over groups of 16 heads
-    // words the plan kernel zeroes on every call (exchange words)
+    // words zeroed on every call before the walk (exchange words)
     uint64_t* clear;
     int64_t clear_words;
     // lane kernel: per-token totals over all lanes, [ring slots][64]
