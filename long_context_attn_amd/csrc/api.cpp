@@ -547,10 +547,12 @@ static la_status run_state(la::PrefillArgs& a, const Layout& L, void* workspace,
     a.states = reinterpret_cast<float*>(ws + L.off_states);
     a.clear = nullptr;
     a.clear_words = 0;
-    hipError_t e = la::launch_plan(a, stream);
+    // uniform rows on the MFMA path: the chunk-sum kernel writes the plan
+    const bool mfma = la::state_mfma_supported(a);
+    a.inline_plan = mfma && a.cu == nullptr && a.seqlen > 0;
+    hipError_t e = a.inline_plan ? hipSuccess : la::launch_plan(a, stream);
     if (e == hipSuccess)
-        e = la::state_mfma_supported(a) ? la::launch_chunk_state_mfma(a, stream)
-                                        : la::launch_chunk_state_valu(a, stream);
+        e = mfma ? la::launch_chunk_state_mfma(a, stream) : la::launch_chunk_state_valu(a, stream);
     if (e == hipSuccess) e = la::launch_state_scan(a, stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
