@@ -184,7 +184,7 @@ bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block
     L->off_gstates = off;
     off = align_up(off + sizeof(float) * (size_t)maxc * heads * DD);
     L->off_y = off;
-    off = align_up(off + act);
+    off = align_up(off + (L->mfma ? act / 2 : act));  // y: bf16 on the MFMA path
     L->off_dy = off;
     off = align_up(off + (L->mfma ? act / 2 : act));
     if (!L->mfma) {

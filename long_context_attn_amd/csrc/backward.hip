@@ -215,9 +215,9 @@ __device__ __forceinline__ void store8(__bf16* p, const float (&x)[8]) {
 // reductions give r and <a, yhat>, and the same registers give dy (DYT:
 // fp32, or bf16 as an MFMA operand) and dgate.  dw is accumulated over the
 // workgroup's tokens and written as one partial sum row.
-template <class TT, class DYT, int CPT>
+template <class TT, class DYT, class YT, int CPT>
 __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
-    const float* __restrict__ y, const TT* __restrict__ g, const TT* __restrict__ w,
+    const YT* __restrict__ y, const TT* __restrict__ g, const TT* __restrict__ w,
     const TT* __restrict__ dout, DYT* __restrict__ dy, TT* __restrict__ dg,
     float* __restrict__ dw_part, int64_t T, int HD, float eps) {
     __shared__ float red[2][EW_THREADS / 64];
@@ -359,8 +359,9 @@ hipError_t dw_reduce(const BackwardArgs& a, int HD) {
     return hipGetLastError();
 }
 
-// norm backward launch: CPT pieces of 8 per thread cover H*D <= 2048 CPT
-template <class TT, class DYT>
+// norm backward launch: CPT pieces of 8 per thread cover H*D <= 2048 CPT;
+// y is stored as YT (fp32 on the portable path, bf16 on the MFMA path)
+template <class TT, class DYT, class YT>
 hipError_t norm_backward(const BackwardArgs& a, DYT* dy) {
     if (a.n_tb == 0) return hipSuccess;
     const PrefillArgs& p = a.p;
@@ -368,7 +369,8 @@ hipError_t norm_backward(const BackwardArgs& a, DYT* dy) {
     const int per = (HD / 8 + EW_THREADS - 1) / EW_THREADS;
     const dim3 grid((unsigned)a.n_tb), block(EW_THREADS);
 #define LA_NB(C)                                                                                \
-    hipLaunchKernelGGL((norm_backward_kernel<TT, DYT, C>), grid, block, 0, a.stream, a.y,       \
+    hipLaunchKernelGGL((norm_backward_kernel<TT, DYT, YT, C>), grid, block, 0, a.stream,        \
+                       (const YT*)a.y,                                                          \
                        (const TT*)p.g, (const TT*)p.w, (const TT*)a.dout, dy, (TT*)a.dg,        \
                        a.dw_part, p.total, HD, p.eps)
     if (per <= 1) LA_NB(1);
@@ -406,7 +408,7 @@ hipError_t backward_mfma(const BackwardArgs& a) {
         if ((e = launch_state_scan(s, st)) != hipSuccess) return e;
     }
     if ((e = launch_backward_walk_y(a)) != hipSuccess) return e;
-    if ((e = norm_backward<__bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
+    if ((e = norm_backward<__bf16, __bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
     if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
     if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, true, false, a.gstates, false, st)) != hipSuccess)
         return e;
@@ -440,7 +442,7 @@ hipError_t backward_db(const BackwardArgs& a) {
     if ((e = walk<TT, D, BK, false, false, 0>(a, a.qs, a.ks, a.vs, p.states, a.y, nullptr,
                                                nullptr)) != hipSuccess)
         return e;
-    if ((e = norm_backward<TT, float>(a, dy)) != hipSuccess) return e;
+    if ((e = norm_backward<TT, float, float>(a, dy)) != hipSuccess) return e;
     if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
     // reverse chunk sums of q~^T dy, G_exit and dS0
     hipLaunchKernelGGL((chunk_sum_kernel<D>), cgrid, dim3(D), 0, st, a.qs, dy, p.hdr, p.chunks,

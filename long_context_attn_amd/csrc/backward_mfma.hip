@@ -59,7 +59,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, in
 
 // One walk per (chunk, head).  SX, SK, SV: SiLU on X, K, V; REV: anti-causal;
 // TRS: the state is read transposed; EPI = 0: Y to yout (fp32), 1: gout =
-// Y * SiLU'(raw) (bf16).  Waves 4-7 stage the tiles (two blocks ahead, two
+// Y * SiLU'(raw) (bf16), 2: gout = Y (bf16).  Waves 4-7 stage the tiles (two blocks ahead, two
 // LDS buffers), waves 0-3 hold 32 columns of R each and compute, as in the
 // forward walk; the consumers store their outputs straight from the
 // accumulators.
@@ -229,6 +229,7 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_walk_mfma_kernel(
             bf16x4 rw[2][4];
             if (EPI == 1) {
                 // the raw inputs of the SiLU' factor, loaded ahead of the products
+                // (EPI 2 stores Y in bf16 with no factor)
                 const __amdgpu_buffer_rsrc_t rr = tile_rsrc(raw + tbase, n, HD);
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_walk_mfma_kernel(
                         bf16x4 o;
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            o[u] = (__bf16)(O[tb][4 * q + u] * silu_grad_f((float)rw[tb][q][u]));
+                            o[u] = (__bf16)(EPI == 1 ? O[tb][4 * q + u] * silu_grad_f((float)rw[tb][q][u])
+                                                     : O[tb][4 * q + u]);
                         ob[tb][q] = __builtin_bit_cast(u32x2, o);
                         __builtin_amdgcn_raw_buffer_store_b64(ob[tb][q], ro,
                                                               (ooff + 32 * tb * HD + 8 * q) * 2, 0, 0);
@@ -331,8 +333,9 @@ hipError_t walk(const BackwardArgs& a, const void* x, const void* k, const void*
 bool backward_mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD; }
 
 hipError_t launch_backward_walk_y(const BackwardArgs& a) {
-    return walk<true, true, true, false, false, 0>(a, a.p.q, a.p.k, a.p.v, a.p.states, a.y,
-                                                   nullptr, nullptr);
+    // Y in bf16 (the forward rounds it to bf16 before its norm as well)
+    return walk<true, true, true, false, false, 2>(a, a.p.q, a.p.k, a.p.v, a.p.states, nullptr,
+                                                   nullptr, a.y);
 }
 
 hipError_t launch_backward_walks_grad(const BackwardArgs& a) {

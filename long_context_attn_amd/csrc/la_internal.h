@@ -142,8 +142,9 @@ struct BackwardArgs {
     void *dq, *dk, *dv, *dg;  // [T][H][D] outputs
     float* dw;                // [H*D] gradient w.r.t. the norm weight
     float* d_init;            // [nseq][H][D][D] gradient w.r.t. the initial states, or null
-    // workspace: y [T][H][D] fp32; dy [T][H][D] (fp32, bf16 on the MFMA
-    // path); q~, k~, v~ [T][H][D] fp32 (portable path only); reverse chunk
+    // workspace: y [T][H][D] and dy [T][H][D] (fp32; bf16 on the MFMA path,
+    // where y is read through a cast); q~, k~, v~ [T][H][D] fp32 (portable
+    // path only); reverse chunk
     // sums / G_exit [max_chunks][H][D][D]; dw partial sums
     // [n_tb + backward_dw_slices()][H*D]
     float *qs, *ks, *vs, *y, *gstates, *dw_part;

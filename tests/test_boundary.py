@@ -198,21 +198,21 @@ def test_state_validation(lib):
 
 
 def test_backward_workspace_size(lib):
-    # plan + two states per chunk + y (fp32) and dy + dw partial sums per 8 tokens
+    # plan + two states per chunk + y and dy + dw partial sums per 8 tokens
     # (plus 32 rows of the second reduction level);
-    # bf16 at head_dim 128 (MFMA walks): dy in bf16 and no other copies;
-    # otherwise dy and q~, k~, v~ in fp32
+    # bf16 at head_dim 128 (MFMA walks): y and dy in bf16 and no other copies;
+    # otherwise y, dy and q~, k~, v~ in fp32
     T, H, D = 8192, 64, 128
     act = T * H * D * 4
     states = 2 * (T // 256 + 1) * H * D * D * 4
     parts = (T // 8 + 32) * H * D * 4
-    need = act + act // 2 + states + parts
+    need = act + states + parts
     assert need <= ops.backward_workspace_size(T, 1, H, D, 64, 256) < need + 65536
     need = 5 * act + states + parts
     ws = ops.backward_workspace_size(T, 1, H, D, 64, 256, dtype=torch.float32)
     assert need <= ws < need + 65536
     # automatic chunks: 2048 tokens on the MFMA path (about one walk per CU)
-    need = act + act // 2 + 2 * (T // 2048 + 1) * H * D * D * 4 + parts
+    need = act + 2 * (T // 2048 + 1) * H * D * D * 4 + parts
     assert need <= ops.backward_workspace_size(T, 1, H, D, 64, 0) < need + 65536
     assert ops.backward_workspace_size(T, 1, H, 96, 64, 0) == 0
     assert ops.backward_workspace_size(T, 1, 257, D, 64, 0) == 0  # heads * head_dim > 32768
