@@ -284,7 +284,7 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
             const float msc = mrun * sl2;
             // Block b + 1's scores on the matrix cores with block b's
             // exponentials in between: step s issues the two products of
-            // features 16 s .. 16 s + 15 (K operands read one step ahead) and
+            // features 16 s .. 16 s + 15 (K operands read two steps ahead) and
             // four of the 32 exponentials; every two steps complete eight, and
             // they become one P^T operand (accumulator registers r0 .. r0 + 7
             // of tile m hold keys 16 t + 8 (j / 4) + 4 g + j % 4; one swap
@@ -294,20 +294,22 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
             const __bf16* sK = L.k[1 - P];
             Sn[0] = f32x16{};
             Sn[1] = f32x16{};
-            bf16x8 ka[2][2];
+            bf16x8 ka[3][2];  // K operands, read two steps ahead
             ka[0][0] = ld_row_operand(sK, l32, 8 * g);
             ka[0][1] = ld_row_operand(sK, 32 + l32, 8 * g);
+            ka[1][0] = ld_row_operand(sK, l32, 16 + 8 * g);
+            ka[1][1] = ld_row_operand(sK, 32 + l32, 16 + 8 * g);
             float ps = 0.f;
             float pv[8];
             bf16x8 pb[MB / 16];
 #pragma unroll
             for (int st = 0; st < MD / 16; ++st) {
-                if (st + 1 < MD / 16) {
-                    ka[(st + 1) & 1][0] = ld_row_operand(sK, l32, 16 * (st + 1) + 8 * g);
-                    ka[(st + 1) & 1][1] = ld_row_operand(sK, 32 + l32, 16 * (st + 1) + 8 * g);
+                if (st + 2 < MD / 16) {
+                    ka[(st + 2) % 3][0] = ld_row_operand(sK, l32, 16 * (st + 2) + 8 * g);
+                    ka[(st + 2) % 3][1] = ld_row_operand(sK, 32 + l32, 16 * (st + 2) + 8 * g);
                 }
-                Sn[0] = mfma32(ka[st & 1][0], qb[st], Sn[0]);
-                Sn[1] = mfma32(ka[st & 1][1], qb[st], Sn[1]);
+                Sn[0] = mfma32(ka[st % 3][0], qb[st], Sn[0]);
+                Sn[1] = mfma32(ka[st % 3][1], qb[st], Sn[1]);
                 const int t = st >> 1, m = t >> 1, r0 = 8 * (t & 1) + 4 * (st & 1);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -325,16 +327,20 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
             lsum += ps;
-            // O^T += V^T P^T, V operands read one product ahead
+            // O^T += V^T P^T, V operands read three products ahead (LDS latency
+            // is what the products wait on here)
             const __bf16* sV = L.v[P];
-            bf16x8 va[2];
-            va[0] = ld_tr_operand(sV, 0, 0, lane);
+            constexpr int VA = 4, NPV = (MB / 16) * (MD / 32);
+            bf16x8 va[VA];
 #pragma unroll
-            for (int i = 0; i < (MB / 16) * (MD / 32); ++i) {
+            for (int i = 0; i < VA - 1; ++i) va[i] = ld_tr_operand(sV, 16 * (i >> 2), 32 * (i & 3), lane);
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
                 const int t = i >> 2, n = i & 3;
-                if (i + 1 < (MB / 16) * (MD / 32))
-                    va[(i + 1) & 1] = ld_tr_operand(sV, 16 * ((i + 1) >> 2), 32 * ((i + 1) & 3), lane);
-                O[n] = mfma32(va[i & 1], pb[t], O[n]);
+                if (i + VA - 1 < NPV)
+                    va[(i + VA - 1) % VA] =
+                        ld_tr_operand(sV, 16 * ((i + VA - 1) >> 2), 32 * ((i + VA - 1) & 3), lane);
+                O[n] = mfma32(va[i % VA], pb[t], O[n]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
