@@ -115,7 +115,12 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(
 }
 
 // --------------------------------------------------------- attention
-constexpr int FA_THREADS = 256;  // four waves, 32 queries each
+// One 32-query sub-tile per wave, four waves: two waves share each SIMD and
+// overlap one's MFMA work with the other's VALU work.  Two sub-tiles per wave
+// (half the LDS reads per FLOP, one wave per SIMD) measured 2300 against
+// 1234 us at 8192 x 64 heads.
+constexpr int FA_QT = 1;  // 32-query sub-tiles per wave
+constexpr int FA_NW = 4;  // waves per workgroup
 
 struct FaLds {
     __bf16 k[2][TILE];
@@ -135,11 +140,17 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
+// QT: 32-query sub-tiles per wave; NW: waves per workgroup (QT * NW * 32 =
+// 128 queries per tile).  Each K or V operand read from LDS feeds QT
+// products, so QT = 2 halves the LDS reads per FLOP, at twice the registers
+// (one wave per SIMD instead of two).
+template <int QT, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void softmax_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ out, const PlanHeader* __restrict__ hdr,
     const SegEntry* __restrict__ segs, const ChunkEntry* __restrict__ tiles, int H, float sl2,
     int rope_dim, const RopeTheta th) {
+    static_assert(QT * NW * 32 == SOFTMAX_TILE, "a workgroup covers one query tile");
     __shared__ __attribute__((aligned(16))) FaLds L;
     const int ntile = hdr->n_chunks;
     // Workgroups are dealt to the eight XCDs in turn; when the heads divide
@@ -166,20 +177,24 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
     const int64_t qend = qstart + qlen;
     const int nkb = (int)((qend - s0 + MB - 1) / MB);
 
-    // this wave's queries: Q^T operands, lane = query l32, features 16 s + 8 g .. + 7
-    const int64_t q0w = qstart + 32 * w;
-    const int qrows = max(0, min(32, qlen - 32 * w));
-    bf16x8 qb[MD / 16];
-    {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q + q0w * HD + (int64_t)h * MD, qrows, HD);
+    // this wave's queries: sub-tile qt holds queries q0w + 32 qt + l32; Q^T
+    // operands with features 16 s + 8 g .. + 7
+    const int64_t q0w = qstart + 32 * QT * w;
+    const int qrows = max(0, min(32 * QT, qlen - 32 * QT * w));
+    bf16x8 qb[QT][MD / 16];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int rows = max(0, min(32, qrows - 32 * qt));
+        const __amdgpu_buffer_rsrc_t rs =
+            tile_rsrc(q + (q0w + 32 * qt) * HD + (int64_t)h * MD, rows, HD);
         const int voff = (l32 * HD + 8 * g) * 2;
 #pragma unroll
         for (int s = 0; s < MD / 16; ++s)
-            qb[s] = __builtin_bit_cast(bf16x8,
-                                       __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * s, 0));
+            qb[qt][s] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * s, 0));
         // rotate the first rope_dim features at the query's position (as
         // rope_kernel does for K)
-        const int64_t pos = q0w + l32 - s0;
+        const int64_t pos = q0w + 32 * qt + l32 - s0;
 #pragma unroll
         for (int s = 0; s < MD / 16; ++s) {
             const int f0 = 16 * s + 8 * g;
@@ -187,32 +202,33 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float2 r = rope_cs(pos, th.t[f0 / 2 + u]);
-                    const float a = (float)qb[s][2 * u], b = (float)qb[s][2 * u + 1];
-                    qb[s][2 * u] = (__bf16)(a * r.x - b * r.y);
-                    qb[s][2 * u + 1] = (__bf16)(a * r.y + b * r.x);
+                    const float a = (float)qb[qt][s][2 * u], b = (float)qb[qt][s][2 * u + 1];
+                    qb[qt][s][2 * u] = (__bf16)(a * r.x - b * r.y);
+                    qb[qt][s][2 * u + 1] = (__bf16)(a * r.y + b * r.x);
                 }
             }
         }
     }
 
     // K / V tiles go from HBM straight into LDS (buffer loads with the LDS
-    // as destination, no registers): wave w stages rows 16 w .. 16 w + 15 of
-    // a 64-key tile with four 1 KiB loads, lane l of each filling physical
-    // 16-byte chunk l % 16 of row 4 i + l / 16 with the logical chunk that the
-    // swizzle puts there.  Rows past a ragged end repeat the last key: their
-    // scores are always masked, so they only need to be finite.
+    // as destination, no registers): wave w stages rows 64 / NW * w .. of a
+    // 64-key tile with 1 KiB loads, lane l of each filling physical 16-byte
+    // chunk l % 16 of row 4 i + l / 16 with the logical chunk that the swizzle
+    // puts there.  Rows past a ragged end repeat the last key: their scores
+    // are always masked, so they only need to be finite.
     // K runs one block ahead of V: while the exponentials of block b run on
     // the VALU, the scores of block b + 1 run on the matrix cores.  In
     // iteration b the LDS holds K(b + 1) and V(b), and the loads of K(b + 2)
     // and V(b + 1) fill the buffers that K(b) and V(b - 1) left before the
     // last barrier; each wave waits for its own loads before the next barrier.
+    constexpr int RPW = MB / NW;  // rows staged per wave
     auto stage = [&](const __bf16* base, int b, __bf16* dst) {
         const int64_t kb0 = s0 + (int64_t)b * MB;
         const int n = (int)min((int64_t)MB, qend - kb0);
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base + kb0 * HD + (int64_t)h * MD, n, HD);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row0 = 16 * w + 4 * i;
+        for (int i = 0; i < RPW / 4; ++i) {
+            const int row0 = RPW * w + 4 * i;
             const int row = row0 + (lane >> 4);
             const int f = ((row & 3) << 2) | ((row >> 2) & 3);
             const int vo = (min(row, n - 1) * HD + 8 * ((lane & 15) ^ f)) * 2;
@@ -230,103 +246,131 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
     loads_done();
     __syncthreads();
 
-    f32x16 O[MD / 32] = {};
-    float mrun = -INFINITY, lsum = 0.f;  // running maximum (raw score units) and sum
+    f32x16 O[QT][MD / 32] = {};
+    float mrun[QT], lsum[QT];  // running maximum (raw score units) and sum
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        mrun[qt] = -INFINITY;
+        lsum[qt] = 0.f;
+    }
     // The running maximum only moves when a score exceeds it by more than
     // 8 / sl2, so that probabilities stay below 2^8 and the rescale of the
     // output is rare.
     const float tau = 8.f / sl2;
-    const int64_t qabs = q0w + l32;  // this lane's query
-    auto scores = [&](const __bf16* sK, f32x16 (&S)[2]) {
-        S[0] = f32x16{};
-        S[1] = f32x16{};
+    auto scores = [&](const __bf16* sK, f32x16 (&S)[QT][2]) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) S[qt][0] = S[qt][1] = f32x16{};
 #pragma unroll
         for (int s = 0; s < MD / 16; ++s)
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                S[m] = mfma32(ld_row_operand(sK, 32 * m + l32, 16 * s + 8 * g), qb[s], S[m]);
+            for (int m = 0; m < 2; ++m) {
+                const bf16x8 ko = ld_row_operand(sK, 32 * m + l32, 16 * s + 8 * g);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) S[qt][m] = mfma32(ko, qb[qt][s], S[qt][m]);
+            }
     };
-    f32x16 Sa[2], Sb[2];
+    f32x16 Sa[QT][2], Sb[QT][2];
     if (last_w >= 0) scores(L.k[0], Sa);
+    // iteration 0 loads K(2) into the buffer these scores read: every wave
+    // must be done with it first
+    __syncthreads();
     // iteration b (P = b % 2): softmax and O += P V for block b (scores in
     // Sc), scores of block b + 1 into Sn
-    auto step = [&](auto par, int b, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+    auto step = [&](auto par, int b, f32x16 (&Sc)[QT][2], f32x16 (&Sn)[QT][2]) {
         constexpr int P = decltype(par)::value;
         if (b + 2 < nkb) stage(k, b + 2, L.k[P]);
         if (b + 1 < nkb) stage(v, b + 1, L.v[1 - P]);
         if (b <= last_w) {
             const int64_t kb0 = s0 + (int64_t)b * MB;
-            if (kb0 + MB - 1 > q0w) {  // the block reaches the diagonal: mask keys after the query
-                const int qrel = (int)min((int64_t)MB, qabs - kb0);
+            float msc[QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                const int64_t qabs = q0w + 32 * qt + l32;  // this lane's query
+                if (kb0 + MB - 1 > q0w + 32 * qt) {  // reaches the diagonal: mask keys after the query
+                    const int qrel = (int)max((int64_t)-1, min((int64_t)MB, qabs - kb0));
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (32 * m + 8 * (r >> 2) + 4 * g + (r & 3) > qrel)
+                                Sc[qt][m][r] = -INFINITY;
+                }
+                float bm = -INFINITY;
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * m + 8 * (r >> 2) + 4 * g + (r & 3) > qrel) Sc[m][r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, Sc[qt][m][r]);
+                bm = pair_max(bm);
+                const bool up = bm > mrun[qt] + tau;
+                if (__builtin_amdgcn_ballot_w64(up) != 0) {
+                    const float mnew = up ? bm : mrun[qt];
+                    const float alpha = __builtin_amdgcn_exp2f((mrun[qt] - mnew) * sl2);
+                    mrun[qt] = mnew;
+                    lsum[qt] *= alpha;
+#pragma unroll
+                    for (int n = 0; n < MD / 32; ++n)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) O[qt][n][r] *= alpha;
+                }
+                msc[qt] = mrun[qt] * sl2;
             }
-            float bm = -INFINITY;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, Sc[m][r]);
-            bm = pair_max(bm);
-            const bool up = bm > mrun + tau;
-            if (__builtin_amdgcn_ballot_w64(up) != 0) {
-                const float mnew = up ? bm : mrun;
-                const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);
-                mrun = mnew;
-                lsum *= alpha;
-#pragma unroll
-                for (int n = 0; n < MD / 32; ++n)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) O[n][r] *= alpha;
-            }
-            const float msc = mrun * sl2;
             // Block b + 1's scores on the matrix cores with block b's
-            // exponentials in between: step s issues the two products of
-            // features 16 s .. 16 s + 15 (K operands read two steps ahead) and
-            // four of the 32 exponentials; every two steps complete eight, and
-            // they become one P^T operand (accumulator registers r0 .. r0 + 7
-            // of tile m hold keys 16 t + 8 (j / 4) + 4 g + j % 4; one swap
-            // between the lane halves makes them keys 16 t + 8 g + j).  The
-            // fences keep this order.  A wave past its last block computes
-            // scores from whatever the buffer holds and never uses them.
+            // exponentials in between: step st issues the products of
+            // features 16 st .. 16 st + 15 (K operands read two steps ahead)
+            // and four of each sub-tile's 32 exponentials; every two steps
+            // complete eight per sub-tile, and they become one P^T operand
+            // (accumulator registers r0 .. r0 + 7 of tile m hold keys
+            // 16 t + 8 (j / 4) + 4 g + j % 4; one swap between the lane
+            // halves makes them keys 16 t + 8 g + j).  The fences keep this
+            // order.  A wave past its last block computes scores from
+            // whatever the buffer holds and never uses them.
             const __bf16* sK = L.k[1 - P];
-            Sn[0] = f32x16{};
-            Sn[1] = f32x16{};
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) Sn[qt][0] = Sn[qt][1] = f32x16{};
             bf16x8 ka[3][2];  // K operands, read two steps ahead
             ka[0][0] = ld_row_operand(sK, l32, 8 * g);
             ka[0][1] = ld_row_operand(sK, 32 + l32, 8 * g);
             ka[1][0] = ld_row_operand(sK, l32, 16 + 8 * g);
             ka[1][1] = ld_row_operand(sK, 32 + l32, 16 + 8 * g);
-            float ps = 0.f;
-            float pv[8];
-            bf16x8 pb[MB / 16];
+            float ps[QT], pv8[QT][8];
+            bf16x8 pb[QT][MB / 16];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) ps[qt] = 0.f;
 #pragma unroll
             for (int st = 0; st < MD / 16; ++st) {
                 if (st + 2 < MD / 16) {
                     ka[(st + 2) % 3][0] = ld_row_operand(sK, l32, 16 * (st + 2) + 8 * g);
                     ka[(st + 2) % 3][1] = ld_row_operand(sK, 32 + l32, 16 * (st + 2) + 8 * g);
                 }
-                Sn[0] = mfma32(ka[st % 3][0], qb[st], Sn[0]);
-                Sn[1] = mfma32(ka[st % 3][1], qb[st], Sn[1]);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    Sn[qt][0] = mfma32(ka[st % 3][0], qb[qt][st], Sn[qt][0]);
+                    Sn[qt][1] = mfma32(ka[st % 3][1], qb[qt][st], Sn[qt][1]);
+                }
                 const int t = st >> 1, m = t >> 1, r0 = 8 * (t & 1) + 4 * (st & 1);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[m][r0 + u], sl2, -msc));
-                    pv[4 * (st & 1) + u] = e;
-                    ps += e;
-                }
-                if (st & 1) {
-                    const unsigned p0 = pack_bf16(pv[0], pv[1]), p1 = pack_bf16(pv[2], pv[3]);
-                    const unsigned p2 = pack_bf16(pv[4], pv[5]), p3 = pack_bf16(pv[6], pv[7]);
-                    const auto x02 = __builtin_amdgcn_permlane32_swap(p0, p2, false, false);
-                    const auto x13 = __builtin_amdgcn_permlane32_swap(p1, p3, false, false);
-                    pb[t] = __builtin_bit_cast(bf16x8, u32x4{x02[0], x13[0], x02[1], x13[1]});
+                for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float e =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[qt][m][r0 + u], sl2, -msc[qt]));
+                        pv8[qt][4 * (st & 1) + u] = e;
+                        ps[qt] += e;
+                    }
+                    if (st & 1) {
+                        const unsigned p0 = pack_bf16(pv8[qt][0], pv8[qt][1]);
+                        const unsigned p1 = pack_bf16(pv8[qt][2], pv8[qt][3]);
+                        const unsigned p2 = pack_bf16(pv8[qt][4], pv8[qt][5]);
+                        const unsigned p3 = pack_bf16(pv8[qt][6], pv8[qt][7]);
+                        const auto x02 = __builtin_amdgcn_permlane32_swap(p0, p2, false, false);
+                        const auto x13 = __builtin_amdgcn_permlane32_swap(p1, p3, false, false);
+                        pb[qt][t] = __builtin_bit_cast(bf16x8, u32x4{x02[0], x13[0], x02[1], x13[1]});
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            lsum += ps;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) lsum[qt] += ps[qt];
             // O^T += V^T P^T, V operands read three products ahead (LDS latency
             // is what the products wait on here)
             const __bf16* sV = L.v[P];
@@ -340,7 +384,8 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
                 if (i + VA - 1 < NPV)
                     va[(i + VA - 1) % VA] =
                         ld_tr_operand(sV, 16 * ((i + VA - 1) >> 2), 32 * ((i + VA - 1) & 3), lane);
-                O[n] = mfma32(va[i % VA], pb[t], O[n]);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) O[qt][n] = mfma32(va[i % VA], pb[qt][t], O[qt][n]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -352,20 +397,27 @@ __global__ __launch_bounds__(FA_THREADS, 2) void softmax_fwd_kernel(
         if (b + 1 < nkb) step(std::integral_constant<int, 1>{}, b + 1, Sb, Sa);
     }
 
-    // out = O / sum, lane = query l32, features 32 n + 8 jj + 4 g .. + 3
-    if (qrows > 0) {
-        const float inv = 1.f / pair_sum(lsum);
-        const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + q0w * HD + (int64_t)h * MD, qrows, HD);
-        const int ovoff = (l32 * HD + 4 * g) * 2;
+    // out = O / sum, lane = query l32 of each sub-tile, features 32 n + 8 jj + 4 g .. + 3
 #pragma unroll
-        for (int n = 0; n < MD / 32; ++n)
+    for (int qt = 0; qt < QT; ++qt) {
+        const int rows = max(0, min(32, qrows - 32 * qt));
+        if (rows > 0) {
+            const float inv = 1.f / pair_sum(lsum[qt]);
+            const __amdgpu_buffer_rsrc_t ro =
+                tile_rsrc(out + (q0w + 32 * qt) * HD + (int64_t)h * MD, rows, HD);
+            const int ovoff = (l32 * HD + 4 * g) * 2;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const unsigned lo = pack_bf16(O[n][4 * jj + 0] * inv, O[n][4 * jj + 1] * inv);
-                const unsigned hi = pack_bf16(O[n][4 * jj + 2] * inv, O[n][4 * jj + 3] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, ovoff,
-                                                      (32 * n + 8 * jj) * 2, 0);
-            }
+            for (int n = 0; n < MD / 32; ++n)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const unsigned lo =
+                        pack_bf16(O[qt][n][4 * jj + 0] * inv, O[qt][n][4 * jj + 1] * inv);
+                    const unsigned hi =
+                        pack_bf16(O[qt][n][4 * jj + 2] * inv, O[qt][n][4 * jj + 3] * inv);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, ovoff,
+                                                          (32 * n + 8 * jj) * 2, 0);
+                }
+        }
     }
 }
 
@@ -558,7 +610,8 @@ hipError_t launch_softmax_fwd(const SoftmaxArgs& a, hipStream_t st) {
     if (a.max_tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_tiles * a.H));
     const __bf16* kk = a.rope_dim > 0 ? a.kr : (const __bf16*)a.k;
-    hipLaunchKernelGGL(softmax_fwd_kernel, grid, dim3(FA_THREADS), 0, st, (const __bf16*)a.q, kk,
+    hipLaunchKernelGGL((softmax_fwd_kernel<FA_QT, FA_NW>), grid, dim3(64 * FA_NW), 0, st,
+                       (const __bf16*)a.q, kk,
                        (const __bf16*)a.v, (__bf16*)a.out, a.hdr, a.segs, a.tiles, a.H,
                        a.scale * 1.4426950408889634f, a.rope_dim, rope_theta(a));
     return hipGetLastError();
