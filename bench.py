@@ -256,10 +256,10 @@ def bench_backward(args, la, torch, inputs):
     ws = torch.empty(la.backward_workspace_size(B * N, B, H, D, cfg["block"], 0), dtype=torch.uint8,
                      device="cuda")
     call = lambda: la.backward(*x, wd, dout, block=cfg["block"], eps=cfg["eps"], workspace=ws)
-    for _ in range(3):
+    for _ in range(20):
         call()
     torch.cuda.synchronize()
-    n = 10
+    n = 30
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()

@@ -183,21 +183,7 @@ __global__ __launch_bounds__(D) void lin_walk_kernel(
     }
 }
 
-// 8 consecutive elements as fp32, and back
-__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        o[i] = a[i];
-        o[4 + i] = b[i];
-    }
-}
-__device__ __forceinline__ void load8(const __bf16* p, float (&o)[8]) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
-}
+// 8 consecutive fp32 values stored as fp32 or bf16
 __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
@@ -209,46 +195,87 @@ __device__ __forceinline__ void store8(__bf16* p, const float (&x)[8]) {
     *reinterpret_cast<bf16x8*>(p) = v;
 }
 
+// 8 consecutive elements kept in their storage type (bf16 pieces take half
+// the registers of fp32 ones), widened to fp32 where they are used
+template <class T>
+struct Piece;
+template <>
+struct Piece<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+    // taken as rewritten: values widened from it before this point are not reused after it
+    __device__ __forceinline__ void fence() { asm volatile("" : "+v"(a), "+v"(b)); }
+};
+template <>
+struct Piece<__bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
+    __device__ __forceinline__ void fence() {
+        f32x4 x = __builtin_bit_cast(f32x4, v);
+        asm volatile("" : "+v"(x));
+        v = __builtin_bit_cast(bf16x8, x);
+    }
+};
+
 // Norm backward: one workgroup per NB_TOKENS consecutive tokens.  Thread t
 // holds the 8-element pieces t, t + 256, ... (CPT of them) of a token's H*D
-// values in registers: one pass loads y, gate and dout, two block
-// reductions give r and <a, yhat>, and the same registers give dy (DYT:
-// fp32, or bf16 as an MFMA operand) and dgate.  dw is accumulated over the
-// workgroup's tokens and written as one partial sum row.
+// values in registers, in their storage type: one pass loads y, gate and
+// dout, two block reductions give r and <a, yhat>, and the same registers
+// give dy (DYT: fp32, or bf16 as an MFMA operand) and dgate (the gate's
+// sigmoid is evaluated in both passes rather than kept, which keeps enough
+// workgroups resident to have several tokens' loads in flight per CU).  dw
+// is accumulated in LDS over the workgroup's tokens (each thread its own
+// entries) and written as one partial sum row.
 template <class TT, class DYT, class YT, int CPT>
 __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
     const YT* __restrict__ y, const TT* __restrict__ g, const TT* __restrict__ w,
     const TT* __restrict__ dout, DYT* __restrict__ dy, TT* __restrict__ dg,
     float* __restrict__ dw_part, int64_t T, int HD, float eps) {
     __shared__ float red[2][EW_THREADS / 64];
+    // this thread's dw sums, one column per thread (conflict-free)
+    __shared__ float dwp[CPT][8][EW_THREADS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nch = HD >> 3;
     const int64_t t_begin = (int64_t)blockIdx.x * NB_TOKENS;
     const int64_t t_end = min(T, t_begin + NB_TOKENS);
-    float wt[CPT][8], dwp[CPT][8];
+    Piece<TT> wt[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int ch = tid + EW_THREADS * c;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dwp[c][i] = 0.f;
-        if (ch < nch) load8(w + 8 * ch, wt[c]);
+        for (int i = 0; i < 8; ++i) dwp[c][i][tid] = 0.f;
+        if (ch < nch) wt[c].load(w + 8 * ch);
     }
     for (int64_t t = t_begin; t < t_end; ++t) {
         const int64_t base = t * HD;
-        float yv[CPT][8], sg[CPT][8], go[CPT][8];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) wt[c].fence();  // widened per token, not held
+        Piece<YT> yv[CPT];
+        Piece<TT> gr[CPT], go[CPT];
         float ss = 0.f, ay = 0.f;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int ch = tid + EW_THREADS * c;
             if (ch < nch) {
-                load8(y + base + 8 * ch, yv[c]);
-                load8(g + base + 8 * ch, sg[c]);
-                load8(dout + base + 8 * ch, go[c]);
+                yv[c].load(y + base + 8 * ch);
+                gr[c].load(g + base + 8 * ch);
+                go[c].load(dout + base + 8 * ch);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int ch = tid + EW_THREADS * c;
+            if (ch < nch) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    sg[c][i] = sigmoid_f(sg[c][i]);
-                    ss += yv[c][i] * yv[c][i];
-                    ay += go[c][i] * wt[c][i] * sg[c][i] * yv[c][i];
+                    const float yy = yv[c][i];
+                    ss += yy * yy;
+                    ay += go[c][i] * wt[c][i] * sigmoid_f(gr[c][i]) * yy;
                 }
             }
         }
@@ -273,15 +300,24 @@ __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
         const float m = ay * r / (float)HD;  // <a, yhat> / HD
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
+            yv[c].fence();
+            gr[c].fence();
+            go[c].fence();
+            wt[c].fence();
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
             const int ch = tid + EW_THREADS * c;
             if (ch < nch) {
                 float d1[8], d2[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
+                    const float sg = sigmoid_f(gr[c][i]);
                     const float yh = yv[c][i] * r;
-                    d1[i] = r * (go[c][i] * wt[c][i] * sg[c][i] - yh * m);
-                    d2[i] = go[c][i] * yh * wt[c][i] * sg[c][i] * (1.0f - sg[c][i]);
-                    dwp[c][i] += go[c][i] * yh * sg[c][i];
+                    const float gw = go[c][i] * wt[c][i] * sg;
+                    d1[i] = r * (gw - yh * m);
+                    d2[i] = gw * yh * (1.0f - sg);
+                    dwp[c][i][tid] += go[c][i] * yh * sg;
                 }
                 store8(dy + base + 8 * ch, d1);
                 store8(dg + base + 8 * ch, d2);
@@ -292,7 +328,12 @@ __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int ch = tid + EW_THREADS * c;
-        if (ch < nch) store8(part + 8 * ch, dwp[c]);
+        if (ch < nch) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = dwp[c][i][tid];
+            store8(part + 8 * ch, x);
+        }
     }
 }
 
