@@ -167,7 +167,8 @@ bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block
     if (chunk < block || chunk % block != 0) return false;
     const int64_t maxc = total / chunk + nseq;
     if (maxc * heads > (int64_t)0x7fffffff) return false;
-    const int64_t ntb = (total + la::backward_norm_tokens() - 1) / la::backward_norm_tokens();
+    const int64_t tpb = la::backward_norm_tokens(total);
+    const int64_t ntb = (total + tpb - 1) / tpb;
     if (ntb > (int64_t)0x7fffffff) return false;
     L->chunk = chunk;
     L->max_chunks = (int)maxc;

@@ -29,7 +29,8 @@ namespace la {
 namespace {
 
 constexpr int EW_THREADS = 256;  // elementwise and norm kernels
-constexpr int NB_TOKENS = 8;     // tokens per workgroup of the norm backward
+constexpr int NB_TOKENS = 8;     // tokens per workgroup of the norm backward, at least
+constexpr int64_t NB_GROUPS = 2048;  // norm backward workgroups (dw partial rows), at most
 
 __device__ __forceinline__ float silu_grad_f(float x) {
     const float s = sigmoid_f(x);
@@ -222,7 +223,7 @@ struct Piece<__bf16> {
     }
 };
 
-// Norm backward: one workgroup per NB_TOKENS consecutive tokens.  Thread t
+// Norm backward: one workgroup per tpb consecutive tokens.  Thread t
 // holds the 8-element pieces t, t + 256, ... (CPT of them) of a token's H*D
 // values in registers, in their storage type: one pass loads y, gate and
 // dout, two block reductions give r and <a, yhat>, and the same registers
@@ -235,14 +236,14 @@ template <class TT, class DYT, class YT, int CPT>
 __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
     const YT* __restrict__ y, const TT* __restrict__ g, const TT* __restrict__ w,
     const TT* __restrict__ dout, DYT* __restrict__ dy, TT* __restrict__ dg,
-    float* __restrict__ dw_part, int64_t T, int HD, float eps) {
+    float* __restrict__ dw_part, int64_t T, int64_t tpb, int HD, float eps) {
     __shared__ float red[2][EW_THREADS / 64];
     // this thread's dw sums, one column per thread (conflict-free)
     __shared__ float dwp[CPT][8][EW_THREADS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nch = HD >> 3;
-    const int64_t t_begin = (int64_t)blockIdx.x * NB_TOKENS;
-    const int64_t t_end = min(T, t_begin + NB_TOKENS);
+    const int64_t t_begin = (int64_t)blockIdx.x * tpb;
+    const int64_t t_end = min(T, t_begin + tpb);
     Piece<TT> wt[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -413,7 +414,7 @@ hipError_t norm_backward(const BackwardArgs& a, DYT* dy) {
     hipLaunchKernelGGL((norm_backward_kernel<TT, DYT, YT, C>), grid, block, 0, a.stream,        \
                        (const YT*)a.y,                                                          \
                        (const TT*)p.g, (const TT*)p.w, (const TT*)a.dout, dy, (TT*)a.dg,        \
-                       a.dw_part, p.total, HD, p.eps)
+                       a.dw_part, p.total, backward_norm_tokens(p.total), HD, p.eps)
     if (per <= 1) LA_NB(1);
     else if (per <= 2) LA_NB(2);
     else if (per <= 4) LA_NB(4);
@@ -513,7 +514,10 @@ hipError_t backward_t(const BackwardArgs& a) {
 
 }  // namespace
 
-int backward_norm_tokens() { return NB_TOKENS; }
+int64_t backward_norm_tokens(int64_t total) {
+    const int64_t t = (total + NB_GROUPS - 1) / NB_GROUPS;
+    return t > NB_TOKENS ? t : (int64_t)NB_TOKENS;
+}
 int backward_dw_slices() { return DW_SLICES; }
 int backward_max_hd() { return 16 * 8 * EW_THREADS; }
 

@@ -152,7 +152,7 @@ struct BackwardArgs {
     int n_tb;
     bool mfma;
 };
-int backward_norm_tokens();   // tokens per dw partial sum row
+int64_t backward_norm_tokens(int64_t total);  // tokens per dw partial sum row
 int backward_dw_slices();     // extra dw rows for the second reduction level
 int backward_max_hd();        // largest heads * head_dim of the norm backward
 hipError_t launch_backward(const BackwardArgs& a);

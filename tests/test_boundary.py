@@ -198,8 +198,8 @@ def test_state_validation(lib):
 
 
 def test_backward_workspace_size(lib):
-    # plan + two states per chunk + y and dy + dw partial sums per 8 tokens
-    # (plus 32 rows of the second reduction level);
+    # plan + two states per chunk + y and dy + dw partial sums per 8 tokens,
+    # at most 2048 rows (plus 32 rows of the second reduction level);
     # bf16 at head_dim 128 (MFMA walks): y and dy in bf16 and no other copies;
     # otherwise y, dy and q~, k~, v~ in fp32
     T, H, D = 8192, 64, 128
@@ -219,6 +219,11 @@ def test_backward_workspace_size(lib):
     assert ops.backward_workspace_size(T, 1, H, D, 64, 100) == 0
     assert ops.backward_workspace_size(T, 1, H, D, 64, -1) == 0
     assert ops.backward_workspace_size(0, 0, H, D, 64, 0) > 0
+    # 1M tokens: the dw partial rows stop at 2048 (512 tokens each)
+    T = 1 << 20
+    act = T * H * D * 4
+    need = act + 2 * (T // 8192 + 1) * H * D * D * 4 + (2048 + 32) * H * D * 4
+    assert need <= ops.backward_workspace_size(T, 1, H, D, 64, 8192) < need + 65536
 
 
 def test_backward_validation(lib):

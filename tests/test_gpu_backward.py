@@ -80,6 +80,17 @@ def test_backward_bf16(D, block, dist):
         compare(grads, ref, torch.bfloat16, "bf16 D=%d %s chunk=%d" % (D, dist, chunk))
 
 
+def test_backward_long_norm_groups():
+    """More than 2048 x 8 tokens: the norm backward's workgroups take 11 tokens
+    each (1910 of them, the last with one token), so each dweight partial row
+    sums 11 tokens."""
+    B, N, H, D = 1, 21000, 2, 128
+    args, ref = batch_case(B, N, H, D, torch.bfloat16, "unit", 24)
+    say("backward bf16 21000 tokens x 2 heads")
+    grads = run_batch(args, B, N, H, D, torch.bfloat16, 64, 0)
+    compare(grads, ref, torch.bfloat16, "bf16 21000 tokens")
+
+
 def test_backward_without_states():
     B, N, H, D = 1, 200, 2, 64
     args, ref = batch_case(B, N, H, D, torch.float32, "unit", 23, with_states=False)
