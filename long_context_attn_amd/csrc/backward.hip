@@ -93,6 +93,8 @@ __global__ __launch_bounds__(D) void chunk_sum_kernel(const float* __restrict__ 
 
 // Reverse exclusive scan per (sequence, head): each chunk sum B_c is replaced
 // by G_exit(c) = dS_final + sum_{c' > c} B_c'; dS0 = dS_final + sum_c B_c.
+// Without d_init the first chunk's sum is not read (it may not have been
+// formed).
 constexpr int RSCAN_THREADS = 256;
 __global__ __launch_bounds__(RSCAN_THREADS) void reverse_scan_kernel(
     float* __restrict__ states, const SegEntry* __restrict__ segs, const float* d_final,
@@ -107,6 +109,10 @@ __global__ __launch_bounds__(RSCAN_THREADS) void reverse_scan_kernel(
     const SegEntry se = segs[s];
     for (int c = se.first + se.count - 1; c >= se.first; --c) {
         f32x4* p = reinterpret_cast<f32x4*>(states + ((int64_t)c * H + h) * DD + e);
+        if (c == se.first && d_init == nullptr) {
+            *p = run;
+            break;
+        }
         const f32x4 sum = *p;
         *p = run;
         run += sum;
@@ -441,7 +447,7 @@ hipError_t backward_mfma(const BackwardArgs& a) {
     const PrefillArgs& p = a.p;
     hipStream_t st = a.stream;
     const int HD = p.H * p.D;
-    hipError_t e = launch_chunk_sums_mfma(p, p.k, p.v, true, true, p.states, true, st);
+    hipError_t e = launch_chunk_sums_mfma(p, p.k, p.v, true, true, p.states, SumSkip::last, st);
     if (e != hipSuccess) return e;
     {
         PrefillArgs s = p;
@@ -452,7 +458,9 @@ hipError_t backward_mfma(const BackwardArgs& a) {
     if ((e = launch_backward_walk_y(a)) != hipSuccess) return e;
     if ((e = norm_backward<__bf16, __bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
     if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
-    if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, true, false, a.gstates, false, st)) != hipSuccess)
+    // each sequence's first chunk sum only feeds dS0
+    if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, true, false, a.gstates,
+                                    a.d_init ? SumSkip::none : SumSkip::first, st)) != hipSuccess)
         return e;
     if ((e = reverse_scan(a)) != hipSuccess) return e;
     return launch_backward_walks_grad(a);

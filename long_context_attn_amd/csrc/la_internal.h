@@ -120,8 +120,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
 bool state_mfma_supported(const PrefillArgs& a);
 hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
 // states[c][h] = sum over chunk c of f(x)^T g(y), f and g SiLU or the identity
+// chunks a chunk-sum launch leaves out: none, each sequence's last (a forward
+// scan never reads it) or each sequence's first (a reverse scan reads it only
+// for the gradient of the initial state)
+enum class SumSkip : int { none = 0, last = 1, first = 2 };
 hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_x,
-                                  bool silu_y, float* states, bool skip_last, hipStream_t st);
+                                  bool silu_y, float* states, SumSkip skip, hipStream_t st);
 // lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,
 // 32-column state slice) walks every sequence whole; needs heads * 4 <= cus
 // (all lanes resident at once).  The plan runs first with chunk = 64 and no

@@ -78,7 +78,7 @@ template <bool SA, bool SB>
 __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
-    const ChunkEntry* __restrict__ chunks, float* __restrict__ states, int H, bool skip_last,
+    const ChunkEntry* __restrict__ chunks, float* __restrict__ states, int H, SumSkip skip,
     const InlinePlan ip) {
     __shared__ __attribute__((aligned(16))) StateLds L;
     const int n_sum = (int)gridDim.x - ip.extra;
@@ -91,13 +91,14 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     if (ip.extra > 0) {
         if (c >= ip.nseq * ip.cps) return;
         ce = uniform_chunk(ip, c);
-        if (skip_last && c - ce.seg * ip.cps == ip.cps - 1) return;
+        const int i = c - ce.seg * ip.cps;
+        if ((skip == SumSkip::last && i == ip.cps - 1) || (skip == SumSkip::first && i == 0)) return;
     } else {
         if (c >= hdr->n_chunks) return;
         ce = chunks[c];
-        if (skip_last) {
+        if (skip != SumSkip::none) {
             const SegEntry se = segs[ce.seg];
-            if (c == se.first + se.count - 1) return;
+            if (c == (skip == SumSkip::last ? se.first + se.count - 1 : se.first)) return;
         }
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
 bool state_mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.block == MB; }
 
 hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_x,
-                                  bool silu_y, float* states, bool skip_last, hipStream_t st) {
+                                  bool silu_y, float* states, SumSkip skip, hipStream_t st) {
     if (a.max_chunks == 0) return hipSuccess;
     InlinePlan ip{};
     if (a.inline_plan) {
@@ -204,12 +205,13 @@ hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const voi
                       : (silu_y ? &chunk_state_mfma_kernel<false, true>
                                 : &chunk_state_mfma_kernel<false, false>);
     hipLaunchKernelGGL(fn, grid, dim3(ST_THREADS), 0, st, (const __bf16*)x, (const __bf16*)y,
-                       a.hdr, a.segs, a.chunks, states, a.H, skip_last, ip);
+                       a.hdr, a.segs, a.chunks, states, a.H, skip, ip);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st) {
-    return launch_chunk_sums_mfma(a, a.k, a.v, !a.preact, !a.preact, a.states, a.skip_last, st);
+    return launch_chunk_sums_mfma(a, a.k, a.v, !a.preact, !a.preact, a.states,
+                                  a.skip_last ? SumSkip::last : SumSkip::none, st);
 }
 
 }  // namespace la

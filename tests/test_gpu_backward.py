@@ -80,6 +80,27 @@ def test_backward_bf16(D, block, dist):
         compare(grads, ref, torch.bfloat16, "bf16 D=%d %s chunk=%d" % (D, dist, chunk))
 
 
+def test_backward_bf16_without_initial_gradient():
+    """No gradient w.r.t. the initial states requested: the MFMA path then
+    skips each sequence's first chunk sum of q~^T dy (it only feeds that
+    gradient); every other gradient must be unchanged."""
+    B, N, H, D = 2, 700, 4, 128
+    args, ref = batch_case(B, N, H, D, torch.bfloat16, "unit", 25)
+    q, k, v, g, w, dout, init, dfin = args
+    x = [dev(a, torch.bfloat16).view(B, N, H, D) for a in (q, k, v, g)]
+    gd = dev(dout, torch.bfloat16).view(B, N, H, D)
+    for chunk in (0, 128):
+        say("backward bf16 without d_initial_state, chunk", chunk)
+        dq, dk, dv, dg, dw, d_init = la.backward(
+            *x, dev(w, torch.bfloat16), gd, block=64, initial_state=torch.from_numpy(init).cuda(),
+            d_final_state=torch.from_numpy(dfin).cuda(), chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        assert d_init is None
+        T = B * N
+        compare(tuple(t.view(T, H, D) for t in (dq, dk, dv, dg)) + (dw, None), ref,
+                torch.bfloat16, "bf16 no d_init chunk=%d" % chunk)
+
+
 def test_backward_long_norm_groups():
     """More than 2048 x 8 tokens: the norm backward's workgroups take 11 tokens
     each (1910 of them, the last with one token), so each dweight partial row
