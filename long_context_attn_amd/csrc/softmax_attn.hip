@@ -41,7 +41,8 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ rope
 constexpr int ROPE_THREADS = 256;
-constexpr int ROPE_TOKENS = 16;  // tokens per workgroup
+constexpr int ROPE_TOKENS = 8;   // tokens per workgroup
+constexpr int ROPE_BATCH = 8;    // loads in flight per thread
 constexpr int ROPE_MAX_PAIRS = 64;
 
 // the rotation frequencies theta_p = base^(-2p / rope_dim), passed by value
@@ -95,22 +96,32 @@ __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(
     const int HD = H * MD;
     const int per_token = HD / 8;  // 16-byte pieces of one token
     const int64_t n = (int64_t)nt * per_token;
-    for (int64_t e = threadIdx.x; e < n; e += ROPE_THREADS) {
-        const int t = (int)(e / per_token);
-        const int piece = (int)(e - (int64_t)t * per_token);
-        const int f = (piece % (MD / 8)) * 8;  // first feature of the piece within its head
-        const int64_t off = (first + t) * HD + (int64_t)piece * 8;
-        bf16x8 x = *reinterpret_cast<const bf16x8*>(k + off);
-        if (f < rope_dim) {
+    // ROPE_BATCH pieces per thread are loaded before any is rotated and stored
+    for (int64_t e0 = threadIdx.x; e0 < n; e0 += (int64_t)ROPE_BATCH * ROPE_THREADS) {
+        bf16x8 x[ROPE_BATCH];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float2 r = cs[t][f / 2 + u];
-                const float a = (float)x[2 * u], b = (float)x[2 * u + 1];
-                x[2 * u] = (__bf16)(a * r.x - b * r.y);
-                x[2 * u + 1] = (__bf16)(a * r.y + b * r.x);
-            }
+        for (int j = 0; j < ROPE_BATCH; ++j) {
+            const int64_t e = e0 + (int64_t)j * ROPE_THREADS;
+            if (e < n) x[j] = *reinterpret_cast<const bf16x8*>(k + first * HD + e * 8);
         }
-        *reinterpret_cast<bf16x8*>(kr + off) = x;
+#pragma unroll
+        for (int j = 0; j < ROPE_BATCH; ++j) {
+            const int64_t e = e0 + (int64_t)j * ROPE_THREADS;
+            if (e >= n) break;
+            const int t = (int)(e / per_token);
+            const int piece = (int)(e - (int64_t)t * per_token);
+            const int f = (piece % (MD / 8)) * 8;  // first feature of the piece within its head
+            if (f < rope_dim) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float2 r = cs[t][f / 2 + u];
+                    const float a = (float)x[j][2 * u], b = (float)x[j][2 * u + 1];
+                    x[j][2 * u] = (__bf16)(a * r.x - b * r.y);
+                    x[j][2 * u + 1] = (__bf16)(a * r.y + b * r.x);
+                }
+            }
+            *reinterpret_cast<bf16x8*>(kr + first * HD + e * 8) = x[j];
+        }
     }
 }
 
