@@ -598,8 +598,9 @@ def main():
                          "prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the layer's multi-GPU sharding is a design "
-              "(see the package documentation), not a path this build runs; use --gpus 1",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the layer "
+              "would shard by heads or along the sequence, with no collective inside a "
+              "kernel); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -29,7 +29,7 @@ BLOCK_TOKENS = 1024
 # tensor ids inside a workload key
 Q, K, V, G, W, LENGTHS, HEAD_PICK, S0_K, S0_V = range(9)
 
-# workload ids (order of the workload list in the design doc)
+# workload ids: 1 tiny fp32 prefill, 2 8K prefill, 3 decode, 4 1M varlen, 5 1M prefill
 TINY_FP32, PREFILL_8K, DECODE, VARLEN_1M, PREFILL_1M = 1, 2, 3, 4, 5
 
 

@@ -11,7 +11,7 @@
  * token; output = RMSNorm(Y) * sigmoid(gate input).  The model card
  * ("2. Model Architecture") fixes 64 heads of dimension 128.
  *
- * Readings taken where the page is silent (each is listed in the design doc):
+ * Readings taken where the page is silent:
  *  - causal, the current token included: the state after token t holds
  *    sum_{u<=t} k~_u^T v~_u and y_t = q~_t S_t (decode order "kv += k^T v,
  *    then y = q kv");
@@ -352,7 +352,7 @@ int la_oracle_backward(const double* q, const double* k, const double* v, const 
  * dimension; the model card, "2. Model Architecture": RoPE on half of the
  * head dimension with base frequency 10,000,000).
  *
- * Readings taken where the pages are silent (listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - rotary embedding as first defined (RoFormer): features (2i, 2i+1) of the
  *    first rope_dim ones form a plane rotated by the angle pos * theta_i,
  *    theta_i = base^(-2i / rope_dim); the other features pass unchanged;
