@@ -151,6 +151,15 @@ def test_backward_varlen(dtype, D, block):
         for s, L in enumerate(lens):
             if L == 0:
                 assert np.array_equal(d_init[s], dfin[s])
+        # without the initial-state gradient (each sequence's first chunk sum
+        # of q~^T dy is then skipped) every other gradient is bit-identical
+        again = la.backward_varlen(*(dev(a, dtype) for a in (q, k, v, g, w, dout)), cu,
+                                   block=block, initial_state=torch.from_numpy(init).cuda(),
+                                   d_final_state=torch.from_numpy(dfin).cuda(), chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        assert again[5] is None
+        for a, b in zip(again[:5], grads[:5]):
+            assert torch.equal(a, b)
 
 
 def test_backward_empty():
