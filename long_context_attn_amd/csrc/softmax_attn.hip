@@ -573,10 +573,14 @@ __global__ __launch_bounds__(MD) void softmax_combine_kernel(const float* __rest
     const int L = len[s];
     if (L < 0 || L >= max_len) return;  // reported by the append step; out left as it was
     const float* pp = part + (int64_t)sh * nsplit * (2 + MD);
+    // only the ranges that hold some of the L + 1 keys (the others hold none)
+    const int nused = min(nsplit, L / SOFTMAX_DEC_SPLIT + 1);
     float M = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, pp[i * (2 + MD)]);
+#pragma unroll 8
+    for (int i = 0; i < nused; ++i) M = fmaxf(M, pp[i * (2 + MD)]);
     float lt = 0.f, ot = 0.f;
-    for (int i = 0; i < nsplit; ++i) {
+#pragma unroll 8
+    for (int i = 0; i < nused; ++i) {
         const float mi = pp[i * (2 + MD)];
         if (mi == -INFINITY) continue;
         const float w = __builtin_amdgcn_exp2f(mi - M);
