@@ -27,9 +27,11 @@
  *   - Work is enqueued asynchronously on `stream`; calls do not synchronize.
  *   - Errors: arguments are validated on the host before any HIP call; on a
  *     validation error nothing is enqueued.  A launch failure reported by
- *     hipGetLastError returns LA_ERR_HIP.  Device-side contents (cu_seqlens
- *     values, non-finite inputs) are not checked; invalid cu_seqlens leave
- *     `out` unspecified.  `out` must not alias an input.
+ *     hipGetLastError returns LA_ERR_HIP.  Device-side conditions (invalid
+ *     cu_seqlens values, a cross-workgroup wait that gave up) leave `out`
+ *     unspecified and are recorded in the workspace, readable with
+ *     lightning_attn_workspace_status.  Non-finite inputs are not checked.
+ *     `out` must not alias an input.
  */
 #ifndef LIGHTNING_ATTN_H
 #define LIGHTNING_ATTN_H
@@ -60,10 +62,43 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype;
 LA_API const char* lightning_attn_status_string(la_status s);
 
 /*
+ * Device-side status of the last call that used `workspace`.  Some conditions
+ * can only be seen by the kernels, after the call has returned LA_OK: they
+ * are recorded in a header at the start of the workspace of every prefill,
+ * state, backward, layer and softmax-prefill call, and that call's `out` (or
+ * gradients, or final states) is then unspecified.  This call copies the
+ * header to the host after the work already enqueued on `stream` has
+ * finished (it synchronizes `stream`):
+ *   status[0]  error: 0 = ok;
+ *              1 = cu_seqlens inconsistent (cu[0] != 0, a decreasing entry,
+ *                  or cu[nseq] != total_tokens); nothing was processed;
+ *              2 = chunk table overflow (cannot happen with a workspace of
+ *                  the size the *_workspace_size call returns);
+ *              3 = a cross-workgroup wait of the fused prefill walk gave up
+ *                  (about a second of polling): the workgroups of one chunk
+ *                  could not all run at once, e.g. because other work held
+ *                  compute units on a concurrent stream
+ *   status[1]  error 3: the wait that gave up first (1 = group sums of the
+ *              RMSNorm exchange, 4 = the norm factors; lane kernel: 1, 2 or 4
+ *              for its three exchange levels), else 0
+ *   status[2], status[3]  error 3: its chunk (lane kernel: 64-token block)
+ *              and head (lane kernel: lane), else 0
+ *   workspace: the same pointer and its size (at least 64 bytes: the header);
+ *              status: host int32[4].
+ * Not meaningful for the decode calls (their workspaces have no header: the
+ * softmax decode reports its per-sequence status words itself).
+ */
+LA_API la_status lightning_attn_workspace_status(const void* workspace, size_t workspace_bytes,
+                                                 int32_t* status, hipStream_t stream);
+
+/*
  * Supported shapes: head_dim in {16, 32, 64, 128}; block in {16, 32, 64} and
  * block <= chunk; heads >= 1.  bf16 with head_dim 128 and block 64 runs the
- * MFMA kernels; every other supported combination runs the fp32 vector-ALU
- * kernels (same results up to rounding).
+ * MFMA kernels, whose walk fuses the RMSNorm across heads and therefore needs
+ * the workgroups of all heads of a chunk resident at once (one per compute
+ * unit): with more heads than the device has compute units, and for every
+ * other supported combination, the fp32 vector-ALU kernels run instead (same
+ * results up to rounding; the workspace size follows that choice).
  *
  * chunk_tokens: the sequence is cut into chunks of this many tokens that are
  * processed in parallel (the running state entering each chunk is an
@@ -170,9 +205,17 @@ LA_API la_status lightning_attn_state_varlen(const void* k, const void* v,
  *   initial_state:   [nseq][heads][head_dim][head_dim] fp32 or NULL (zeros)
  *   d_final_state:   same shape, or NULL (no gradient reaches the final state)
  *   d_initial_state: same shape, or NULL (not written)
- * All arithmetic is fp32 (portable vector-ALU kernels, any supported shape);
- * the workspace holds fp32 copies of q~, k~, v~, y and dy (20 bytes per
- * element of q) plus two states per chunk.  chunk_tokens: 0 = automatic, or
+ * Two paths, chosen by dtype and head_dim:
+ *   - bf16 with head_dim 128: the walks run on bf16 MFMA with fp32
+ *     accumulation and an fp32 running state; SiLU is applied to q, k, v as
+ *     they are loaded (no copies of q~, k~, v~), and the recomputed y and dy
+ *     are kept in bf16 (4 bytes per element of q in the workspace).  Every
+ *     gradient, dweight and d_initial_state included, is therefore at bf16
+ *     accuracy.
+ *   - any other supported shape: fp32 vector-ALU kernels; the workspace holds
+ *     fp32 q~, k~, v~, y and dy (20 bytes per element of q).
+ * Both also keep two fp32 states per chunk and head in the workspace.
+ * chunk_tokens: 0 = automatic, or
  * a multiple of `block` (the result does not depend on it beyond rounding).
  * heads * head_dim must be at most 32768 (else the workspace size is 0 and
  * the call returns LA_ERR_UNSUPPORTED).  Outputs must not alias inputs.
@@ -216,7 +259,9 @@ LA_API la_status lightning_attn_backward_varlen(
  *   w_out:       [heads*head_dim][hidden] bf16
  *   out:         [batch][seqlen][hidden] bf16
  *   initial_state / final_state: as for lightning_attn_prefill
- * bf16 only, head_dim 128 (LA_ERR_UNSUPPORTED otherwise).  The first call on
+ * bf16 only, head_dim 128, and heads at most the device's compute units (the
+ * attention runs the fused MFMA walk; LA_ERR_UNSUPPORTED and a workspace size
+ * of 0 otherwise).  The first call on
  * a device creates that device's hipBLASLt handle, kept until the process
  * ends; the GEMMs use a slice of the caller's workspace.
  */

@@ -7,16 +7,17 @@ gfx950, C ABI in include/lightning_attn.h); this package only marshals torch
 tensors into it.  There is no CPU fallback: if the library is not built the
 calls raise.
 """
-from .ops import (LightningAttnError, backward, backward_varlen,  # noqa: F401
+from .ops import (LightningAttnDeviceError, LightningAttnError, backward,  # noqa: F401
+                  backward_varlen,
                   backward_workspace_size, decode, decode_workspace_size, layer_prefill,
                   layer_workspace_size, library, prefill, prefill_varlen, prefill_workspace_size,
                   softmax_decode, softmax_decode_workspace_size, softmax_prefill,
                   softmax_prefill_varlen, softmax_workspace_size, state,
-                  state_varlen, state_workspace_size, status_string)
+                  state_varlen, state_workspace_size, status_string, workspace_status)
 
 __all__ = ["prefill", "prefill_varlen", "state", "state_varlen", "backward", "backward_varlen",
            "layer_prefill", "decode", "prefill_workspace_size", "state_workspace_size",
            "backward_workspace_size", "layer_workspace_size", "decode_workspace_size", "library",
            "softmax_prefill", "softmax_prefill_varlen", "softmax_workspace_size",
            "softmax_decode", "softmax_decode_workspace_size",
-           "status_string", "LightningAttnError"]
+           "status_string", "workspace_status", "LightningAttnError", "LightningAttnDeviceError"]

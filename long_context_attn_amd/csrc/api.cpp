@@ -33,6 +33,7 @@ int auto_chunk(int64_t total, int nseq, int heads, int block) {
 
 struct Layout {
     bool lane = false;  // lane kernel (sequences walked whole)
+    bool fused = false; // chunked MFMA walk with the RMSNorm exchange inside
     int chunk = 0;
     int max_chunks = 0;
     int n_slots = 0;
@@ -44,6 +45,14 @@ struct Layout {
 bool fused_path(int head_dim, int block, la_dtype dtype) {
     return dtype == LA_DTYPE_BF16 && head_dim == 128 && block == 64;
 }
+
+// The fused walk's cross-head RMSNorm exchange waits, inside the kernel, on
+// the workgroups of every head of a chunk, one workgroup per CU.  Those waits
+// can only end if all `heads` workgroups of a chunk are resident at once, so
+// the fused walk is taken only when heads <= the device's compute units;
+// wider calls run the portable kernels (walk, then a separate norm kernel),
+// which have no cross-workgroup wait.
+bool fused_fits(int heads) { return heads <= la::device_cu_count(); }
 
 // Which bf16 MFMA kernel runs.  chunk_tokens = -1 asks for the lane kernel
 // (sequences never cut, K and V read once; needs heads * 4 <= CUs).  The
@@ -71,6 +80,7 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     if (total < 0 || nseq < 0 || heads < 1 || !supported_dim(head_dim) || !supported_block(block))
         return false;
     const int cus = la::device_cu_count();
+    fused = fused && fused_fits(heads);
     if (chunk_tokens < 0 && !lane_path(heads, chunk_tokens, fused, cus)) return false;  // only -1
     if (lane_path(heads, chunk_tokens, fused, cus)) {
         // blocks of all sequences, counted by the plan in 32 bits
@@ -120,6 +130,7 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
     }
     const int64_t slots = maxc * (chunk / block);
     if (slots > (int64_t)0x7fffffff) return false;
+    L->fused = true;
     L->n_slots = (int)slots;
     L->off_part = off;
     off = align_up(off + sizeof(uint64_t) * (size_t)slots * heads * block);
@@ -247,7 +258,10 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     }
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
     a.states = reinterpret_cast<float*>(ws + L.off_states);
-    const bool mfma = la::mfma_supported(a);
+    // the layout decided the kernels: the fused MFMA walk needs its exchange
+    // words, which only a fused layout holds
+    const bool mfma = L.fused && la::mfma_supported(a);
+    if (a.preact && !mfma) return LA_ERR_UNSUPPORTED;
     if (mfma) {
         a.skip_last = true;
         a.n_slots = L.n_slots;
@@ -392,6 +406,22 @@ const char* lightning_attn_status_string(la_status s) {
         case LA_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
     }
     return "unknown status";
+}
+
+la_status lightning_attn_workspace_status(const void* workspace, size_t workspace_bytes,
+                                          int32_t* status, hipStream_t stream) {
+    if (!workspace || !status) return LA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
+    if (workspace_bytes < sizeof(la::PlanHeader)) return LA_ERR_WORKSPACE_TOO_SMALL;
+    la::PlanHeader h{};
+    if (hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return LA_ERR_HIP;
+    status[0] = h.error;
+    status[1] = h.wait_site;
+    status[2] = h.wait_chunk;
+    status[3] = h.wait_head;
+    return LA_OK;
 }
 
 size_t lightning_attn_prefill_workspace_size(int64_t total_tokens, int nseq, int heads,
@@ -754,7 +784,9 @@ struct LayerLayout {
 static bool layer_layout(int64_t total, int nseq, int hidden, int heads, int head_dim,
                          LayerLayout* L) {
     if (hidden < 1 || head_dim != 128) return false;
-    if (!plan_layout(total, nseq, heads, head_dim, 64, 0, true, &L->pre)) return false;
+    // the attention reads activated q, k, v, which only the fused walk takes
+    if (!plan_layout(total, nseq, heads, head_dim, 64, 0, true, &L->pre) || !L->pre.fused)
+        return false;
     const size_t act = sizeof(uint16_t) * (size_t)total * heads * head_dim;
     size_t off = align_up(L->pre.bytes);
     L->off_act = off;

@@ -14,7 +14,7 @@
 // activations with SiLU applied on the way into LDS, or as it is (dy), so
 // q~, k~, v~ are never written out.  The walks are independent per (chunk,
 // head): no cross-workgroup wait.
-//   y   = causal(SiLU q, SiLU k, SiLU v; S_entry)      -> fp32
+//   y   = causal(SiLU q, SiLU k, SiLU v; S_entry)      -> bf16
 //   dq  = causal(dy, SiLU v, SiLU k; S_entry^T)        * SiLU'(q)
 //   dk  = anti-causal(SiLU v, dy, SiLU q; G_exit^T)    * SiLU'(k)
 //   dv  = anti-causal(SiLU k, SiLU q, dy; G_exit)      * SiLU'(v)

@@ -5,6 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// plan_body.h is plain C++, so that the plan can also be built and tested on
+// the host; here its functions are compiled for both sides
+#define LA_HD __host__ __device__
+#include "plan_body.h"
+
 namespace la {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -14,29 +19,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 // ---------------------------------------------------------------- workspace
-// Chunk plan: every sequence is cut into chunks of at most `chunk` tokens;
-// chunks of one sequence are consecutive in the table.
-struct PlanHeader {
-    int32_t n_chunks;  // chunks in the table (0 if cu_seqlens was invalid)
-    int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow,
-                       // 3 = a cross-workgroup wait of an MFMA prefill timed out
-    int32_t ticket;    // start-order ticket of the fused walk's workgroups
-    int32_t wait_site; // error 3: which wait gave up first, where and who.  Chunked
-                       // walk: 1 group sums, 4 norm factors (chunk, head).  Lane kernel:
-                       // 1 lanes' sums, 2 group sums, 4 totals (block, lane).
-    int32_t wait_chunk;
-    int32_t wait_head;
-    int32_t pad[10];
-};
-struct SegEntry {
-    int32_t first;  // index of the sequence's first chunk
-    int32_t count;  // number of chunks (0 for an empty sequence)
-};
-struct ChunkEntry {
-    int64_t start;  // first token (packed index)
-    int32_t len;    // tokens in the chunk, 1..chunk
-    int32_t seg;    // owning sequence
-};
+// PlanHeader, SegEntry, ChunkEntry and the plan's arithmetic: plan_body.h
+// (included above, outside the namespace)
 
 // --------------------------------------------------------- element helpers
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -19,6 +19,15 @@ namespace la {
 constexpr int PLAN_THREADS = 1024;
 constexpr int CLEAR_BLOCKS = 256;
 
+// the workgroup as plan_sequences sees it
+struct PlanDevCtx {
+    int64_t* scan;
+    int32_t* bad;
+    int32_t* err;
+    __device__ int tid() const { return threadIdx.x; }
+    __device__ void sync() const { __syncthreads(); }
+};
+
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu, int nseq, int64_t seqlen, int64_t total, int chunk,
     int max_chunks, PlanHeader* __restrict__ hdr, SegEntry* __restrict__ segs,
@@ -30,69 +39,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
             clear[i] = 0;
         return;
     }
-    __shared__ int32_t scan[PLAN_THREADS];
-    __shared__ int32_t bad;
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        hdr->ticket = 0;  // start-order ticket of the MFMA walk
-        hdr->wait_site = hdr->wait_chunk = hdr->wait_head = 0;
-    }
-    if (tid == 0) {
-        bad = 0;
-        if (cu != nullptr && (cu[0] != 0 || (int64_t)cu[nseq] != total)) bad = 1;
-    }
-    __syncthreads();
-    int32_t carry = 0;
-    for (int base = 0; base < nseq; base += PLAN_THREADS) {
-        const int s = base + tid;
-        int64_t start = 0, len = 0;
-        if (s < nseq) {
-            if (cu != nullptr) {
-                start = cu[s];
-                len = (int64_t)cu[s + 1] - start;
-                if (len < 0) bad = 1;
-            } else {
-                start = (int64_t)s * seqlen;
-                len = seqlen;
-            }
-        }
-        const int32_t cnt = len > 0 ? (int32_t)((len + chunk - 1) / chunk) : 0;
-        scan[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < PLAN_THREADS; off <<= 1) {  // inclusive Hillis-Steele
-            const int32_t add = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
-        }
-        const int32_t first = carry + scan[tid] - cnt;
-        if (s < nseq) {
-            segs[s].first = first;
-            segs[s].count = cnt;
-            if (chunks != nullptr && first + cnt <= max_chunks) {
-                for (int32_t c = 0; c < cnt; ++c) {
-                    ChunkEntry e;
-                    e.start = start + (int64_t)c * chunk;
-                    const int64_t rem = len - (int64_t)c * chunk;
-                    e.len = (int32_t)(rem < chunk ? rem : chunk);
-                    e.seg = s;
-                    chunks[first + c] = e;
-                }
-            }
-        }
-        carry += scan[PLAN_THREADS - 1];
-        __syncthreads();
-    }
-    __shared__ int32_t err;
-    if (tid == 0) {
-        err = bad ? 1 : (chunks != nullptr && carry > max_chunks ? 2 : 0);
-        hdr->error = err;
-        hdr->n_chunks = err ? 0 : carry;
-    }
-    __syncthreads();
-    // an invalid plan leaves no chunk to process and every sequence empty
-    if (err != 0)
-        for (int s = tid; s < nseq; s += PLAN_THREADS) segs[s].count = 0;
+    __shared__ int64_t scan[PLAN_THREADS];
+    __shared__ int32_t bad, err;
+    plan_sequences<PLAN_THREADS>(PlanDevCtx{scan, &bad, &err}, cu, nseq, seqlen, total, chunk,
+                                 max_chunks, hdr, segs, chunks);
 }
 
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t st) {

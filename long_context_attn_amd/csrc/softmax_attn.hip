@@ -71,7 +71,8 @@ __device__ __forceinline__ float2 rope_cs(int64_t pos, double theta) {
 }
 
 // K's rotation (the attention kernel turns Q itself as it loads it).
-// Workgroup (tile c, group j): tokens 16 j .. 16 j + 15 of tile c.  Each
+// Workgroup (tile c, group j): the ROPE_TOKENS tokens from ROPE_TOKENS * j
+// on of tile c.  Each
 // token's cos / sin table is built once in LDS and serves all of its heads.
 __global__ __launch_bounds__(ROPE_THREADS) void rope_kernel(
     const __bf16* __restrict__ k, __bf16* __restrict__ kr, const PlanHeader* __restrict__ hdr,

@@ -52,6 +52,9 @@ def library():
         lib = ctypes.CDLL(LIB_PATH)
         lib.lightning_attn_status_string.argtypes = [_I]
         lib.lightning_attn_status_string.restype = ctypes.c_char_p
+        lib.lightning_attn_workspace_status.argtypes = [_P, _SZ, ctypes.POINTER(ctypes.c_int32),
+                                                        _P]
+        lib.lightning_attn_workspace_status.restype = _I
         lib.lightning_attn_prefill_workspace_size.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
         lib.lightning_attn_prefill_workspace_size.restype = _SZ
         lib.lightning_attn_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I, _I,
@@ -104,6 +107,26 @@ def library():
     return _lib
 
 
+class LightningAttnDeviceError(RuntimeError):
+    """A condition the kernels recorded in the workspace (the call itself had
+    returned ok): 1 = cu_seqlens inconsistent, 2 = chunk table overflow, 3 = a
+    cross-workgroup wait of the fused walk gave up."""
+
+    TEXT = {1: "cu_seqlens is inconsistent (cu[0] != 0, a decreasing entry, or cu[nseq] != "
+               "total_tokens); nothing was processed",
+            2: "chunk table overflow",
+            3: "a cross-workgroup wait of the fused prefill walk gave up (the workgroups of "
+               "one chunk could not all run at once)"}
+
+    def __init__(self, status):
+        self.error, self.site, self.chunk, self.head = status
+        text = self.TEXT.get(self.error, "unknown device error")
+        if self.error == 3:
+            text += " (wait site %d, chunk %d, head %d)" % (self.site, self.chunk, self.head)
+        super().__init__("lightning_attn: %s (device error %d); the outputs are unspecified"
+                         % (text, self.error))
+
+
 def status_string(status: int) -> str:
     return library().lightning_attn_status_string(int(status)).decode()
 
@@ -111,6 +134,31 @@ def status_string(status: int) -> str:
 def _check(status: int):
     if status != 0:
         raise LightningAttnError(status, status_string(status))
+
+
+def workspace_status(workspace: torch.Tensor):
+    """Device-side status of the last call that used `workspace` (waits for the
+    current stream): (error, wait site, chunk, head), all 0 when ok."""
+    out = (ctypes.c_int32 * 4)()
+    _check(library().lightning_attn_workspace_status(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), out,
+        _stream(workspace.device)))
+    return tuple(int(x) for x in out)
+
+
+def _debug_default(check):
+    if check is None:
+        return os.environ.get("LA_DEBUG", "0") not in ("", "0")
+    return bool(check)
+
+
+def _check_device(workspace, check):
+    """With check (or LA_DEBUG=1 in the environment): wait for the call and raise
+    LightningAttnDeviceError if the kernels recorded an error."""
+    if _debug_default(check):
+        st = workspace_status(workspace)
+        if st[0] != 0:
+            raise LightningAttnDeviceError(st)
 
 
 def _ptr(t):
@@ -166,7 +214,7 @@ def _workspace(nbytes, device, given):
 
 def prefill(q, k, v, gate, weight, *, block=64, eps=1e-6, initial_state=None,
             return_final_state=False, chunk_tokens=0, out=None, final_state=None,
-            workspace=None):
+            workspace=None, check=None):
     """Causal Lightning Attention prefill of B rows of N tokens.
 
     q, k, v, gate: [B, N, H, D] (float32 or bfloat16, contiguous, one device);
@@ -196,12 +244,13 @@ def prefill(q, k, v, gate, weight, *, block=64, eps=1e-6, initial_state=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(init), _ptr(fs),
         B, N, H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes,
         _stream(dev)))
+    _check_device(ws, check)
     return (out, fs) if return_final_state else out
 
 
 def prefill_varlen(q, k, v, gate, weight, cu_seqlens, *, block=64, eps=1e-6, initial_state=None,
                    return_final_state=False, chunk_tokens=0, out=None, final_state=None,
-                   workspace=None):
+                   workspace=None, check=None):
     """Causal prefill of sequences packed back to back.
 
     q, k, v, gate: [T, H, D]; cu_seqlens: int32 [nseq+1] on the same device
@@ -236,6 +285,7 @@ def prefill_varlen(q, k, v, gate, weight, cu_seqlens, *, block=64, eps=1e-6, ini
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(cu_seqlens), nseq,
         T, _ptr(init), _ptr(fs), H, D, int(block), int(chunk_tokens), float(eps), _dtype(q),
         _ptr(ws), ws_bytes, _stream(dev)))
+    _check_device(ws, check)
     return (out, fs) if return_final_state else out
 
 
@@ -247,7 +297,7 @@ def state_workspace_size(total_tokens, nseq, heads, head_dim, block=64, chunk_to
 
 
 def state(k, v, *, block=64, initial_state=None, final_state=None, chunk_tokens=0,
-          workspace=None):
+          workspace=None, check=None):
     """Final states of B rows of N tokens without outputs: initial_state (or zeros)
     + sum_t SiLU(k_t)^T SiLU(v_t).  k, v: [B, N, H, D]; returns [B, H, D, D] fp32."""
     _same(k, v)
@@ -266,11 +316,12 @@ def state(k, v, *, block=64, initial_state=None, final_state=None, chunk_tokens=
     _check(library().lightning_attn_state(
         _ptr(k), _ptr(v), _ptr(init), _ptr(fs), B, N, H, D, int(block), int(chunk_tokens),
         _dtype(k), _ptr(ws), ws_bytes, _stream(dev)))
+    _check_device(ws, check)
     return fs
 
 
 def state_varlen(k, v, cu_seqlens, *, block=64, initial_state=None, final_state=None,
-                 chunk_tokens=0, workspace=None):
+                 chunk_tokens=0, workspace=None, check=None):
     """Final states of packed sequences without outputs.  k, v: [T, H, D];
     cu_seqlens: int32 [nseq+1] on the same device; returns [nseq, H, D, D] fp32."""
     _same(k, v)
@@ -295,6 +346,7 @@ def state_varlen(k, v, cu_seqlens, *, block=64, initial_state=None, final_state=
     _check(library().lightning_attn_state_varlen(
         _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, T, _ptr(init), _ptr(fs), H, D, int(block),
         int(chunk_tokens), _dtype(k), _ptr(ws), ws_bytes, _stream(dev)))
+    _check_device(ws, check)
     return fs
 
 
@@ -314,7 +366,8 @@ def _backward_outputs(q, nseq, H, D, want_d_init):
 
 
 def backward(q, k, v, gate, weight, dout, *, block=64, eps=1e-6, initial_state=None,
-             d_final_state=None, return_d_initial_state=False, chunk_tokens=0, workspace=None):
+             d_final_state=None, return_d_initial_state=False, chunk_tokens=0, workspace=None,
+             check=None):
     """Gradients of `prefill` for a loss with gradient `dout` w.r.t. the output (and
     `d_final_state` w.r.t. the final states).  q, k, v, gate, dout: [B, N, H, D].
     Returns (dq, dk, dv, dgate, dweight, d_initial_state or None); dweight and
@@ -337,12 +390,13 @@ def backward(q, k, v, gate, weight, dout, *, block=64, eps=1e-6, initial_state=N
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(init), _ptr(dfin),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), B, N, H, D, int(block),
         int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    _check_device(ws, check)
     return dq, dk, dv, dg, dw, d_init
 
 
 def backward_varlen(q, k, v, gate, weight, dout, cu_seqlens, *, block=64, eps=1e-6,
                     initial_state=None, d_final_state=None, return_d_initial_state=False,
-                    chunk_tokens=0, workspace=None):
+                    chunk_tokens=0, workspace=None, check=None):
     """Gradients of `prefill_varlen`; q, k, v, gate, dout: [T, H, D], cu_seqlens int32."""
     _same(q, q, k, v, gate, weight, dout)
     if q.dim() != 3 or any(t.shape != q.shape for t in (k, v, gate, dout)):
@@ -368,6 +422,7 @@ def backward_varlen(q, k, v, gate, weight, dout, cu_seqlens, *, block=64, eps=1e
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(cu_seqlens), nseq, T,
         _ptr(init), _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), H,
         D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    _check_device(ws, check)
     return dq, dk, dv, dg, dw, d_init
 
 
@@ -377,7 +432,8 @@ def layer_workspace_size(total_tokens, nseq, hidden, heads, head_dim=128) -> int
 
 
 def layer_prefill(x, w_qkvg, weight, w_out, *, eps=1e-6, initial_state=None,
-                  return_final_state=False, out=None, final_state=None, workspace=None):
+                  return_final_state=False, out=None, final_state=None, workspace=None,
+                  check=None):
     """The layer with its projections.  x: [B, N, hidden] bf16; w_qkvg: [4, hidden, H*D]
     (Wq, Wk, Wv, Wg, y = x W); weight: [H*D]; w_out: [H*D, hidden].  Head dim 128."""
     _same(x, x, w_qkvg, weight, w_out)
@@ -405,6 +461,7 @@ def layer_prefill(x, w_qkvg, weight, w_out, *, eps=1e-6, initial_state=None,
     _check(library().lightning_attn_layer_prefill(
         _ptr(x), _ptr(w_qkvg), _ptr(weight), _ptr(w_out), _ptr(out), _ptr(init), _ptr(fs), B, N,
         hidden, H, D, float(eps), _ptr(ws), ws_bytes, _stream(dev)))
+    _check_device(ws, check)
     return (out, fs) if return_final_state else out
 
 
@@ -447,7 +504,7 @@ def _softmax_args(q, k, v, rope_dim, scale):
 
 
 def softmax_prefill(q, k, v, *, rope_dim=None, rope_base=ROPE_BASE, scale=None, out=None,
-                    workspace=None):
+                    workspace=None, check=None):
     """The hybrid's softmax attention layer on B rows of N tokens: q and k
     rotated on their first rope_dim features (default head_dim / 2, base 1e7),
     then causal softmax attention with logits scaled by `scale` (default
@@ -466,11 +523,12 @@ def softmax_prefill(q, k, v, *, rope_dim=None, rope_base=ROPE_BASE, scale=None, 
     _check(library().lightning_attn_softmax_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, N, H, D, rd, float(rope_base), sc, _dtype(q),
         _ptr(ws), ws_bytes, _stream(q.device)))
+    _check_device(ws, check)
     return out
 
 
 def softmax_prefill_varlen(q, k, v, cu_seqlens, *, rope_dim=None, rope_base=ROPE_BASE, scale=None,
-                           out=None, workspace=None):
+                           out=None, workspace=None, check=None):
     """softmax_prefill on sequences packed back to back: q, k, v [T, H, D] bf16,
     cu_seqlens int32 [nseq+1] on the same device; positions restart at 0 in
     every sequence."""
@@ -494,6 +552,7 @@ def softmax_prefill_varlen(q, k, v, cu_seqlens, *, rope_dim=None, rope_base=ROPE
     _check(library().lightning_attn_softmax_prefill_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), nseq, T, H, D, rd,
         float(rope_base), sc, _dtype(q), _ptr(ws), ws_bytes, _stream(q.device)))
+    _check_device(ws, check)
     return out
 
 

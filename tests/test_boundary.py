@@ -43,9 +43,9 @@ def test_header_declares_the_three_calls():
               "lightning_attn_layer_prefill", "lightning_attn_layer_workspace_size",
               "lightning_attn_softmax_prefill", "lightning_attn_softmax_prefill_varlen",
               "lightning_attn_softmax_workspace_size", "lightning_attn_softmax_decode",
-              "lightning_attn_softmax_decode_workspace_size"):
+              "lightning_attn_softmax_decode_workspace_size", "lightning_attn_workspace_status"):
         assert n in names
-    assert len(names) == 25
+    assert len(names) == 26
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -104,6 +104,33 @@ def test_prefill_workspace_size(lib):
     # varlen: one extra chunk per sequence at most
     assert ops.prefill_workspace_size(1000, 3, 2, 64, 32, 64) >= (1000 // 64 + 3) * 2 * 64 * 64 * 4
     assert ops.decode_workspace_size(256, 64, 128) >= 256 * 64 * 128 * 4 + 256 * 64 * 4
+
+
+def test_fused_walk_needs_heads_within_cus(lib):
+    """The fused walk's cross-head exchange waits on the workgroups of every head
+    of a chunk (one per CU), so it is taken only for heads <= CUs (256 without a
+    GPU); wider calls get the portable kernels' workspace (no exchange words),
+    the same size as for fp32, and the layer (fused walk only) is refused."""
+    for heads in (255, 256):
+        bf = ops.prefill_workspace_size(8192, 1, heads, 128, 64, 1024)
+        f32 = ops.prefill_workspace_size(8192, 1, heads, 128, 64, 1024, dtype=torch.float32)
+        assert bf > f32  # + exchange words
+    for heads in (257, 512):
+        bf = ops.prefill_workspace_size(8192, 1, heads, 128, 64, 1024)
+        f32 = ops.prefill_workspace_size(8192, 1, heads, 128, 64, 1024, dtype=torch.float32)
+        assert bf == f32 > 0
+        assert ops.layer_workspace_size(8192, 1, 6144, heads, 128) == 0
+    assert ops.layer_workspace_size(8192, 1, 6144, 256, 128) > 0
+    assert lib.lightning_attn_layer_prefill(A, A, A, A, A, None, None, 1, 100, 256, 257, 128,
+                                            1e-6, A, 1 << 40, None) == UNSUP
+
+
+def test_workspace_status_validation(lib):
+    st = (ctypes.c_int32 * 4)()
+    assert lib.lightning_attn_workspace_status(None, 1 << 20, st, None) == NULLP
+    assert lib.lightning_attn_workspace_status(A, 1 << 20, None, None) == NULLP
+    assert lib.lightning_attn_workspace_status(A + 8, 1 << 20, st, None) == MISAL
+    assert lib.lightning_attn_workspace_status(A, 32, st, None) == WS
 
 
 def _prefill(lib, q=A, k=A, v=A, g=A, w=A, out=A, init=None, fin=None, batch=1, seqlen=128,

@@ -22,8 +22,8 @@ STATE_TOL = {torch.float32: 1e-5, torch.bfloat16: 4e-3}
 
 
 def plan_error(ws):
-    """Error code the kernels leave in the workspace's plan header (0 = ok)."""
-    return int(ws[4:8].cpu().view(torch.int32)[0])
+    """Error code the kernels leave in the workspace (0 = ok), through the C ABI."""
+    return la.workspace_status(ws)[0]
 
 
 def run_prefill(q, k, v, g, w, B, dtype, block, chunk=0, init=None, eps=1e-6):
@@ -190,7 +190,10 @@ def test_invalid_cu_seqlens_reported(chunk):
     say("invalid cu_seqlens, chunk", chunk)
     la.prefill_varlen(*args, bad, chunk_tokens=chunk, workspace=ws)
     torch.cuda.synchronize()
-    assert plan_error(ws) == 1
+    assert la.workspace_status(ws) == (1, 0, 0, 0)
+    # the binding raises on it when asked (check=True, or LA_DEBUG=1)
+    with pytest.raises(la.LightningAttnDeviceError, match="cu_seqlens"):
+        la.prefill_varlen(*args, bad, chunk_tokens=chunk, workspace=ws, check=True)
     good = torch.tensor([0, 100, 300], dtype=torch.int32, device="cuda")
     out = la.prefill_varlen(*args, good, chunk_tokens=chunk, workspace=ws)
     torch.cuda.synchronize()

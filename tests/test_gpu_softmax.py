@@ -191,3 +191,44 @@ def test_softmax_decode_bad_length_is_reported():
     assert status == [0, 1, 1]
     assert torch.all(out[1:] == 9.0)           # skipped sequences keep their output
     assert torch.count_nonzero(kc[1:]) == 0    # and their caches
+
+
+@pytest.mark.slow
+def test_softmax_decode_bench_shape():
+    """One decode step at the shape bench.py times: 32 sequences x 64 heads,
+    caches of max_len 16384 holding 1024..16383 keys (lengths from a seeded
+    stream).  Six seeded sequences and the longest one carry seeded tokens and
+    are compared with the oracle's attention row of the new token (every
+    head); the others hold plausible filler and only have to run."""
+    S, H, D, max_len = 32, 64, 128, 16384
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([synth.SEED, 96, 5, 0])))
+    lens = [int(x) for x in g.integers(1024, max_len, size=S)]
+    picks = sorted(set(synth.pick(6, S, 96, 1)) | {int(np.argmax(lens))})
+    say("softmax decode bench shape: lengths", lens, "compared", picks)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2025 * 1000 + 97)
+    kc = torch.empty(S, H, max_len, D, device="cuda", dtype=BF)
+    vc = torch.empty_like(kc)
+    for t in (kc, vc):
+        for i in range(S):
+            t[i].normal_(generator=gen)
+    qn = torch.randn(S, H, D, device="cuda", generator=gen).to(BF)
+    kn, vn = torch.randn_like(qn), torch.randn_like(qn)
+    refs = {}
+    for s_ in picks:
+        L = lens[s_]
+        q, k, v = qkv(L + 1, H, D, key=500 + s_)
+        kr = host(dev(oracle.rope(k[:L]), BF))  # the cache's keys: rotated, bf16
+        kc[s_, :, :L] = dev(np.ascontiguousarray(kr.transpose(1, 0, 2)), BF)
+        vc[s_, :, :L] = dev(np.ascontiguousarray(v[:L].transpose(1, 0, 2)), BF)
+        qn[s_], kn[s_], vn[s_] = dev(q[L], BF), dev(k[L], BF), dev(v[L], BF)
+        refs[s_] = oracle.softmax_attention(q, k, v, rows=[L])[L]
+    ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = torch.empty(la.softmax_decode_workspace_size(S, max_len, H, D), dtype=torch.uint8,
+                     device="cuda")
+    out = la.softmax_decode(qn, kn, vn, kc, vc, ln, workspace=ws)
+    torch.cuda.synchronize()
+    assert ws[:4 * S].view(torch.int32).cpu().tolist() == [0] * S
+    o = host(out)
+    check(o[picks], np.stack([refs[s_] for s_ in picks]), BF,
+          "softmax decode 32 x 64 heads, caches 1K-16K, sequences %s" % picks)

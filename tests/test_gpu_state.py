@@ -25,7 +25,7 @@ CASES = [(torch.bfloat16, 128, 64), (torch.bfloat16, 64, 32), (torch.float32, 64
 
 
 def plan_error(ws):
-    return int(ws[4:8].cpu().view(torch.int32)[0])
+    return la.workspace_status(ws)[0]
 
 
 @pytest.mark.parametrize("dtype,D,block", CASES)

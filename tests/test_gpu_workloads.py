@@ -10,9 +10,16 @@ compares what the fp64 oracle can compute in seconds:
   * decode, 256 sequences x 64 heads, 64 steps: each step's outputs and the
     final states of four seeded sequences whose initial states the oracle
     built from their seeded prefixes;
-  * varlen, 1,048,576 packed tokens: every output and final state of three
-    seeded sequences of at most 8192 tokens, packed among the others (also
-    for the lane kernel);
+  * varlen, 1,048,576 packed tokens (automatic chunks of 8192 tokens): every
+    output and final state of three seeded sequences of at most 8192 tokens,
+    packed among the others (also for the lane kernel); every output and
+    final state, on all heads, of a seeded sequence of 16K-40K tokens (several
+    chunks: the scanned states entering them); the longest sequence (about
+    124K tokens, 16 chunks): its final state on four seeded heads and its
+    last 1024 outputs, which the oracle computes from the GPU's state after
+    the tokens before them (checked on the four heads on its own);
+  * the layer with its projections at the shape bench.py times (8192
+    tokens, hidden 6144, 64 heads): every output;
   * one sequence of 1,048,576 tokens: the first 2048 outputs; the state after
     1,047,552 tokens on four seeded heads; the last 1024 outputs, which the
     oracle computes from the GPU's state after 1,047,552 tokens (the four
@@ -77,8 +84,16 @@ def test_prefill_8k_workload():
     runs = {}
     for chunk in (0, -1):
         say("prefill 8K: chunk_tokens", chunk)
-        runs[chunk] = la.prefill(*args, return_final_state=True, chunk_tokens=chunk)
+        runs[chunk] = la.prefill(*args, return_final_state=True, chunk_tokens=chunk, check=True)
         torch.cuda.synchronize()
+    # a second call of the benched configuration gives the same bits (the
+    # cross-head sums are added in a fixed order; the store path keeps every
+    # stored register allocated until the next barrier)
+    say("prefill 8K: second call, bitwise")
+    again = la.prefill(*args, return_final_state=True, check=True)
+    torch.cuda.synchronize()
+    assert torch.equal(again[0], runs[0][0]) and torch.equal(again[1], runs[0][1])
+    del again
     say("prefill 8K: state-only pass")
     fs_only = la.state(args[1], args[2])
     torch.cuda.synchronize()
@@ -132,23 +147,51 @@ def test_varlen_1m_workload():
     T = 1 << 20
     lens = synth.varlen_lengths(T)
     cu = synth.cu_seqlens(lens)
+    assert la.prefill_workspace_size(T, len(lens), H, D) == la.prefill_workspace_size(
+        T, len(lens), H, D, 64, 8192)  # the automatic chunk at this size: 8192 tokens
     cand = [i for i, L in enumerate(lens) if 0 < L <= 8192 and i > 0]
     picks = [cand[i] for i in synth.pick(3, len(cand), synth.VARLEN_1M, 1)]
-    say("varlen: %d sequences, sampled" % len(lens), [(s, lens[s]) for s in picks])
+    # a sequence of several chunks, compared whole on every head
+    mids = [i for i, L in enumerate(lens) if 16384 < L <= 40000]
+    mid = mids[synth.pick(1, len(mids), synth.VARLEN_1M, 2)[0]]
+    # the longest one: final state on four heads, last 1024 outputs
+    far = int(np.argmax(lens))
+    fheads = synth.pick_heads(4, H, synth.VARLEN_1M)
+    say("varlen: %d sequences, sampled" % len(lens), [(s, lens[s]) for s in picks],
+        "whole", (mid, lens[mid]), "longest", (far, lens[far]), "heads", fheads)
     q, k, v, g = (gpu_normal((T, H, D), 41 + t) for t in range(4))
+    ids = (synth.Q, synth.K, synth.V, synth.G)
     wins = {}
-    for s in picks:
+    for s in picks + [mid]:
         a, b = int(cu[s]), int(cu[s + 1])
         ins = [synth.block_tensor(synth.VARLEN_1M, t, a, b, range(H), D, 1.0, threads=THREADS)
-               for t in (synth.Q, synth.K, synth.V, synth.G)]
+               for t in ids]
         for dst, x in zip((q, k, v, g), ins):
             put(dst, slice(a, b), range(H), x)
         wins[s] = ins
+    fa, fb = int(cu[far]), int(cu[far + 1])
+    fw = fb - 1024
+    kf = synth.block_tensor(synth.VARLEN_1M, synth.K, fa, fb, fheads, D, 1.0, threads=THREADS)
+    vf = synth.block_tensor(synth.VARLEN_1M, synth.V, fa, fb, fheads, D, 1.0, threads=THREADS)
+    put(k, slice(fa, fb), fheads, kf)
+    put(v, slice(fa, fb), fheads, vf)
+    last = [synth.block_tensor(synth.VARLEN_1M, t, fw, fb, range(H), D, 1.0, threads=THREADS)
+            for t in ids]
+    for dst, x in zip((q, k, v, g), last):
+        put(dst, slice(fw, fb), range(H), x)
+    # the longest sequence's inputs on the four heads as the GPU holds them
+    kf, vf = host(k[fa:fb, fheads]), host(v[fa:fb, fheads])
     say("varlen: inputs ready")
     w = torch.ones(H * D, dtype=BF16, device="cuda")
     cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
-    out, fs = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True)
+    out, fs = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True, check=True)
     torch.cuda.synchronize()
+    # the longest sequence's state after its first lens - 1024 tokens, on every head
+    say("varlen: state of the longest sequence before its last 1024 tokens")
+    n0 = fw - fa
+    fs_w = la.state(k[fa:fw].view(1, n0, H, D), v[fa:fw].view(1, n0, H, D), check=True)
+    torch.cuda.synchronize()
+    far_out, far_fs, fs_w = host(out[fw:fb]), host(fs[far:far + 1]), host(fs_w)
     # the lane kernel on the same pack: only the sampled sequences are kept
     say("varlen: lane kernel (chunk_tokens -1)")
     out_l, fs_l = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True,
@@ -157,15 +200,32 @@ def test_varlen_1m_workload():
     lane = {s: (host(out_l[int(cu[s]):int(cu[s + 1])]), host(fs_l[s:s + 1])) for s in picks}
     del q, k, v, g, out_l, fs_l
     wh = np.ones(H * D, np.float32)
-    for s in picks:
+    for s in picks + [mid]:
         a, b = int(cu[s]), int(cu[s + 1])
         ref, st = oracle.prefill(*wins[s], wh, return_state=True)
         check(host(out[a:b]), ref, BF16, "varlen sequence %d (%d tokens)" % (s, b - a))
         err = rel_state(host(fs[s:s + 1]), st)
         say("varlen sequence %d final state rel err %.2e" % (s, err))
         assert err < STATE_TOL
-        check(lane[s][0], ref, BF16, "varlen sequence %d, lane kernel" % s)
-        assert rel_state(lane[s][1], st) < STATE_TOL
+        if s in lane:
+            check(lane[s][0], ref, BF16, "varlen sequence %d, lane kernel" % s)
+            assert rel_state(lane[s][1], st) < STATE_TOL
+    # the longest sequence: states on the four heads, then the last window from
+    # the GPU's state entering it
+    st_w = None
+    for a in range(0, n0, synth.CHUNK_TOKENS):
+        b = min(n0, a + synth.CHUNK_TOKENS)
+        st_w = oracle.state(kf[a:b], vf[a:b], init_state=st_w)
+    err = rel_state(fs_w[:, fheads], st_w)
+    say("varlen longest (%d tokens): state after %d tokens, heads %s, rel err %.2e"
+        % (fb - fa, n0, fheads, err))
+    assert err < STATE_TOL
+    st_f = oracle.state(kf[n0:], vf[n0:], init_state=st_w)
+    err = rel_state(far_fs[:, fheads], st_f)
+    say("varlen longest: final state rel err %.2e" % err)
+    assert err < STATE_TOL
+    ref = oracle.prefill(*last, wh, init_state=fs_w)
+    check(far_out, ref, BF16, "varlen longest, tokens [%d, %d) from the GPU state" % (n0, fb - fa))
 
 
 @pytest.mark.slow
@@ -211,3 +271,27 @@ def test_prefill_1m_workload():
     check(out_first, ref, BF16, "prefill 1M tokens [0, %d)" % first)
     ref = oracle.prefill(*win[T1], wh, init_state=host(fs1))
     check(out_last, ref, BF16, "prefill 1M tokens [%d, %d) from the GPU state" % (T1, N))
+
+
+@pytest.mark.slow
+def test_layer_8k_hidden6144_workload():
+    """lightning_attn_layer_prefill at the shape bench.py times: 8192 tokens,
+    hidden 6144 (the model's), 64 heads x 128; x ~ N(0, 1), projections
+    N(0, 1/fan_in), norm weight N(1, 0.02), all bf16 from seeded streams.
+    Every output against the oracle's layer (fp64 products around the pinned
+    prefill)."""
+    N, hidden = 8192, 6144
+    HD = H * D
+    key = (synth.SEED, 92, 0)
+    x = synth.normal(key + (0,), (N, hidden), bf16=True)
+    wq = synth.normal(key + (1,), (4, hidden, HD), scale=1.0 / np.sqrt(hidden), bf16=True)
+    w = synth.normal(key + (2,), (HD,), scale=0.02, mean=1.0, bf16=True)
+    wo = synth.normal(key + (3,), (HD, hidden), scale=1.0 / np.sqrt(HD), bf16=True)
+    say("layer 8K x hidden 6144: inputs ready")
+    out = la.layer_prefill(dev(x, BF16).view(1, N, hidden), dev(wq, BF16), dev(w, BF16),
+                           dev(wo, BF16), check=True)
+    torch.cuda.synchronize()
+    out = host(out).reshape(N, hidden)
+    say("layer 8K x hidden 6144: GPU done")
+    ref = oracle.layer(x, wq, w, wo)
+    check(out, ref, BF16, "layer 8192 tokens, hidden 6144, 64 heads")
