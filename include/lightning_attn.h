@@ -53,7 +53,8 @@ typedef enum {
     LA_ERR_UNSUPPORTED = 3,        /* head_dim, block, chunk or dtype outside the supported set */
     LA_ERR_MISALIGNED = 4,         /* a pointer is not 16-byte aligned */
     LA_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below the matching *_workspace_size() */
-    LA_ERR_HIP = 6                 /* the HIP runtime reported an error while enqueueing */
+    LA_ERR_HIP = 6,                /* the HIP runtime reported an error while enqueueing */
+    LA_ERR_SCRATCH_TOO_SMALL = 7   /* sizes exceed the fixed scratch of lightning_attn_decode_noalloc */
 } la_status;
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype;
@@ -353,6 +354,29 @@ LA_API la_status lightning_attn_decode(const void* q, const void* k, const void*
                                 const void* norm_weight, void* out, float* state, int nseq,
                                 int heads, int head_dim, float eps, la_dtype dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lightning_attn_decode without a workspace and without any allocation, for
+ * callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as lightning_attn_decode.  The
+ * two-kernel decode path (fewer sequences than the device has compute units,
+ * or heads * head_dim above the per-sequence kernel's LDS limit) keeps y and
+ * the per-head sums of squares in a fixed device array of the library, 4 MiB
+ * + 64 KiB per GPU, held from the library's load until the process ends:
+ * shapes whose lightning_attn_decode_workspace_size exceeds it return
+ * LA_ERR_SCRATCH_TOO_SMALL with nothing enqueued (e.g. 128 sequences x 64
+ * heads x 128 fit; 255 sequences do not).  The other shapes use no scratch.
+ * The array's device address is looked up on the first call on each device.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, threads) race and must be serialised by the
+ * caller.  Nothing is carried from one call to the next.
+ */
+LA_API la_status lightning_attn_decode_noalloc(const void* q, const void* k, const void* v,
+                                               const void* gate, const void* norm_weight,
+                                               void* out, float* state, int nseq, int heads,
+                                               int head_dim, float eps, la_dtype dtype,
+                                               hipStream_t stream);
 
 /*
  * Instrumented variants, for attributing time to the kernels of one call.

@@ -404,6 +404,8 @@ const char* lightning_attn_status_string(la_status s) {
         case LA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
         case LA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the required size";
         case LA_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
+        case LA_ERR_SCRATCH_TOO_SMALL:
+            return "sizes exceed the fixed scratch of the no-allocation entry point";
     }
     return "unknown status";
 }
@@ -1033,6 +1035,25 @@ la_status lightning_attn_decode(const void* q, const void* k, const void* v, con
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_impl(q, k, v, gate, norm_weight, out, state, nseq, heads, head_dim, eps, dtype,
                        workspace, workspace_bytes, stream, Marks());
+}
+
+la_status lightning_attn_decode_noalloc(const void* q, const void* k, const void* v,
+                                        const void* gate, const void* norm_weight, void* out,
+                                        float* state, int nseq, int heads, int head_dim, float eps,
+                                        la_dtype dtype, hipStream_t stream) {
+    if (nseq < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
+    if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim)) return LA_ERR_UNSUPPORTED;
+    if ((int64_t)nseq * heads > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
+    if (nseq == 0) return LA_OK;
+    const size_t need = lightning_attn_decode_workspace_size(nseq, heads, head_dim);
+    const bool scratch = la::decode_uses_workspace(nseq, heads, head_dim);
+    if (scratch && need > la::decode_scratch_bytes()) return LA_ERR_SCRATCH_TOO_SMALL;
+    // the shapes that run one kernel per sequence read no workspace: decode_impl
+    // still validates one, so it gets the scratch's address and a size that passes
+    void* ws = nullptr;
+    if (la::decode_scratch(&ws) != hipSuccess) return LA_ERR_HIP;
+    return decode_impl(q, k, v, gate, norm_weight, out, state, nseq, heads, head_dim, eps, dtype,
+                       ws, scratch ? la::decode_scratch_bytes() : need, stream, Marks());
 }
 
 la_status lightning_attn_decode_profiled(

@@ -14,6 +14,7 @@
 // per-head sums of squares in the workspace, and a second kernel applies the
 // norm and gate per sequence.
 #include <atomic>
+#include <mutex>
 
 #include "la_internal.h"
 
@@ -168,6 +169,51 @@ constexpr size_t DEC_SEQ_LDS_MAX = 44 * 1024;
 bool decode_fused(const DecodeArgs& a) {
     return a.nseq >= device_cu_count() &&
            sizeof(float) * ((size_t)a.H * a.D + a.H) <= DEC_SEQ_LDS_MAX;
+}
+
+bool decode_uses_workspace(int nseq, int H, int D) {
+    DecodeArgs a{};
+    a.nseq = nseq;
+    a.H = H;
+    a.D = D;
+    return !decode_fused(a);
+}
+
+// ------------------------------------------ fixed scratch (no allocation)
+// The scratch of the two-kernel decode (y [S][H*D] fp32, then the per-head
+// sums of squares [S][H], at the offsets of the caller's workspace) for the
+// entry point that allocates nothing.  Each GPU holds its own copy from the
+// library's load until the process ends.  The host never uses the array's
+// name as an address: its device address is looked up once per device with
+// hipGetSymbolAddress and kept.  Every call on a GPU shares the array (calls
+// that overlap on one GPU race); nothing in it needs clearing, since the
+// state kernel writes every value the norm kernel reads.
+constexpr size_t DEC_SCRATCH_BYTES = (size_t(4) << 20) + (size_t(64) << 10);
+static __device__ __align__(256) unsigned char scratch[DEC_SCRATCH_BYTES];
+
+size_t decode_scratch_bytes() { return DEC_SCRATCH_BYTES; }
+
+hipError_t decode_scratch(void** out) {
+    constexpr int MAXDEV = 64;
+    static std::atomic<void*> ptrs[MAXDEV];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = ptrs[dev].load(std::memory_order_acquire);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            ptrs[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 template <class TT, int D>

@@ -168,6 +168,13 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_state(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_norm(const DecodeArgs& a, hipStream_t st);
+// whether a decode of this shape runs the two-kernel path, which keeps y and
+// the sums of squares in scratch memory (else one kernel per sequence, none)
+bool decode_uses_workspace(int nseq, int H, int D);
+// the fixed scratch of the no-allocation decode: its size, and the current
+// device's address of it (looked up on the first call on each device)
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** out);
 
 // --------------------------------------------- softmax attention layer
 // The hybrid's softmax layer: rotary embedding on the first rope_dim features,

@@ -103,6 +103,9 @@ def library():
         lib.lightning_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
                                               _SZ, _P]
         lib.lightning_attn_decode.restype = _I
+        lib.lightning_attn_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F,
+                                                      _I, _P]
+        lib.lightning_attn_decode_noalloc.restype = _I
         _lib = lib
     return _lib
 
@@ -482,6 +485,27 @@ def decode(q, k, v, gate, weight, state, *, eps=1e-6, out=None, workspace=None):
     _check(library().lightning_attn_decode(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(state), S, H, D,
         float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    return out
+
+
+def decode_noalloc(q, k, v, gate, weight, state, *, eps=1e-6, out=None):
+    """`decode` through the entry point that allocates nothing: its scratch is
+    a fixed array of the library (4 MiB + 64 KiB per GPU); shapes that need
+    more raise (status 7).  Calls that overlap on one GPU race.  `out` may be
+    passed in so that the call allocates nothing on the torch side either."""
+    _same(q, k, v, gate, weight)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or gate.shape != q.shape:
+        raise ValueError("q, k, v, gate must share one [S, H, D] shape")
+    S, H, D = q.shape
+    if weight.numel() != H * D:
+        raise ValueError("weight must have H*D elements")
+    dev = q.device
+    _state(state, (S, H, D, D), dev, "state")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(library().lightning_attn_decode_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(state), S, H, D,
+        float(eps), _dtype(q), _stream(dev)))
     return out
 
 

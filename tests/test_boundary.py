@@ -43,9 +43,10 @@ def test_header_declares_the_three_calls():
               "lightning_attn_layer_prefill", "lightning_attn_layer_workspace_size",
               "lightning_attn_softmax_prefill", "lightning_attn_softmax_prefill_varlen",
               "lightning_attn_softmax_workspace_size", "lightning_attn_softmax_decode",
-              "lightning_attn_softmax_decode_workspace_size", "lightning_attn_workspace_status"):
+              "lightning_attn_softmax_decode_workspace_size", "lightning_attn_workspace_status",
+              "lightning_attn_decode_noalloc"):
         assert n in names
-    assert len(names) == 26
+    assert len(names) == 27
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -61,7 +62,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     assert ops.status_string(0) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert len(ops.status_string(s)) > 10
     assert ops.status_string(99) == "unknown status"
 
@@ -398,6 +399,23 @@ def test_decode_validation(lib):
     assert call(dtype=5) == UNSUP
     assert call(ws_bytes=16) == WS
     assert call(nseq=0, q=None, state=None) == OK
+
+
+def test_decode_noalloc_validation(lib):
+    """Host-side checks of the no-allocation decode (nothing reaches HIP)."""
+    def call(q=A, state=A, nseq=8, heads=4, d=64, eps=1e-6, dtype=F32):
+        return lib.lightning_attn_decode_noalloc(q, A, A, A, A, A, state, nseq, heads, d, eps,
+                                                 dtype, None)
+    assert call(nseq=-1) == SHAPE
+    assert call(heads=0) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(d=96) == UNSUP
+    assert call(dtype=5) == UNSUP
+    assert call(nseq=0, q=None, state=None) == OK
+    # y of 255 sequences x 64 heads x 128 (fewer sequences than the 256 CUs assumed
+    # without a GPU: the two-kernel path) needs 8.2 MB, more than the fixed 4 MiB + 64 KiB
+    assert call(nseq=255, heads=64, d=128, dtype=BF16) == 7
+    assert ops.status_string(7).startswith("sizes exceed the fixed scratch")
 
 
 def test_stage_names_and_profiled_validation(lib):
