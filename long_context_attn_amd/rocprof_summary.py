@@ -2,7 +2,9 @@
 
     python -m long_context_attn_amd.rocprof_summary TRACE_CSV [--title T] [--command C]
     python -m long_context_attn_amd.rocprof_summary pmc --fetch CSV --write CSV
-           --workload NAME --copy-bytes N [--update JSON] [--title T] [--command C]
+           --workload NAME --copy-bytes N [--kernel-workload K=W ...] [--update JSON]
+           [--title T] [--command C]
+    python -m long_context_attn_amd.rocprof_summary counters CSV [--title T] [--command C]
 
 The first form groups the dispatches of the library's kernels (names in
 namespace la::) of a --kernel-trace run by kernel and launch grid, so that
@@ -98,7 +100,42 @@ def _pmc_values(path):
     return vals, copy
 
 
-def pmc_summary(fetch_csv, write_csv, workload, copy_bytes, title, command, update=None):
+def counters_summary(path, title, command, simds=1024):
+    """Median per dispatch of every counter of a --pmc csv, per kernel."""
+    vals = OrderedDict()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "la::" not in name and not name.startswith("_ZN2la"):
+                continue
+            k = short_name(name).replace("la::", "")
+            vals.setdefault(k, OrderedDict()).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    names = []
+    for d in vals.values():
+        for c in d:
+            if c not in names:
+                names.append(c)
+    out = ["# " + title, "", "Command (repo root, one MI355X):", ""]
+    out += ["    " + c for c in command.split(" ;; ")]
+    note = "Median per dispatch."
+    if "MfmaUtil" in names or "VALUBusy" in names:
+        note += ("  MfmaUtil and VALUBusy are rocprofv3's derived metrics, in percent: the MFMA "
+                 "unit's busy cycles over all %d SIMDs, and the cycles the CUs spend issuing "
+                 "vector-ALU instructions, each against the GPU's active cycles." % simds)
+    out += ["", note, "",
+            "| kernel | dispatches | " + " | ".join(names) + " |",
+            "|---|---|" + "---|" * len(names)]
+    for k, d in vals.items():
+        row = [k, str(max(len(v) for v in d.values()))]
+        for c in names:
+            row.append("%.4g" % statistics.median(d[c]) if c in d else "")
+        out.append("| " + " | ".join(row) + " |")
+    return "\n".join(out) + "\n"
+
+
+def pmc_summary(fetch_csv, write_csv, workload, copy_bytes, title, command, update=None,
+                kernel_workloads=None):
     import json
     import os
     from .build import source_sha
@@ -124,7 +161,8 @@ def pmc_summary(fetch_csv, write_csv, workload, copy_bytes, title, command, upda
         rd, wr = fk * 1024 * f_fetch, wk * 1024 * f_write
         out.append("| %s | %d | %.0f | %.0f | %.1f | %.1f | %.1f |" % (
             k, len(fv[k]), fk, wk, rd / 1e6, wr / 1e6, (rd + wr) / 1e6))
-        entries["%s@%s" % (k, workload)] = dict(
+        wl = (kernel_workloads or {}).get(k, workload)
+        entries["%s@%s" % (k, wl)] = dict(
             hbm_bytes_per_launch=int(rd + wr), read_bytes=int(rd), write_bytes=int(wr),
             fetch_factor=round(f_fetch, 4), write_factor=round(f_write, 4), source_sha=sha)
     if update:
@@ -146,11 +184,23 @@ def main():
         ap.add_argument("--workload", required=True)
         ap.add_argument("--copy-bytes", type=int, required=True)
         ap.add_argument("--update")
+        ap.add_argument("--kernel-workload", action="append", default=[],
+                        help="KERNEL=WORKLOAD: the workload a kernel's dispatches belong to")
         ap.add_argument("--title", default="rocprofv3 traffic counters")
         ap.add_argument("--command", default="")
         a = ap.parse_args()
+        kw = dict(x.split("=", 1) for x in a.kernel_workload)
         print(pmc_summary(a.fetch, a.write, a.workload, a.copy_bytes, a.title, a.command,
-                          a.update), end="")
+                          a.update, kw), end="")
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("counters")
+        ap.add_argument("csv")
+        ap.add_argument("--title", default="rocprofv3 counters")
+        ap.add_argument("--command", default="")
+        a = ap.parse_args()
+        print(counters_summary(a.csv, a.title, a.command), end="")
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("trace")
