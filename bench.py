@@ -299,10 +299,11 @@ def bench_backward(args, la, torch, inputs):
 def bench_layer(args, la, torch):
     """The layer with its projections on the 8K workload: hidden 6144 (the
     model's hidden size) projected up to q, k, v and gate (64 heads x 128),
-    SiLU applied in the q/k/v GEMM epilogue, the attention as in the main
-    line, and the 8192 -> 6144 output projection.  Weights are synthetic,
-    N(0, 1/fan_in) in bf16.  The five GEMMs hold 5 x 2 x 8192 x 6144 x 8192
-    FLOPs; the attention's share is the main line's time."""
+    the activations applied in the GEMM epilogue, the attention as in the
+    main line, and the 8192 -> 6144 output projection, once with the
+    library's own GEMM kernel and once with hipBLASLt.  Weights are
+    synthetic, N(0, 1/fan_in) in bf16.  The five GEMMs hold 5 x 2 x 8192 x
+    6144 x 8192 FLOPs; the attention's share is the main line's time."""
     cfg = PREFILL_8K
     B, N, H, D = cfg["batch"], cfg["seqlen"], cfg["heads"], cfg["head_dim"]
     hidden, HD = LAYER_HIDDEN, cfg["heads"] * cfg["head_dim"]
@@ -316,26 +317,31 @@ def bench_layer(args, la, torch):
     out = torch.empty_like(x)
     ws = torch.empty(la.layer_workspace_size(B * N, B, hidden, H, D), dtype=torch.uint8,
                      device="cuda")
-    call = lambda: la.layer_prefill(x, wq, w, wo, eps=cfg["eps"], out=out, workspace=ws)
-    for _ in range(10):
-        call()
-    torch.cuda.synchronize()
-    n = 20
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
     gemm_flops = 5 * 2 * B * N * hidden * HD
-    res = dict(workload="layer_8k_hidden6144_64h_d128_bf16", us_per_call=round(us, 1),
-               tokens_per_s=round(B * N / (us * 1e-6), 1), gemm_flops=gemm_flops,
-               gemm_tflops_overall=round(gemm_flops / (us * 1e-6) / 1e12, 1),
-               mfma_frac_overall=round(gemm_flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
-    log("layer with projections: %.1f us/call, %.0f TFLOP/s over the whole call"
-        % (us, res["gemm_tflops_overall"]))
+    res = dict(workload="layer_8k_hidden6144_64h_d128_bf16", gemm_flops=gemm_flops)
+    # the library's GEMM kernel (the layer's default) and hipBLASLt beside it
+    for gemm in ("mfma", "hipblaslt"):
+        call = lambda: la.layer_prefill(x, wq, w, wo, eps=cfg["eps"], out=out, workspace=ws,
+                                        gemm=gemm)
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        n = 20
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        tf = gemm_flops / (us * 1e-6) / 1e12
+        res[gemm] = dict(us_per_call=round(us, 1), tokens_per_s=round(B * N / (us * 1e-6), 1),
+                         gemm_tflops_overall=round(tf, 1),
+                         mfma_frac_overall=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+        log("layer with projections, %s GEMMs: %.1f us/call, %.0f TFLOP/s over the whole call"
+            % (gemm, us, tf))
+    res["us_per_call"] = res["mfma"]["us_per_call"]
     del x, wq, wo, out, ws
     return res
 
@@ -491,6 +497,19 @@ def bench_decode(args, la, torch, hip):
     for e in evs:
         hip.destroy(e)
     state_bytes = 2 * S * H * D * D * 4  # read + write of the fp32 state
+    # what a plain in-place read-modify-write stream reaches on this GPU
+    # (torch's elementwise kernel over 1 GiB of fp32): the decode's ceiling
+    buf = torch.ones(1 << 28, device=dev)
+    for _ in range(3):
+        buf.add_(1.0)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        buf.add_(1.0)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbs = 2 * buf.numel() * 4 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del buf
     k_us = per["decode_state"] * 1e3
     # with S >= CUs one kernel per sequence applies the norm too: the
     # decode_norm stage then launches nothing and is not listed
@@ -504,6 +523,8 @@ def bench_decode(args, la, torch, hip):
                state_hbm_frac=round(state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                kernels_us=kernels,
                state_kernel_GBps=round(state_bytes / (k_us * 1e-6) / 1e9, 1),
+               stream_rmw_GBps=round(stream_gbs, 1),
+               of_stream_rmw=round(state_bytes / (ms * 1e-3) / 1e9 / stream_gbs, 4),
                initial_state="K~^T V~ of a prefill of length U{1024..32768} per sequence, "
                              "N(0,1) k/v (torch generator), built with the library's varlen prefill")
     log("decode: %.1f us/step, state %.0f GB/s (%.1f%% of HBM peak), kernels %s" %

@@ -59,6 +59,10 @@ typedef enum {
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype;
 
+/* GEMM kernels of lightning_attn_layer_prefill: the library's own bf16 MFMA
+ * kernel, or hipBLASLt (kept as the baseline the former is timed against). */
+typedef enum { LA_GEMM_MFMA = 0, LA_GEMM_HIPBLASLT = 1 } la_gemm;
+
 /* Human-readable text for a status code (static storage, never NULL). */
 LA_API const char* lightning_attn_status_string(la_status s);
 
@@ -250,10 +254,17 @@ LA_API la_status lightning_attn_backward_varlen(
  *     q~, k~, v~ = SiLU(x Wq), SiLU(x Wk), SiLU(x Wv);  g = x Wg
  *     out        = (RMSNorm(q~ S) * w * sigmoid(g)) Wo  (as lightning_attn_prefill)
  * The four input projections and the output projection are bf16 GEMMs with
- * fp32 accumulation on hipBLASLt.  SiLU is applied by the epilogue of the q,
- * k, v GEMMs to the fp32 accumulators before rounding to bf16, and the
- * attention kernels then read the activated q, k, v (the gate's sigmoid is
- * applied by the attention, as in lightning_attn_prefill).
+ * fp32 accumulation; `gemm` picks the kernels:
+ *   LA_GEMM_MFMA       the library's bf16 MFMA GEMM: the four input
+ *                      projections in one launch, SiLU on q, k, v and the
+ *                      logistic function on the gate applied to the fp32
+ *                      accumulators before the one rounding to bf16 (the
+ *                      attention then reads activated operands and multiplies
+ *                      by the stored sigmoid(gate)); then the output GEMM.
+ *                      Needs hidden % 64 == 0.
+ *   LA_GEMM_HIPBLASLT  hipBLASLt, one call per projection, SiLU in the q, k, v
+ *                      epilogues, the gate's sigmoid applied by the attention
+ *                      (as in lightning_attn_prefill); the baseline.
  *   x:           [batch][seqlen][hidden] bf16
  *   w_qkvg:      [4][hidden][heads*head_dim] bf16 (Wq, Wk, Wv, Wg; y = x W)
  *   norm_weight: [heads*head_dim] bf16
@@ -262,9 +273,10 @@ LA_API la_status lightning_attn_backward_varlen(
  *   initial_state / final_state: as for lightning_attn_prefill
  * bf16 only, head_dim 128, and heads at most the device's compute units (the
  * attention runs the fused MFMA walk; LA_ERR_UNSUPPORTED and a workspace size
- * of 0 otherwise).  The first call on
- * a device creates that device's hipBLASLt handle, kept until the process
- * ends; the GEMMs use a slice of the caller's workspace.
+ * of 0 otherwise).  With LA_GEMM_HIPBLASLT the first call on a device
+ * creates that device's hipBLASLt handle, and each shape's matmul
+ * description and chosen algorithm are kept, until the process ends; the
+ * hipBLASLt GEMMs use a slice of the caller's workspace.
  */
 LA_API size_t lightning_attn_layer_workspace_size(int64_t total_tokens, int nseq, int hidden,
                                                   int heads, int head_dim);
@@ -272,8 +284,8 @@ LA_API la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg,
                                               const void* norm_weight, const void* w_out,
                                               void* out, const float* initial_state,
                                               float* final_state, int batch, int64_t seqlen,
-                                              int hidden, int heads, int head_dim, float eps,
-                                              void* workspace, size_t workspace_bytes,
+                                              int hidden, int heads, int head_dim, la_gemm gemm,
+                                              float eps, void* workspace, size_t workspace_bytes,
                                               hipStream_t stream);
 
 /*

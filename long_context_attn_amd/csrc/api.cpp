@@ -813,12 +813,22 @@ size_t lightning_attn_layer_workspace_size(int64_t total_tokens, int nseq, int h
 la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg, const void* norm_weight,
                                        const void* w_out, void* out, const float* initial_state,
                                        float* final_state, int batch, int64_t seqlen, int hidden,
-                                       int heads, int head_dim, float eps, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
+                                       int heads, int head_dim, la_gemm gemm, float eps,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
     if (batch < 0 || seqlen < 0 || heads < 1 || hidden < 1 || !(eps >= 0.0f))
         return LA_ERR_BAD_SHAPE;
     if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
     if (head_dim != 128) return LA_ERR_UNSUPPORTED;
+    if (gemm != LA_GEMM_MFMA && gemm != LA_GEMM_HIPBLASLT) return LA_ERR_UNSUPPORTED;
+    // the library's GEMM: hidden is the reduction of the input projections
+    // (a multiple of its 64-wide k steps) and the width of the output one
+    if (gemm == LA_GEMM_MFMA && !la::gemm_mfma_supported((int64_t)batch * seqlen,
+                                                         heads * head_dim, hidden))
+        return LA_ERR_UNSUPPORTED;
+    if (gemm == LA_GEMM_MFMA && !la::gemm_mfma_supported((int64_t)batch * seqlen, hidden,
+                                                         heads * head_dim))
+        return LA_ERR_UNSUPPORTED;
     const int64_t total = (int64_t)batch * seqlen;
     if (total > 0) {
         la_status s = check_ptrs(x, w_qkvg, w_out, norm_weight, out, out);
@@ -840,14 +850,24 @@ la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg, const 
     void* gws = ws + L.off_gemm;
     const size_t gbytes = la::gemm_workspace_bytes();
     const size_t wmat = sizeof(uint16_t) * (size_t)hidden * HD;
-    // SiLU in the epilogue of the q, k, v projections; the gate stays raw (its
-    // sigmoid is applied by the attention when it finalises the outputs)
-    const la::GemmAct acts_of[4] = {la::GemmAct::silu, la::GemmAct::silu, la::GemmAct::silu,
-                                   la::GemmAct::none};
     hipError_t e = hipSuccess;
-    for (int i = 0; i < 4 && e == hipSuccess; ++i)
-        e = la::gemm_bf16(x, static_cast<const char*>(w_qkvg) + i * wmat, acts + i * act, total, HD,
-                          hidden, acts_of[i], gws, gbytes, stream);
+    const bool own = gemm == LA_GEMM_MFMA;
+    if (own) {
+        // one launch for the four input projections: SiLU on q, k, v and the
+        // logistic function on the gate in the epilogue (2 bits per projection)
+        const unsigned acts_qkvg = 1u | (1u << 2) | (1u << 4) | (2u << 6);
+        e = la::gemm_bf16_mfma(x, w_qkvg, acts, total, HD, hidden, 4, (int64_t)hidden * HD,
+                               (int64_t)total * HD, acts_qkvg, stream);
+    } else {
+        // hipBLASLt: SiLU in the epilogue of the q, k, v projections; the gate
+        // stays raw (its sigmoid is applied by the attention when it finalises
+        // the outputs)
+        const la::GemmAct acts_of[4] = {la::GemmAct::silu, la::GemmAct::silu, la::GemmAct::silu,
+                                       la::GemmAct::none};
+        for (int i = 0; i < 4 && e == hipSuccess; ++i)
+            e = la::gemm_bf16(x, static_cast<const char*>(w_qkvg) + i * wmat, acts + i * act,
+                              total, HD, hidden, acts_of[i], gws, gbytes, stream);
+    }
     if (e != hipSuccess) return LA_ERR_HIP;
     la::PrefillArgs a{};
     a.q = acts; a.k = acts + act; a.v = acts + 2 * act; a.g = acts + 3 * act;
@@ -862,9 +882,12 @@ la_status lightning_attn_layer_prefill(const void* x, const void* w_qkvg, const 
     a.eps = eps;
     a.bf16 = true;
     a.preact = true;
+    a.gate_act = own;
     la_status s = run_prefill(a, L.pre, workspace, stream);
     if (s != LA_OK) return s;
-    e = la::gemm_bf16(attn, w_out, out, total, hidden, HD, la::GemmAct::none, gws, gbytes, stream);
+    e = own ? la::gemm_bf16_mfma(attn, w_out, out, total, hidden, HD, 1, 0, 0, 0u, stream)
+            : la::gemm_bf16(attn, w_out, out, total, hidden, HD, la::GemmAct::none, gws, gbytes,
+                            stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

@@ -99,25 +99,119 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_state_kernel(
 
 // One workgroup per sequence: all H heads in turn, their y kept in LDS, then
 // the norm and the gate (used when there are at least as many sequences as
-// CUs, so that whole sequences still fill the chip).
+// CUs, so that whole sequences still fill the chip).  The heads are
+// software-pipelined with one barrier each: step h issues the loads of head
+// h + 1's state into the other register set and applies SiLU to its q, k, v,
+// passes the barrier, finishes head h - 1's y (its per-wave partial sums,
+// left in LDS by step h - 1), then updates head h's state and forms its
+// partial y.  So a head's state loads are in flight while the previous head
+// is processed.
 template <class TT, int D>
 __global__ __launch_bounds__(DEC_THREADS) void decode_seq_kernel(
     const TT* __restrict__ q, const TT* __restrict__ k, const TT* __restrict__ v,
     const TT* __restrict__ g, const TT* __restrict__ w, TT* __restrict__ out,
     float* __restrict__ state, int H, float eps) {
-    extern __shared__ float ys[];  // [H * D] y of this token, then [H] sums of squares
+    constexpr int TPR = D / 4;               // threads per state row (4 columns each)
+    constexpr int NRG = DEC_THREADS / TPR;   // row groups
+    constexpr int RPT = (D + NRG - 1) / NRG; // rows per thread
+    constexpr int YW = (D + 63) / 64;        // waves that finish a head's y
+    constexpr int NW = DEC_THREADS / 64;     // waves
+    extern __shared__ float ys[];            // [H * D] y of this token, then [H][YW] sums of y^2
+    __shared__ float qkv[3][3][D];           // SiLU(q), SiLU(k), SiLU(v) of three heads (ring)
+    __shared__ f32x4 red[2][NW][TPR];        // partial y of two heads, per wave
     const int64_t s = blockIdx.x;
     const int HD = H * D;
     float* ss = ys + HD;
-    for (int h = 0; h < H; ++h) {
-        const float t = decode_pair<TT, D>(q, k, v, state, s * H + h, ys + h * D);
-        if (threadIdx.x == 0) ss[h] = t;
+    const int tid = threadIdx.x;
+    const int cq = tid % TPR, rg = tid / TPR, j0 = cq * 4;
+    const int64_t DD = (int64_t)D * D;
+    // rows of head hh's state with the non-temporal hint; a head past the last
+    // gets an empty range (its loads return zeros and touch no memory)
+    auto load_rows = [&](int hh, f32x4 (&r)[RPT]) {
+        const bool in = hh < H;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(state + (s * H + (in ? hh : 0)) * DD), (short)0,
+            __builtin_amdgcn_readfirstlane(in ? (int)(DD * 4) : 0), 0x00020000);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = min(rg + m * NRG, D - 1);
+            r[m] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i * TPR + cq) * 16, 0, 2));
+        }
+    };
+    auto silu_qkv = [&](int hh) {
+        if (hh < H && tid < D) {
+            const int64_t idx = (s * H + hh) * D + tid;
+            qkv[hh % 3][0][tid] = silu_f(to_f32(q[idx]));
+            qkv[hh % 3][1][tid] = silu_f(to_f32(k[idx]));
+            qkv[hh % 3][2][tid] = silu_f(to_f32(v[idx]));
+        }
+    };
+    // y of head hh (sum over the row groups, in order) and its sum of squares
+    // per wave
+    auto finish = [&](int hh) {
+        float sq = 0.f;
+        if (tid < D) {
+            float yj = 0.f;
+            for (int r = 0; r < NW; ++r) yj += red[hh & 1][r][tid / 4][tid % 4];
+            ys[hh * D + tid] = yj;
+            sq = yj * yj;
+        }
+        if (tid < 64 * YW) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+            if ((tid & 63) == 0) ss[hh * YW + (tid >> 6)] = sq;
+        }
+    };
+    f32x4 R0[RPT], R1[RPT], st[RPT];
+    auto step = [&](int h, f32x4 (&cur)[RPT], f32x4 (&nxt)[RPT]) {
+        load_rows(h + 1, nxt);
+        silu_qkv(h + 1);
+        __syncthreads();
+        // the stored state of step h - 1 is no longer read by its stores
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) asm volatile("" ::"v"(st[m]));
+        if (h >= 1) finish(h - 1);
+        const float* qs = qkv[h % 3][0];
+        const float* ks = qkv[h % 3][1];
+        const float* vs = qkv[h % 3][2];
+        const f32x4 vj = {vs[j0], vs[j0 + 1], vs[j0 + 2], vs[j0 + 3]};
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        f32x4* S = reinterpret_cast<f32x4*>(state + (s * H + h) * DD);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + m * NRG;
+            if (i < D) {
+                st[m] = cur[m] + ks[i] * vj;
+                __builtin_nontemporal_store(st[m], &S[i * TPR + cq]);
+                y += qs[i] * st[m];
+            }
+        }
+        // the row groups of a wave summed across its lanes, one partial per wave
+#pragma unroll
+        for (int off = TPR; off < 64; off *= 2)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) y[u] += __shfl_xor(y[u], off);
+        if ((tid & 63) < TPR) red[h & 1][tid >> 6][cq] = y;
+    };
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_rows(0, R0);
+    silu_qkv(0);
+    for (int h = 0; h < H; h += 2) {
+        step(h, R0, R1);
+        if (h + 1 < H) step(h + 1, R1, R0);
     }
     __syncthreads();
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) asm volatile("" ::"v"(st[m]));
+    finish(H - 1);
+    __syncthreads();
     float tot = 0.f;
-    for (int h = 0; h < H; ++h) tot += ss[h];  // head order
+    for (int h = 0; h < H; ++h)
+        for (int i = 0; i < YW; ++i) tot += ss[h * YW + i];  // head order
     const float r = 1.0f / __builtin_sqrtf(tot / (float)HD + eps);
-    for (int e = threadIdx.x; e < HD; e += DEC_THREADS) {
+    for (int e = tid; e < HD; e += DEC_THREADS) {
         const int64_t idx = s * HD + e;
         out[idx] = from_f32<TT>(ys[e] * r * to_f32(w[e]) * sigmoid_f(to_f32(g[idx])));
     }
@@ -161,14 +255,15 @@ int device_cu_count() {
     return n;
 }
 
-// The per-sequence kernel keeps a token's H * D values of y (and H sums) in
-// dynamic LDS, next to about 17 KiB of static LDS: 44 KiB keeps the total
-// within the 64 KiB a launch gets without opting in to more.
-constexpr size_t DEC_SEQ_LDS_MAX = 44 * 1024;
+// The per-sequence kernel keeps a token's H * D values of y (and 2 H sums) in
+// dynamic LDS, next to about 21 KiB of static LDS (two heads' per-wave partial
+// y and three heads' q, k, v): 40 KiB of dynamic LDS keeps the total within
+// the 64 KiB a launch gets without opting in to more.
+constexpr size_t DEC_SEQ_LDS_MAX = 40 * 1024;
 
 bool decode_fused(const DecodeArgs& a) {
     return a.nseq >= device_cu_count() &&
-           sizeof(float) * ((size_t)a.H * a.D + a.H) <= DEC_SEQ_LDS_MAX;
+           sizeof(float) * ((size_t)a.H * a.D + 2 * (size_t)a.H) <= DEC_SEQ_LDS_MAX;
 }
 
 bool decode_uses_workspace(int nseq, int H, int D) {
@@ -219,7 +314,7 @@ hipError_t decode_scratch(void** out) {
 template <class TT, int D>
 static hipError_t decode_state_d(const DecodeArgs& a, hipStream_t st) {
     if (decode_fused(a)) {
-        const size_t lds = sizeof(float) * ((size_t)a.H * D + a.H);
+        const size_t lds = sizeof(float) * ((size_t)a.H * D + 2 * (size_t)a.H);
         hipLaunchKernelGGL((decode_seq_kernel<TT, D>), dim3((unsigned)a.nseq), dim3(DEC_THREADS),
                            lds, st, (const TT*)a.q, (const TT*)a.k, (const TT*)a.v,
                            (const TT*)a.g, (const TT*)a.w, (TT*)a.out, a.state, a.H, a.eps);

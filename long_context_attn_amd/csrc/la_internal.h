@@ -62,8 +62,10 @@ struct PrefillArgs {
     // state: the MFMA walk forms it)
     bool skip_last;
     // MFMA path: q, k, v hold SiLU(q), SiLU(k), SiLU(v) already (applied by
-    // the projection's epilogue); the gate is raw either way
+    // the projection's epilogue)
     bool preact;
+    // with preact: the gate holds sigmoid(gate) already (else it is raw)
+    bool gate_act;
     // MFMA prefill of uniform rows (cu == null): no plan kernel; the chunk-sum
     // kernel computes its chunks from (nseq, seqlen, chunk), and extra
     // workgroups of it write the plan tables, reset the header and clear the
@@ -149,8 +151,16 @@ bool backward_mfma_supported(const PrefillArgs& a);
 hipError_t launch_backward_walk_y(const BackwardArgs& a);
 hipError_t launch_backward_walks_grad(const BackwardArgs& a);
 
-// bf16 projection GEMMs on hipBLASLt: row-major y [rows][n] =
-// act(x [rows][k] w [k][n]), the activation applied to the fp32 accumulators
+// bf16 projection GEMMs on the library's own MFMA kernel: row-major
+// Y_p [M][N] = act_p(X [M][K] W_p [K][N]) for p < P, W_p at w + p * wstride
+// (rows N apart), Y_p at y + p * ystride (rows N apart); acts holds 2 bits per
+// p (0 none, 1 SiLU, 2 logistic), applied to the fp32 accumulators.  Needs
+// N % 8 == 0 and K % 64 == 0.
+bool gemm_mfma_supported(int64_t M, int N, int K);
+hipError_t gemm_bf16_mfma(const void* x, const void* w, void* y, int64_t M, int N, int K, int P,
+                          int64_t wstride, int64_t ystride, unsigned acts, hipStream_t st);
+// the same products on hipBLASLt (the baseline they are timed against):
+// row-major y [rows][n] = act(x [rows][k] w [k][n])
 enum class GemmAct { none, silu };
 size_t gemm_workspace_bytes();
 hipError_t gemm_bf16(const void* x, const void* w, void* y, int64_t rows, int n, int k, GemmAct act,

@@ -82,9 +82,10 @@ struct WalkLds {
 };
 
 // ACT: apply SiLU to q, k, v on load; without it they arrive activated (a
-// projection whose epilogue applied SiLU).  The gate's sigmoid is always
-// applied here, when the outputs are finalised.
-template <bool ACT>
+// projection whose epilogue applied SiLU).  GSIG: apply the logistic function
+// to the gate when the outputs are finalised; without it the gate arrives as
+// sigmoid(gate) (the projection's epilogue applied it).
+template <bool ACT, bool GSIG>
 __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ gate, const __bf16* __restrict__ wgt, __bf16* __restrict__ out,
@@ -171,7 +172,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
                         o[r][u] = (__bf16)((float)y[r][u] * rr[r] * (float)wv[u] *
-                                           sigmoid_f((float)tg.r[r][u]));
+                                           (GSIG ? sigmoid_f((float)tg.r[r][u])
+                                                 : (float)tg.r[r][u]));
                 __builtin_amdgcn_sched_barrier(0);
                 const __amdgpu_buffer_rsrc_t ro =
                     tile_rsrc(out + off0 + (int64_t)jf * MB * HD, rows(jf), HD);
@@ -439,7 +441,9 @@ bool mfma_supported(const PrefillArgs& a) { return a.bf16 && a.D == MD && a.bloc
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
     if (a.max_chunks == 0 && a.nseq == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H + a.nseq));
-    auto* fn = a.preact ? &prefill_mfma_kernel<false> : &prefill_mfma_kernel<true>;
+    auto* fn = a.preact ? (a.gate_act ? &prefill_mfma_kernel<false, false>
+                                      : &prefill_mfma_kernel<false, true>)
+                        : &prefill_mfma_kernel<true, true>;
     hipLaunchKernelGGL(fn, grid, dim3(NTHREADS), 0, st, (const __bf16*)a.q, (const __bf16*)a.k,
                        (const __bf16*)a.v, (const __bf16*)a.g, (const __bf16*)a.w, (__bf16*)a.out,
                        a.hdr, a.segs, a.chunks, a.init_state, a.final_state, a.states, a.part,

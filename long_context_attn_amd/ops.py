@@ -81,8 +81,8 @@ def library():
         lib.lightning_attn_backward_varlen.restype = _I
         lib.lightning_attn_layer_workspace_size.argtypes = [_I64, _I, _I, _I, _I]
         lib.lightning_attn_layer_workspace_size.restype = _SZ
-        lib.lightning_attn_layer_prefill.argtypes = [_P] * 7 + [_I, _I64, _I, _I, _I, _F, _P, _SZ,
-                                                                _P]
+        lib.lightning_attn_layer_prefill.argtypes = [_P] * 7 + [_I, _I64, _I, _I, _I, _I, _F, _P,
+                                                                _SZ, _P]
         lib.lightning_attn_layer_prefill.restype = _I
         lib.lightning_attn_softmax_workspace_size.argtypes = [_I64, _I, _I, _I, _I]
         lib.lightning_attn_softmax_workspace_size.restype = _SZ
@@ -434,11 +434,17 @@ def layer_workspace_size(total_tokens, nseq, hidden, heads, head_dim=128) -> int
         int(total_tokens), int(nseq), int(hidden), int(heads), int(head_dim)))
 
 
+GEMM_BACKENDS = {"mfma": 0, "hipblaslt": 1}
+
+
 def layer_prefill(x, w_qkvg, weight, w_out, *, eps=1e-6, initial_state=None,
                   return_final_state=False, out=None, final_state=None, workspace=None,
-                  check=None):
+                  check=None, gemm="mfma"):
     """The layer with its projections.  x: [B, N, hidden] bf16; w_qkvg: [4, hidden, H*D]
-    (Wq, Wk, Wv, Wg, y = x W); weight: [H*D]; w_out: [H*D, hidden].  Head dim 128."""
+    (Wq, Wk, Wv, Wg, y = x W); weight: [H*D]; w_out: [H*D, hidden].  Head dim 128.
+    gemm: "mfma" (the library's GEMM kernel, hidden % 64 == 0) or "hipblaslt"."""
+    if gemm not in GEMM_BACKENDS:
+        raise ValueError("gemm must be one of %s" % sorted(GEMM_BACKENDS))
     _same(x, x, w_qkvg, weight, w_out)
     if x.dim() != 3 or w_qkvg.dim() != 3 or w_qkvg.shape[0] != 4 or w_qkvg.shape[1] != x.shape[2]:
         raise ValueError("x must be [B, N, hidden] and w_qkvg [4, hidden, H*D]")
@@ -463,7 +469,7 @@ def layer_prefill(x, w_qkvg, weight, w_out, *, eps=1e-6, initial_state=None,
     ws = _workspace(ws_bytes, dev, workspace)
     _check(library().lightning_attn_layer_prefill(
         _ptr(x), _ptr(w_qkvg), _ptr(weight), _ptr(w_out), _ptr(out), _ptr(init), _ptr(fs), B, N,
-        hidden, H, D, float(eps), _ptr(ws), ws_bytes, _stream(dev)))
+        hidden, H, D, GEMM_BACKENDS[gemm], float(eps), _ptr(ws), ws_bytes, _stream(dev)))
     _check_device(ws, check)
     return (out, fs) if return_final_state else out
 

@@ -122,7 +122,7 @@ def test_fused_walk_needs_heads_within_cus(lib):
         assert bf == f32 > 0
         assert ops.layer_workspace_size(8192, 1, 6144, heads, 128) == 0
     assert ops.layer_workspace_size(8192, 1, 6144, 256, 128) > 0
-    assert lib.lightning_attn_layer_prefill(A, A, A, A, A, None, None, 1, 100, 256, 257, 128,
+    assert lib.lightning_attn_layer_prefill(A, A, A, A, A, None, None, 1, 100, 256, 257, 128, 0,
                                             1e-6, A, 1 << 40, None) == UNSUP
 
 
@@ -298,10 +298,10 @@ def test_layer_workspace_and_validation(lib):
     assert ops.layer_workspace_size(T, 1, hidden, H, 64) == 0   # head_dim 128 only
     assert ops.layer_workspace_size(T, 1, 0, H, D) == 0
 
-    def call(x=A, w=A, out=A, batch=2, seqlen=100, hidden=256, heads=2, d=128, eps=1e-6, ws=A,
-             ws_bytes=1 << 40):
+    def call(x=A, w=A, out=A, batch=2, seqlen=100, hidden=256, heads=2, d=128, gemm=0, eps=1e-6,
+             ws=A, ws_bytes=1 << 40):
         return lib.lightning_attn_layer_prefill(x, w, A, A, out, None, None, batch, seqlen, hidden,
-                                                heads, d, eps, ws, ws_bytes, None)
+                                                heads, d, gemm, eps, ws, ws_bytes, None)
     assert call(x=None) == NULLP
     assert call(out=None) == NULLP
     assert call(ws=None) == NULLP
@@ -312,6 +312,9 @@ def test_layer_workspace_and_validation(lib):
     assert call(eps=-1.0) == SHAPE
     assert call(ws_bytes=1024) == WS
     assert call(batch=0, x=None, w=None, out=None) == OK
+    assert call(gemm=2) == UNSUP                     # no such GEMM backend
+    assert call(hidden=200) == UNSUP                 # the library's GEMM: hidden % 64
+    assert call(hidden=200, gemm=1, ws_bytes=8) == WS  # hipBLASLt takes any hidden
 
 
 def test_softmax_workspace_and_validation(lib):

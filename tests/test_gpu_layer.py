@@ -3,10 +3,11 @@ oracle (needs an MI355X).
 
 The oracle multiplies in float64 (x Wq, x Wk, x Wv, x Wg, then the attention
 output by Wo) around its pinned prefill.  On the GPU the projections are bf16
-GEMMs with fp32 accumulation; the q, k, v ones apply SiLU in their epilogue
-before rounding to bf16, so the attention reads one bf16 rounding of each
-activated operand, as the bf16 prefill does; the result is held to the bf16
-bar.
+GEMMs with fp32 accumulation, either the library's own MFMA kernel (SiLU on
+q, k, v and the logistic function on the gate in its epilogue) or hipBLASLt
+(SiLU in the q, k, v epilogues, the gate's sigmoid in the attention); the
+attention reads one bf16 rounding of each activated operand, as the bf16
+prefill does, and the result is held to the bf16 bar.
 """
 import numpy as np
 import pytest
@@ -33,26 +34,30 @@ def layer_inputs(T, hidden, H, key):
     return x, wq, w, wo
 
 
-@pytest.mark.parametrize("B,N,hidden,H", [(2, 300, 256, 2), (1, 1100, 512, 4), (3, 64, 384, 1)])
-def test_layer_against_oracle(B, N, hidden, H):
+@pytest.mark.parametrize("gemm", ["mfma", "hipblaslt"])
+@pytest.mark.parametrize("B,N,hidden,H", [(2, 300, 256, 2), (1, 1100, 512, 4), (3, 64, 384, 1),
+                                          (1, 700, 320, 3)])
+def test_layer_against_oracle(B, N, hidden, H, gemm):
     D = 128
     T = B * N
     x, wq, w, wo = layer_inputs(T, hidden, H, key=31 + H)
     init = np.random.default_rng(H).standard_normal((B, H, D, D)).astype(np.float32) * 0.1
     seg = np.arange(B + 1) * N
     ref, st = oracle.layer(x, wq, w, wo, cu_seqlens=seg, init_state=init, return_state=True)
-    say("layer B", B, "N", N, "hidden", hidden, "H", H)
+    say("layer B", B, "N", N, "hidden", hidden, "H", H, "gemm", gemm)
     out, fs = la.layer_prefill(dev(x, BF16).view(B, N, hidden), dev(wq, BF16), dev(w, BF16),
                                dev(wo, BF16), initial_state=torch.from_numpy(init).cuda(),
-                               return_final_state=True)
+                               return_final_state=True, gemm=gemm, check=True)
     torch.cuda.synchronize()
-    check(host(out).reshape(T, hidden), ref, BF16, "layer B=%d N=%d hidden=%d H=%d" % (B, N, hidden, H))
+    check(host(out).reshape(T, hidden), ref, BF16,
+          "layer B=%d N=%d hidden=%d H=%d gemm=%s" % (B, N, hidden, H, gemm))
     err = rel_state(host(fs), st)
     say("layer final state rel err %.2e" % err)
     assert err < 8e-3
 
 
-def test_layer_matches_prefill_on_projected_inputs():
+@pytest.mark.parametrize("gemm", ["mfma", "hipblaslt"])
+def test_layer_matches_prefill_on_projected_inputs(gemm):
     """The layer's attention equals lightning_attn_prefill run on the same
     projected inputs: with Wo = I the two outputs agree to bf16 rounding."""
     B, N, H, D = 1, 500, 2, 128
@@ -60,7 +65,7 @@ def test_layer_matches_prefill_on_projected_inputs():
     x, wq, w, _ = layer_inputs(B * N, hidden, H, key=40)
     eye = np.eye(HD, dtype=np.float32)
     out = la.layer_prefill(dev(x, BF16).view(B, N, hidden), dev(wq, BF16), dev(w, BF16),
-                           dev(eye, BF16))
+                           dev(eye, BF16), gemm=gemm)
     torch.cuda.synchronize()
     xs = dev(x, BF16).float()
     proj = [(xs @ dev(wq[i], BF16).float()) for i in range(4)]
@@ -69,4 +74,19 @@ def test_layer_matches_prefill_on_projected_inputs():
     torch.cuda.synchronize()
     emax, emean = oracle.compare(host(out).reshape(N, HD), host(ref).reshape(N, HD))
     say("layer vs prefill on projected inputs: e_max %.2e e_mean %.2e" % (emax, emean))
+    assert emax < 2e-2 and emean < 2e-3
+
+
+def test_layer_gemm_backends_agree():
+    """The library's GEMM and hipBLASLt on the same layer inputs (ragged token
+    count, hidden a multiple of 64 but not of the 256-wide tiles): both
+    round the same fp32 products to bf16, so they agree to bf16 rounding."""
+    B, N, hidden, H = 2, 517, 448, 2
+    x, wq, w, wo = layer_inputs(B * N, hidden, H, key=44)
+    args = (dev(x, BF16).view(B, N, hidden), dev(wq, BF16), dev(w, BF16), dev(wo, BF16))
+    a = la.layer_prefill(*args, gemm="mfma")
+    b = la.layer_prefill(*args, gemm="hipblaslt")
+    torch.cuda.synchronize()
+    emax, emean = oracle.compare(host(a).reshape(B * N, hidden), host(b).reshape(B * N, hidden))
+    say("layer, MFMA GEMM vs hipBLASLt: e_max %.2e e_mean %.2e" % (emax, emean))
     assert emax < 2e-2 and emean < 2e-3

@@ -288,10 +288,13 @@ def test_layer_8k_hidden6144_workload():
     w = synth.normal(key + (2,), (HD,), scale=0.02, mean=1.0, bf16=True)
     wo = synth.normal(key + (3,), (HD, hidden), scale=1.0 / np.sqrt(HD), bf16=True)
     say("layer 8K x hidden 6144: inputs ready")
-    out = la.layer_prefill(dev(x, BF16).view(1, N, hidden), dev(wq, BF16), dev(w, BF16),
-                           dev(wo, BF16), check=True)
-    torch.cuda.synchronize()
-    out = host(out).reshape(N, hidden)
+    args = (dev(x, BF16).view(1, N, hidden), dev(wq, BF16), dev(w, BF16), dev(wo, BF16))
+    outs = {}
+    for gemm in ("mfma", "hipblaslt"):
+        outs[gemm] = host(la.layer_prefill(*args, check=True, gemm=gemm)).reshape(N, hidden)
+        torch.cuda.synchronize()
+    del args
     say("layer 8K x hidden 6144: GPU done")
     ref = oracle.layer(x, wq, w, wo)
-    check(out, ref, BF16, "layer 8192 tokens, hidden 6144, 64 heads")
+    for gemm, out in outs.items():
+        check(out, ref, BF16, "layer 8192 tokens, hidden 6144, 64 heads, GEMM %s" % gemm)
