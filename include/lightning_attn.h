@@ -84,10 +84,8 @@ LA_API const char* lightning_attn_status_string(la_status s);
  *                  could not all run at once, e.g. because other work held
  *                  compute units on a concurrent stream
  *   status[1]  error 3: the wait that gave up first (1 = group sums of the
- *              RMSNorm exchange, 4 = the norm factors; lane kernel: 1, 2 or 4
- *              for its three exchange levels), else 0
- *   status[2], status[3]  error 3: its chunk (lane kernel: 64-token block)
- *              and head (lane kernel: lane), else 0
+ *              RMSNorm exchange, 4 = the norm factors), else 0
+ *   status[2], status[3]  error 3: its chunk and head, else 0
  *   workspace: the same pointer and its size (at least 64 bytes: the header);
  *              status: host int32[4].
  * Not meaningful for the decode calls (their workspaces have no header: the
@@ -109,12 +107,9 @@ LA_API la_status lightning_attn_workspace_status(const void* workspace, size_t w
  * processed in parallel (the running state entering each chunk is an
  * exclusive prefix sum of per-chunk states).  0 lets the library choose (about
  * one (chunk, head) work item per compute unit, at most 8192 tokens); a
- * positive value must be a multiple of `block`.  -1 asks the MFMA path not to
- * cut sequences at all: one workgroup per (head, 32-column slice of the
- * state) walks each sequence whole, which needs heads * 4 <= the device's
- * compute units and bf16 with head_dim 128 and block 64 (else the workspace
- * size is 0 and the call returns LA_ERR_UNSUPPORTED).  The result does not
- * depend on it beyond rounding.
+ * positive value must be a multiple of `block`; negative values return
+ * LA_ERR_BAD_SHAPE (workspace size 0).  The result does not depend on it
+ * beyond rounding.
  *
  * Workspace bytes needed by a prefill over `total_tokens` tokens in `nseq`
  * sequences (a batch of B rows of N tokens is nseq = B, total = B*N).

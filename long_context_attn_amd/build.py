@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning_attn.so")
-SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "lane.hip", "state_mfma.hip",
+SOURCES = ["api.cpp", "plan_scan_norm.hip", "valu.hip", "mfma.hip", "state_mfma.hip",
            "decode.hip", "backward.hip", "backward_mfma.hip", "gemm_hipblaslt.cpp", "gemm.hip",
            "softmax_attn.hip"]
 ARCH = "gfx950"

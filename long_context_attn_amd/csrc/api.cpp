@@ -32,12 +32,11 @@ int auto_chunk(int64_t total, int nseq, int heads, int block) {
 }
 
 struct Layout {
-    bool lane = false;  // lane kernel (sequences walked whole)
     bool fused = false; // chunked MFMA walk with the RMSNorm exchange inside
     int chunk = 0;
     int max_chunks = 0;
     int n_slots = 0;
-    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rsub = 0, off_tot = 0,
+    size_t off_segs = 0, off_chunks = 0, off_states = 0, off_part = 0, off_rsub = 0,
            off_clear_end = 0, bytes = 0;
 };
 
@@ -54,24 +53,9 @@ bool fused_path(int head_dim, int block, la_dtype dtype) {
 // which have no cross-workgroup wait.
 bool fused_fits(int heads) { return heads <= la::device_cu_count(); }
 
-// Which bf16 MFMA kernel runs.  chunk_tokens = -1 asks for the lane kernel
-// (sequences never cut, K and V read once; needs heads * 4 <= CUs).  The
-// automatic choice (0) is the chunked two-pass prefill: on MI355X the lane
-// kernel's four workgroups per head each apply SiLU to the head's full Q and
-// K, and at 8192 tokens x 64 heads it measured 364 us against 211 us.
-bool lane_path(int heads, int chunk_tokens, bool fused, int cus) {
-    if (!fused || chunk_tokens != -1) return false;
-    const int lanes = heads * la::lane_slices();
-    return lanes <= cus && lanes <= la::lane_max_lanes();
-}
-
-// Workspace: [PlanHeader][SegEntry x nseq], then
-//  * lane kernel: exchange rings part [XR][lanes][64], rsub [XR][groups][64]
-//    and tot [XR][64] of 8-byte words, cleared by the plan on every call;
-//  * otherwise [ChunkEntry x max_chunks], then per-chunk states
-//    [max_chunks][H][D][D] fp32 (chunk sums, then the states entering the
-//    chunks), then
-//  * MFMA path: the words cleared on every call before the walk (by the plan
+// Workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks], then
+// per-chunk states [max_chunks][H][D][D] fp32 (chunk sums, then the states
+// entering the chunks), then on the fused MFMA path the words cleared on every call before the walk (by the plan
 //    kernel, or for uniform rows by the chunk-sum kernel), the
 //    per-(chunk, block) RMSNorm exchange part [n_slots][H][64] and
 //    rsub [n_slots][ceil(H/16)][64].
@@ -79,31 +63,8 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
                  bool fused, Layout* L) {
     if (total < 0 || nseq < 0 || heads < 1 || !supported_dim(head_dim) || !supported_block(block))
         return false;
-    const int cus = la::device_cu_count();
     fused = fused && fused_fits(heads);
-    if (chunk_tokens < 0 && !lane_path(heads, chunk_tokens, fused, cus)) return false;  // only -1
-    if (lane_path(heads, chunk_tokens, fused, cus)) {
-        // blocks of all sequences, counted by the plan in 32 bits
-        if (total / block + nseq > (int64_t)0x7fffffff) return false;
-        L->lane = true;
-        L->chunk = block;
-        L->max_chunks = 0;
-        size_t off = align_up(sizeof(la::PlanHeader));
-        L->off_segs = off;
-        off = align_up(off + sizeof(la::SegEntry) * (size_t)nseq);
-        const size_t xr = (size_t)la::lane_ring_slots();
-        const size_t lanes = (size_t)heads * la::lane_slices();
-        const size_t groups = (lanes + la::lane_group_size() - 1) / la::lane_group_size();
-        L->off_part = off;
-        off = align_up(off + sizeof(uint64_t) * xr * lanes * block);
-        L->off_rsub = off;
-        off = align_up(off + sizeof(uint64_t) * xr * groups * block);
-        L->off_tot = off;
-        off = align_up(off + sizeof(uint64_t) * xr * block);
-        L->off_clear_end = off;
-        L->bytes = off;
-        return true;
-    }
+    if (chunk_tokens < 0) return false;
     int chunk = chunk_tokens;
     // Both paths: about one (chunk, head) item per CU.  For the MFMA walk
     // that is 2048-token chunks at 8192 tokens x 64 heads, the fastest
@@ -239,23 +200,6 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     a.max_chunks = L.max_chunks;
     a.hdr = reinterpret_cast<la::PlanHeader*>(ws);
     a.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
-    if (L.lane) {
-        // the plan counts 64-token blocks, writes no chunk table and clears
-        // the exchange rings; then one lane kernel does everything else
-        a.chunks = nullptr;
-        a.states = nullptr;
-        a.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
-        a.rsub = reinterpret_cast<uint64_t*>(ws + L.off_rsub);
-        a.tot = reinterpret_cast<uint64_t*>(ws + L.off_tot);
-        a.clear = a.part;
-        a.clear_words = (int64_t)((L.off_clear_end - L.off_part) / sizeof(uint64_t));
-        hipError_t e = marks.mark(stream);
-        if (e == hipSuccess) e = la::launch_plan(a, stream);
-        for (int i = 0; i < 3 && e == hipSuccess; ++i) e = marks.mark(stream);
-        if (e == hipSuccess) e = la::launch_prefill_lane(a, stream);
-        for (int i = 0; i < 2 && e == hipSuccess; ++i) e = marks.mark(stream);
-        return e == hipSuccess ? LA_OK : LA_ERR_HIP;
-    }
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
     a.states = reinterpret_cast<float*>(ws + L.off_states);
     // the layout decided the kernels: the fused MFMA walk needs its exchange
@@ -444,7 +388,7 @@ static la_status prefill_impl(const void* q, const void* k, const void* v, const
                               la_dtype dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, Marks marks) {
     if (batch < 0 || seqlen < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
-    if (chunk_tokens < -1) return LA_ERR_BAD_SHAPE;
+    if (chunk_tokens < 0) return LA_ERR_BAD_SHAPE;
     if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
         return LA_ERR_UNSUPPORTED;
     if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
@@ -523,7 +467,7 @@ la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void
                                         la_dtype dtype, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
     if (nseq < 0 || total_tokens < 0 || total_tokens > 0x7fffffffLL || heads < 1 ||
-        !(eps >= 0.0f) || chunk_tokens < -1)
+        !(eps >= 0.0f) || chunk_tokens < 0)
         return LA_ERR_BAD_SHAPE;
     if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
         return LA_ERR_UNSUPPORTED;

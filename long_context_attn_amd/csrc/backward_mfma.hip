@@ -119,11 +119,10 @@ __device__ __forceinline__ void walk_producer(const WalkGeom<REV>& G, const __bf
 // sX + b * TILE (and likewise sK, sV); sP is this walk's score tile.  entry
 // is the (chunk, head)'s D x D state, read transposed when TRS.  EPI = 0: Y
 // to yout (fp32), 1: gout = Y * SiLU'(raw) (bf16), 2: gout = Y (bf16).
-// LEAN fits the wave in 168 registers (three waves per SIMD): R^T X^T moves
-// after the first barrier (O is then not held across it), the operands of
-// the scores and of the state update are read in halves and quarters, and
-// the lane's LDS addresses are formed anew in every iteration instead of
-// being held in registers for the whole walk.
+// LEAN fits the wave in 168 registers (three waves per SIMD): the operands
+// of R^T X^T, of the scores and of the state update are read in halves and
+// quarters, and the lane's LDS addresses are formed anew in every iteration
+// instead of being held in registers for the whole walk.
 template <bool REV, bool TRS, int EPI, bool LEAN>
 __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf16* sX0,
                                               const __bf16* sK0, const __bf16* sV0, __bf16* sP,
@@ -144,7 +143,10 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
     u32x2 ob[2][4];      // bf16 (EPI 1, 2)
     for (int it = 0; it < iters; ++it) {
         int lane = lane0;
-        if (LEAN) asm volatile("" : "+v"(lane));
+        if (LEAN) {
+            lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+            asm volatile("" : "+v"(lane));
+        }
         const int l32 = lane & 31, g = lane >> 5;
         const int dv = 32 * w + l32;
         const int jc = it - 1;  // visit index of the block computed in this iteration
@@ -184,9 +186,26 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
                 for (int tb = 0; tb < 2; ++tb) O[tb] = mfma32(a, xo[s % XS][tb], O[tb]);
             }
         };
-        // ---- phase 1: the scores (and R^T X^T unless LEAN)
+        const int blk = G.blk_of(jc), n = G.rows(blk);
+        const int64_t tbase = G.off0 + (int64_t)max(blk, 0) * MB * HD;
+        // output positions: token t = 32 tb + l32, dims 32 w + 8 q + 4 g .. + 3
+        const int ooff = l32 * HD + 32 * w + 4 * g;
+        // the raw inputs of the SiLU' factor, loaded ahead of the products
+        // (LEAN: at the end of phase 1, with fewer registers in use)
+        bf16x4 rw[2][4];
+        auto load_raw = [&]() {
+            const __amdgpu_buffer_rsrc_t rr = tile_rsrc(raw + tbase, n, HD);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    rw[tb][q] = __builtin_bit_cast(
+                        bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                    rr, (ooff + 32 * tb * HD + 8 * q) * 2, 0, 0));
+        };
+        // ---- phase 1: R^T X^T and the scores
         if (comp) {
-            if (!LEAN) state_term();
+            state_term();
             if (scores) {
                 constexpr int SH = LEAN ? MD / 32 : MD / 16;  // operands read at once
                 f32x16 pacc = {};
@@ -216,6 +235,10 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
                 }
             }
         }
+        if (EPI == 1 && LEAN && comp) {
+            __builtin_amdgcn_sched_barrier(0);  // not hoisted into the score products
+            load_raw();
+        }
         __syncthreads();  // A
         // ---- phase 2, iteration 0: the state entering the chunk
         if (it == 0) {
@@ -233,40 +256,27 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
         }
         // ---- phase 2: V^T P^T into O, the state update, the outputs
         if (comp) {
-            const int blk = G.blk_of(jc), n = G.rows(blk);
-            const int64_t tbase = G.off0 + (int64_t)blk * MB * HD;
-            // output positions: token t = 32 tb + l32, dims 32 w + 8 q + 4 g .. + 3
-            const int ooff = l32 * HD + 32 * w + 4 * g;
-            // the raw inputs of the SiLU' factor, loaded ahead of the products
-            // (LEAN: ahead of the state update)
-            bf16x4 rw[2][4];
-            auto load_raw = [&]() {
-                const __amdgpu_buffer_rsrc_t rr = tile_rsrc(raw + tbase, n, HD);
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        rw[tb][q] = __builtin_bit_cast(
-                            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                        rr, (ooff + 32 * tb * HD + 8 * q) * 2, 0, 0));
-            };
             if (EPI == 1 && !LEAN) load_raw();
-            if (LEAN) state_term();
             bf16x8 vop[MB / 16];
             bf16x8 pb[MB / 16][2];
+            // P^T operand of token slice s for output tile tb (the slice that
+            // lies outside the window is never read)
+            auto used = [](int s, int tb) { return REV ? (tb == 0 || s >= 2) : (tb == 1 || s < 2); };
+            auto load_p = [&](int s, int tb) {
+                pb[s][tb] = *reinterpret_cast<const bf16x8*>(sP + (32 * tb + l32) * BPP + 16 * s + 8 * g);
+            };
+            // K operands of the state update, KS token slices of 16 at a time
+            // (LEAN: read after the products with the scores, which take their
+            // P^T operands one output tile at a time)
+            constexpr int KS = LEAN ? 1 : 2;
+            bf16x8 ko[KS][4];
 #pragma unroll
             for (int s = 0; s < MB / 16; ++s) {
                 vop[s] = ld_tr_operand(sV, 16 * s, 32 * w, lane);
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
-                    if (REV ? (tb == 0 || s >= 2) : (tb == 1 || s < 2))
-                        pb[s][tb] = *reinterpret_cast<const bf16x8*>(sP + (32 * tb + l32) * BPP +
-                                                                     16 * s + 8 * g);
+                    if (used(s, tb) && (!LEAN || tb == 0)) load_p(s, tb);
             }
-            // K operands of the state update, KS token slices of 16 at a time
-            // (LEAN: read after the products with the scores)
-            constexpr int KS = LEAN ? 1 : 2;
-            bf16x8 ko[KS][4];
             if (!LEAN) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
@@ -275,12 +285,18 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb) {
+                if (LEAN && tb == 1) {
+#pragma unroll
+                    for (int s = 0; s < MB / 16; ++s)
+                        if (used(s, 1)) load_p(s, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
 #pragma unroll
                 for (int s = 0; s < MB / 16; ++s)
-                    if (REV ? (tb == 0 || s >= 2) : (tb == 1 || s < 2))
-                        O[tb] = mfma32(vop[s], pb[s][tb], O[tb]);
-            if (EPI == 1 && LEAN) load_raw();
+                    if (used(s, tb)) O[tb] = mfma32(vop[s], pb[s][tb], O[tb]);
+            }
+            if (LEAN) __builtin_amdgcn_sched_barrier(0);  // P^T operands free before K's
 #pragma unroll
             for (int s0 = 0; s0 < MB / 16; s0 += KS) {
                 if (LEAN || s0 > 0) {

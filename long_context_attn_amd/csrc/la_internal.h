@@ -82,10 +82,6 @@ struct PrefillArgs {
     // words zeroed on every call before the walk (exchange words)
     uint64_t* clear;
     int64_t clear_words;
-    // lane kernel: per-token totals over all lanes, [ring slots][64]
-    // (part and rsub are rings of the same depth, [slots][lanes][64] and
-    // [slots][ceil(lanes / group)][64])
-    uint64_t* tot;
 };
 
 // compute units of the current device (cached per device; 256 if unknown)
@@ -112,15 +108,6 @@ hipError_t launch_chunk_state_mfma(const PrefillArgs& a, hipStream_t st);
 enum class SumSkip : int { none = 0, last = 1, first = 2 };
 hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const void* y, bool silu_x,
                                   bool silu_y, float* states, SumSkip skip, hipStream_t st);
-// lane bf16 MFMA prefill (D = 128, block = 64): one workgroup per (head,
-// 32-column state slice) walks every sequence whole; needs heads * 4 <= cus
-// (all lanes resident at once).  The plan runs first with chunk = 64 and no
-// chunk table, and clears the exchange rings.
-int lane_max_lanes();
-int lane_ring_slots();
-int lane_group_size();
-int lane_slices();
-hipError_t launch_prefill_lane(const PrefillArgs& a, hipStream_t st);
 
 // backward pass (portable fp32 kernels, any supported shape); the plan runs
 // first with the chunk table

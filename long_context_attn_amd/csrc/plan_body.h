@@ -24,9 +24,8 @@ struct PlanHeader {
     int32_t error;     // 0 = ok, 1 = cu_seqlens inconsistent, 2 = table overflow,
                        // 3 = a cross-workgroup wait of an MFMA prefill timed out
     int32_t ticket;    // start-order ticket of the fused walk's workgroups
-    int32_t wait_site; // error 3: which wait gave up first, where and who.  Chunked
-                       // walk: 1 group sums, 4 norm factors (chunk, head).  Lane kernel:
-                       // 1 lanes' sums, 2 group sums, 4 totals (block, lane).
+    int32_t wait_site; // error 3: which wait gave up first, where and who:
+                       // 1 group sums, 4 norm factors (chunk, head)
     int32_t wait_chunk;
     int32_t wait_head;
     int32_t pad[10];

@@ -13,7 +13,7 @@ namespace la {
 // ------------------------------------------------------------------- plan
 // Workgroup 0 (1024 threads): chunk counts per sequence, exclusive scan,
 // then each thread writes the chunk records of its sequences (none when
-// `chunks` is null: the lane kernel only needs the count).  The other
+// `chunks` is null: only the count is wanted).  The other
 // workgroups zero the words the MFMA prefills expect cleared on every call
 // (chunk-state flags and RMSNorm exchange words).
 constexpr int PLAN_THREADS = 1024;

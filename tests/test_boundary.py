@@ -84,16 +84,8 @@ def test_prefill_workspace_size(lib):
     slots = (64 + 1) * (128 // 64)
     need = 65 * 4 * 128 * 128 * 4 + slots * (4 * 64 * 8 + 1 * 64 * 8)
     assert need <= ops.prefill_workspace_size(8192, 1, 4, 128, 64, 0) < need + 65536
-    # -1: the lane kernel (sequences walked whole, 64 x 4 lanes), whose workspace is the
-    # plan header, a record per sequence and three exchange rings of 16 slots of 8-byte
-    # words: 256 lanes x 64 tokens, 16 groups x 64 tokens, 64 totals
-    lane = 16 * (256 * 64 + 16 * 64 + 64) * 8
-    assert lane <= ops.prefill_workspace_size(8192, 1, 64, 128, 64, -1) < lane + 65536
-    lane4 = 16 * (16 * 64 + 1 * 64 + 64) * 8
-    assert lane4 <= ops.prefill_workspace_size(8192, 1, 4, 128, 64, -1) < lane4 + 65536
-    assert ops.prefill_workspace_size(8192, 1, 128, 128, 64, -1) == 0  # 512 lanes > CUs
-    assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, -1, dtype=torch.float32) == 0
-    assert ops.prefill_workspace_size(8192, 1, 64, 64, 64, -1) == 0     # head_dim 64
+    # negative chunk sizes are refused
+    assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, -1) == 0
     assert ops.prefill_workspace_size(8192, 1, 64, 128, 64, -2) == 0
     ws32 = ops.prefill_workspace_size(8192, 1, 64, 128, 64, 1024, dtype=torch.float32)
     assert 9 * 64 * 128 * 128 * 4 <= ws32 < 9 * 64 * 128 * 128 * 4 + 65536
@@ -158,6 +150,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, eps=-1.0) == SHAPE
     assert _prefill(lib, eps=float("nan")) == SHAPE
     assert _prefill(lib, chunk=-64) == SHAPE
+    assert _prefill(lib, chunk=-1) == SHAPE
+    assert _prefill(lib, d=128, block=64, dtype=BF16, chunk=-1) == SHAPE
     assert _prefill(lib, ws_bytes=100) == WS
     # empty batch: valid, nothing to enqueue
     assert _prefill(lib, batch=0, q=None, k=None, v=None, g=None, w=None, out=None) == OK
@@ -175,6 +169,8 @@ def test_varlen_validation(lib):
     assert call(total=1 << 31) == SHAPE
     assert call(nseq=0, total=10) == SHAPE
     assert call(d=48) == UNSUP
+    assert lib.lightning_attn_prefill_varlen(A, A, A, A, A, A, A, 2, 100, None, None, 2, 64, 32,
+                                             -1, 1e-6, F32, A, 1 << 40, None) == SHAPE
     assert call(ws_bytes=64) == WS
     assert call(nseq=0, total=0, q=None, cu=None) == OK
 
@@ -187,7 +183,7 @@ def test_state_workspace_size(lib):
     st = ops.state_workspace_size(8192, 1, 64, 128, 64, 1024)
     # room for total / chunk + nseq chunks (a sequence's last chunk may be partial)
     assert 9 * 64 * 128 * 128 * 4 <= st < 9 * 64 * 128 * 128 * 4 + 65536
-    assert ops.state_workspace_size(8192, 1, 64, 128, 64, -1) == 0  # no lane variant
+    assert ops.state_workspace_size(8192, 1, 64, 128, 64, -1) == 0
     assert ops.state_workspace_size(8192, 1, 64, 96, 64, 0) == 0
     assert ops.state_workspace_size(8192, 1, 64, 128, 64, 100) == 0
     assert ops.state_workspace_size(0, 0, 64, 128, 64, 0) > 0

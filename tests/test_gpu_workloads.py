@@ -5,14 +5,14 @@ configuration bench.py times (the library's automatic chunk length), then
 compares what the fp64 oracle can compute in seconds:
 
   * prefill, 8192 tokens x 64 heads: every output and the final state, for the
-    automatic configuration and for the lane kernel; the state-only pass's
-    final state;
+    automatic configuration (2048-token chunks) and for 1024-token chunks;
+    the state-only pass's final state;
   * decode, 256 sequences x 64 heads, 64 steps: each step's outputs and the
     final states of four seeded sequences whose initial states the oracle
     built from their seeded prefixes;
   * varlen, 1,048,576 packed tokens (automatic chunks of 8192 tokens): every
     output and final state of three seeded sequences of at most 8192 tokens,
-    packed among the others (also for the lane kernel); every output and
+    packed among the others (also with 2048-token chunks); every output and
     final state, on all heads, of a seeded sequence of 16K-40K tokens (several
     chunks: the scanned states entering them); the longest sequence (about
     124K tokens, 16 chunks): its final state on four seeded heads and its
@@ -75,14 +75,15 @@ def put(dst, rows, heads, x):
 
 
 def test_prefill_8k_workload():
-    """The automatic configuration bench.py times, and the lane kernel (sequences
-    walked whole, chunk_tokens = -1), both against the oracle."""
+    """The automatic configuration bench.py times, and 1024-token chunks (eight
+    per sequence, 512 work items for 256 compute units), both against the
+    oracle."""
     N = 8192
     q, k, v, g, w = synth.layer_inputs(synth.PREFILL_8K, N, H, D, "minimax", threads=THREADS)
     say("prefill 8K: inputs ready")
     args = [dev(a, BF16).view(1, N, H, D) for a in (q, k, v, g)] + [dev(w, BF16)]
     runs = {}
-    for chunk in (0, -1):
+    for chunk in (0, 1024):
         say("prefill 8K: chunk_tokens", chunk)
         runs[chunk] = la.prefill(*args, return_final_state=True, chunk_tokens=chunk, check=True)
         torch.cuda.synchronize()
@@ -192,13 +193,13 @@ def test_varlen_1m_workload():
     fs_w = la.state(k[fa:fw].view(1, n0, H, D), v[fa:fw].view(1, n0, H, D), check=True)
     torch.cuda.synchronize()
     far_out, far_fs, fs_w = host(out[fw:fb]), host(fs[far:far + 1]), host(fs_w)
-    # the lane kernel on the same pack: only the sampled sequences are kept
-    say("varlen: lane kernel (chunk_tokens -1)")
-    out_l, fs_l = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True,
-                                    chunk_tokens=-1)
+    # 2048-token chunks on the same pack: only the sampled sequences are kept
+    say("varlen: chunk_tokens 2048")
+    out_c, fs_c = la.prefill_varlen(q, k, v, g, w, cu_dev, return_final_state=True,
+                                    chunk_tokens=2048, check=True)
     torch.cuda.synchronize()
-    lane = {s: (host(out_l[int(cu[s]):int(cu[s + 1])]), host(fs_l[s:s + 1])) for s in picks}
-    del q, k, v, g, out_l, fs_l
+    alt = {s: (host(out_c[int(cu[s]):int(cu[s + 1])]), host(fs_c[s:s + 1])) for s in picks}
+    del q, k, v, g, out_c, fs_c
     wh = np.ones(H * D, np.float32)
     for s in picks + [mid]:
         a, b = int(cu[s]), int(cu[s + 1])
@@ -207,9 +208,9 @@ def test_varlen_1m_workload():
         err = rel_state(host(fs[s:s + 1]), st)
         say("varlen sequence %d final state rel err %.2e" % (s, err))
         assert err < STATE_TOL
-        if s in lane:
-            check(lane[s][0], ref, BF16, "varlen sequence %d, lane kernel" % s)
-            assert rel_state(lane[s][1], st) < STATE_TOL
+        if s in alt:
+            check(alt[s][0], ref, BF16, "varlen sequence %d, 2048-token chunks" % s)
+            assert rel_state(alt[s][1], st) < STATE_TOL
     # the longest sequence: states on the four heads, then the last window from
     # the GPU's state entering it
     st_w = None
