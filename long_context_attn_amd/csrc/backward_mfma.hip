@@ -19,7 +19,10 @@
 //   dk  = anti-causal(SiLU v, dy, SiLU q; G_exit^T)    * SiLU'(k)
 //   dv  = anti-causal(SiLU k, SiLU q, dy; G_exit)      * SiLU'(v)
 // S_entry and G_exit come from chunk sums on MFMA (state_mfma.hip) and the
-// forward and reverse scans.
+// forward and reverse scans.  y and dq run as separate walks; dk and dv run
+// together in bwd_dkdv_mfma_kernel, which stages the four operands once for
+// both.  (y cannot share a walk with dq: dy needs the RMSNorm of y over all
+// heads first, which the forward walk finishes only several blocks later.)
 #include "mfma_common.h"
 
 namespace la {

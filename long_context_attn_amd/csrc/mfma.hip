@@ -47,8 +47,7 @@ constexpr int RGRP = 16;       // heads per sub-reducer group of the RMSNorm exc
 //
 // An item runs nblk + FIN iterations of two phases (barriers A and B).  Per
 // 64-token block j of the chunk (exchange slot s = c * slots_per_chunk + j):
-//   - iteration j: the producers stage Q~ (phase 1), K~ and V~ (phase 2),
-//     which splits their vector-ALU work about evenly between the phases;
+//   - iteration j: the producers stage Q~, K~ (phase 1) and V~ (phase 2);
 //   - iteration j + 1: the consumers compute S^T Q~^T and the scores (phase
 //     1), then V~^T P^T and the state update (phase 2); y is staged as bf16
 //     in LDS ring slot j % 3, sum_dv y^2 per token is reduced over the four
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
             const int buf = it & 1;
             const int b = it;  // block staged in this iteration
             // ---- phase 1: finalise block jf (its y in LDS, its norm factors
-            // left by wave 2 in the previous iteration), then stage q
+            // left by wave 2 in the previous iteration), then stage q and k
             const int jf = b - FIN;
             u32x4 od[4];  // stored output, kept live until barrier A
             if (jf >= 0 && jf < nblk) {
@@ -186,28 +185,28 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
             }
             load(gate, jf + 2, tg);  // finalised in iteration it + 2, same register set
             if (b < nblk) {
-                bf16x8 qs[4];
+                bf16x8 qs[4], ks[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) qs[r] = act8<ACT>(tq.r[r]);
+                for (int r = 0; r < 4; ++r) {
+                    qs[r] = act8<ACT>(tq.r[r]);
+                    ks[r] = act8<ACT>(tk.r[r]);
+                }
                 store_rows(qs, L.q[buf], cc, rg);
+                store_rows(ks, L.k[buf], cc, rg);
             }
             load(q, it + 2, tq);
+            load(k, it + 2, tk);
             __syncthreads();  // A
             if (jf >= 0 && jf < nblk)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) keep(od[r]);
-            // ---- phase 2: stage K~ and V~
+            // ---- phase 2: stage V~
             if (b < nblk) {
-                bf16x8 ks[4], vs[4];
+                bf16x8 vs[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ks[r] = act8<ACT>(tk.r[r]);
-                    vs[r] = act8<ACT>(tv.r[r]);
-                }
-                store_rows(ks, L.k[buf], cc, rg);
+                for (int r = 0; r < 4; ++r) vs[r] = act8<ACT>(tv.r[r]);
                 store_rows(vs, L.v[buf], cc, rg);
             }
-            load(k, it + 2, tk);
             load(v, it + 2, tv);
             __syncthreads();  // B
         };
