@@ -194,7 +194,8 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
         // output positions: token t = 32 tb + l32, dims 32 w + 8 q + 4 g .. + 3
         const int ooff = l32 * HD + 32 * w + 4 * g;
         // the raw inputs of the SiLU' factor, loaded ahead of the products
-        // (LEAN: at the end of phase 1, with fewer registers in use)
+        // (LEAN: after the products with the scores, when fewer registers are
+        // in use)
         bf16x4 rw[2][4];
         auto load_raw = [&]() {
             const __amdgpu_buffer_rsrc_t rr = tile_rsrc(raw + tbase, n, HD);
@@ -238,10 +239,6 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
                 }
             }
         }
-        if (EPI == 1 && LEAN && comp) {
-            __builtin_amdgcn_sched_barrier(0);  // not hoisted into the score products
-            load_raw();
-        }
         __syncthreads();  // A
         // ---- phase 2, iteration 0: the state entering the chunk
         if (it == 0) {
@@ -269,8 +266,7 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
                 pb[s][tb] = *reinterpret_cast<const bf16x8*>(sP + (32 * tb + l32) * BPP + 16 * s + 8 * g);
             };
             // K operands of the state update, KS token slices of 16 at a time
-            // (LEAN: read after the products with the scores, which take their
-            // P^T operands one output tile at a time)
+            // (LEAN: read after the products with the scores)
             constexpr int KS = LEAN ? 1 : 2;
             bf16x8 ko[KS][4];
 #pragma unroll
@@ -278,7 +274,7 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
                 vop[s] = ld_tr_operand(sV, 16 * s, 32 * w, lane);
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
-                    if (used(s, tb) && (!LEAN || tb == 0)) load_p(s, tb);
+                    if (used(s, tb)) load_p(s, tb);
             }
             if (!LEAN) {
 #pragma unroll
@@ -288,18 +284,11 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                if (LEAN && tb == 1) {
-#pragma unroll
-                    for (int s = 0; s < MB / 16; ++s)
-                        if (used(s, 1)) load_p(s, 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int s = 0; s < MB / 16; ++s)
                     if (used(s, tb)) O[tb] = mfma32(vop[s], pb[s][tb], O[tb]);
-            }
-            if (LEAN) __builtin_amdgcn_sched_barrier(0);  // P^T operands free before K's
+            if (EPI == 1 && LEAN) load_raw();
 #pragma unroll
             for (int s0 = 0; s0 < MB / 16; s0 += KS) {
                 if (LEAN || s0 > 0) {

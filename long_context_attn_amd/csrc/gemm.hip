@@ -20,7 +20,9 @@
 //     reads sit on distinct banks.
 // Tiles go from memory straight into LDS (buffer loads with the LDS as
 // destination, no registers) in GNS stages of GBK = 32 k: the loads of the
-// next GNS - 1 stages are in flight while the products of one stage run.
+// next GNS - 2 stages are in flight while the products of one stage run, and
+// the stage after it is complete, so its first operands are read from LDS
+// while this stage's last products run.
 // Measured at 8192 x 6144 x 32768 (the four input projections): 32-wide
 // stages in 4 buffers beat 64-wide ones in 2 by about 13%.
 // Wave w owns n in [128 (w & 1), +128) and m in [64 (w >> 1), +64) of the
@@ -40,12 +42,21 @@
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8
 #endif
+#ifndef GEMM_WAVES
+#define GEMM_WAVES 8
+#endif
+#ifndef GEMM_XPF
+#define GEMM_XPF 1
+#endif
 
 namespace la {
 
 namespace {
 
-constexpr int GT = 512;       // threads per workgroup (8 waves)
+constexpr int GW = GEMM_WAVES;  // waves per workgroup: 4 (128 x 128 each) or 8 (128 x 64)
+constexpr int GT = 64 * GW;     // threads per workgroup
+constexpr int WM = 512 / GW;    // tokens (m) per wave
+constexpr int NJ = WM / 32;     // 32-token accumulator tiles per wave
 constexpr int GBM = 256;      // m (tokens) per tile
 constexpr int GBN = 256;      // n (output features) per tile
 constexpr int GBK = GEMM_BK;  // k per LDS stage
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(GT) void gemm_bf16_kernel(const GemmParams a) {
     // physical chunk l of its rows with the logical chunk the swizzle puts
     // there.
     constexpr int XRPI = 1024 / (GBK * 2);  // X rows per load
-    constexpr int XLPW = GBK / 16;          // X loads per wave
+    constexpr int XLPW = GBM / XRPI / GW;   // X loads per wave (as many W loads)
     constexpr int WLPH = GBK / 4;           // W loads per half tile (4 rows each)
     auto stage = [&](int kt, auto bufc) {
         constexpr int BUF = decltype(bufc)::value;
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(GT) void gemm_bf16_kernel(const GemmParams a) {
     };
 
     const int wn = w & 1, wm = w >> 1;
-    f32x16 C[4][2] = {};
+    f32x16 C[4][NJ] = {};
     const int nk = a.K / GBK;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -191,48 +202,65 @@ __global__ __launch_bounds__(GT) void gemm_bf16_kernel(const GemmParams a) {
     // Step i issues the loads of stage i and computes stage i - (GNS - 1):
     // every load is issued inside the loop (loads issued before it, used only
     // by later passes, make the compiler drain every load at its top).  Each
-    // step waits for this wave's loads of the stage it computes (the later
-    // stages may still be in flight), then for everyone's; the barrier also
-    // frees the buffer the products of the previous step read, which this
-    // step's loads refill.  Past the last stage the last one is loaded again,
-    // so that every step has the same loads in flight.
+    // step waits for this wave's loads of the stage it computes and of the
+    // one after it (the later stages may still be in flight), then for
+    // everyone's; the barrier also frees the buffer the products of the
+    // previous step read, which this step's loads refill.  Past the last
+    // stage the last one is loaded again, so that every step has the same
+    // loads in flight.
+    // Operand sets (double-buffered over the 16-k slices of a stage): A from
+    // the W tile, B from the X tile of the stage in buffer SB.
+    constexpr int KS = GBK / 16;  // 16-k slices per stage
+    static_assert(KS % 2 == 0, "an even number of slices per stage");
+    bf16x8 A[2][4], B[2][NJ];
+    auto operands = [&](auto sbc, int s, int set) {
+        constexpr int SB = decltype(sbc)::value;
+        const __bf16* sw = stage_w<SB>() + wn * GWT;
+        const __bf16* sx = stage_x<SB>();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[set][i] = ld_tr_operand(sw, 16 * s, 32 * i, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            B[set][j] = *reinterpret_cast<const bf16x8*>(
+                sx + xswz(WM * wm + 32 * j + l32, 16 * s + 8 * g));
+    };
+    // With XPF, a step waits for one more stage (the one computed next) and
+    // reads that stage's first operands while its own last products run, so
+    // no step starts with a wait on LDS: the loads then run GNS - 2 stages
+    // ahead instead of GNS - 1.
+    constexpr bool XPF = GEMM_XPF != 0;
+    static_assert(!XPF || GNS >= 3, "the cross-stage operand read needs 3 stages");
     auto step = [&](int i, auto sc) {
         constexpr int S = decltype(sc)::value;  // buffer of stage i
         constexpr int SC = (S + 1) % GNS;       // buffer of stage i - (GNS - 1)
+        constexpr int SN = (S + 2) % GNS;       // buffer of the stage after it
         const int kc = i - (GNS - 1);           // stage computed
-        wait_vm<2 * XLPW * (GNS - 2)>();
+        wait_vm<2 * XLPW * (XPF ? GNS - 3 : GNS - 2)>();
         // a bare barrier: nothing but these loads needs ordering, and a
         // barrier with a fence would also wait for the later stages' loads
         __builtin_amdgcn_s_barrier();
         stage(min(i, nk - 1), sc);
-        if (kc < 0) return;
-        const __bf16* sw = stage_w<SC>() + wn * GWT;
-        const __bf16* sx = stage_x<SC>();
-        bf16x8 A[2][4], B[2][2];
-        auto operands = [&](int s, int set) {
+        if (kc < 0 || kc >= nk) return;
+        if (!XPF || kc == 0) operands(std::integral_constant<int, SC>{}, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) A[set][i] = ld_tr_operand(sw, 16 * s, 32 * i, lane);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                B[set][j] = *reinterpret_cast<const bf16x8*>(
-                    sx + xswz(64 * wm + 32 * j + l32, 16 * s + 8 * g));
-        };
-        operands(0, 0);
-#pragma unroll
-        for (int s = 0; s < GBK / 16; ++s) {
-            if (s + 1 < GBK / 16) operands(s + 1, (s + 1) & 1);
+        for (int s = 0; s < KS; ++s) {
+            if (s + 1 < KS) operands(std::integral_constant<int, SC>{}, s + 1, (s + 1) & 1);
+            else if (XPF && kc + 1 < nk) operands(std::integral_constant<int, SN>{}, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) C[i][j] = mfma32(A[s & 1][i], B[s & 1][j], C[i][j]);
+                for (int j = 0; j < NJ; ++j) C[i][j] = mfma32(A[s & 1][i], B[s & 1][j], C[i][j]);
         }
     };
+    // whole passes of GNS steps (the steps past the last computed stage only
+    // load): with no step skipped inside a pass, the compiler sees the same
+    // loads in flight on every path and keeps its waits partial
     const int steps = nk + GNS - 1;
     for (int i = 0; i < steps; i += GNS) {
         step(i, I0{});
-        if (i + 1 < steps) step(i + 1, I1{});
-        if constexpr (GNS > 2) if (i + 2 < steps) step(i + 2, I2{});
-        if constexpr (GNS > 3) if (i + 3 < steps) step(i + 3, I3{});
+        step(i + 1, I1{});
+        if constexpr (GNS > 2) step(i + 2, I2{});
+        if constexpr (GNS > 3) step(i + 3, I3{});
     }
     wait_vm<0>();
 
@@ -243,11 +271,11 @@ __global__ __launch_bounds__(GT) void gemm_bf16_kernel(const GemmParams a) {
     const unsigned act = (a.acts >> (2 * p)) & 3u;
     __bf16* yp = a.y + p * a.ystride;
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 data[4][2][4];
+    u32x2 data[4][NJ][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 data[i][j][q] = u32x2{
@@ -255,8 +283,8 @@ __global__ __launch_bounds__(GT) void gemm_bf16_kernel(const GemmParams a) {
                     pack_bf16(gemm_act(C[i][j][4 * q + 2], act), gemm_act(C[i][j][4 * q + 3], act))};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = m0 + 64 * wm + 32 * j + l32;
+    for (int j = 0; j < NJ; ++j) {
+        const int m = m0 + WM * wm + 32 * j + l32;
         if (m < a.M) {
             __bf16* row = yp + (int64_t)m * a.ldy;
 #pragma unroll
@@ -271,7 +299,7 @@ __global__ __launch_bounds__(GT) void gemm_bf16_kernel(const GemmParams a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(data[i][j][q]));
 }
