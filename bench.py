@@ -20,7 +20,8 @@ kernels on the stream they run on: the chunk sums, the scan of the states
 entering the chunks, and the walk with the RMSNorm fused), the roofline of
 the walk kernel and the whole call's HBM fraction, the state-only pass on the
 same K and V, the
-backward pass on the same inputs (time per call against its HBM bytes), the
+backward pass on the same inputs (time per call against its HBM bytes; also
+from the activations a prefill saved, and that prefill's time), the
 layer with its projections (hidden 6144: four input GEMMs with SiLU in the
 epilogue, the attention, the output GEMM) as time per call, the hybrid's
 softmax attention layer on the same shape (rotary embedding on half of the
@@ -292,7 +293,45 @@ def bench_backward(args, la, torch, inputs):
                tokens_per_s=round(B * N / (us * 1e-6), 1), algorithmic_bytes=nbytes,
                hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
     log("backward: %.1f us/call (%.2f%% of the HBM roofline)" % (us, 100 * res["hbm_frac"]))
-    del x, dout, ws
+
+    # the training order: a prefill that saves y and the chunk states, then
+    # the backward from them (the same algorithmic bytes)
+    pws = torch.empty(la.prefill_workspace_size(B * N, B, H, D, cfg["block"], 0),
+                      dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x[0])
+    saved = torch.empty(la.saved_size(B * N, B, H, D, cfg["block"], 0), dtype=torch.uint8,
+                        device="cuda")
+
+    def timed(fn, n):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(n):
+            fn()
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / n
+
+    fwd = lambda: la.prefill(*x, wd, block=cfg["block"], eps=cfg["eps"], out=out, workspace=pws)
+    fwd_save = lambda: la.prefill(*x, wd, block=cfg["block"], eps=cfg["eps"], out=out,
+                                  workspace=pws, save_for_backward=True, saved=saved)
+    bwd_saved = lambda: la.backward(*x, wd, dout, block=cfg["block"], eps=cfg["eps"],
+                                    workspace=ws, saved=saved)
+    us_fwd = timed(fwd, n)
+    us_fwd_save = timed(fwd_save, n)
+    us_saved = timed(bwd_saved, n)
+    res["from_saved"] = dict(
+        us_per_call=round(us_saved, 1), hbm_frac=round(nbytes / (us_saved * 1e-6) / 1e9 /
+                                                       HBM_PEAK_GBS, 4),
+        prefill_us=round(us_fwd, 1), prefill_saving_us=round(us_fwd_save, 1),
+        saved_bytes=int(saved.numel()))
+    log("backward from saved activations: %.1f us/call (%.2f%% of the HBM roofline); the "
+        "prefill that saves them %.1f us against %.1f" % (us_saved, 100 * res["from_saved"]["hbm_frac"],
+                                                          us_fwd_save, us_fwd))
+    del x, dout, ws, pws, out, saved
     return res
 
 

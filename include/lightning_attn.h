@@ -242,6 +242,61 @@ LA_API la_status lightning_attn_backward_varlen(
     hipStream_t stream);
 
 /*
+ * Activations saved by a prefill for its backward pass (training: the
+ * forward runs first anyway).  The backward above recomputes y = q~ S, the
+ * attention output before the norm, and the states S entering the chunks,
+ * from q, k, v: one pass of chunk sums of k~^T v~, a scan, and one walk.  A
+ * prefill can keep both instead, and the backward then starts from them:
+ *   saved: y, the dtype of q, [total_tokens][heads][head_dim], then (16-byte
+ *          aligned) the fp32 state entering every chunk,
+ *          [max_chunks][heads][head_dim][head_dim] (the initial state
+ *          included), in the chunk layout both calls derive from the same
+ *          (total_tokens, nseq, heads, head_dim, block, chunk_tokens).
+ * The prefill's outputs are the same bits as lightning_attn_prefill's; the
+ * backward's gradients are those of lightning_attn_backward (y read instead
+ * of recomputed: the same bf16 values up to the rounding of the last bit).
+ * The buffer is owned by the caller, written by the prefill and only read by
+ * the backward, which must get the same q, k, v, gate, norm_weight, eps,
+ * initial_state, chunk_tokens and shapes as the prefill that wrote it.
+ * Only the fused bf16 MFMA path saves (bf16, head_dim 128, block 64, heads at
+ * most the device's compute units): elsewhere lightning_attn_saved_size
+ * returns 0 and the calls return LA_ERR_UNSUPPORTED.  A buffer smaller than
+ * lightning_attn_saved_size returns LA_ERR_WORKSPACE_TOO_SMALL; a null one
+ * LA_ERR_NULL_POINTER.  Other arguments, workspaces and errors as for
+ * lightning_attn_prefill(_varlen) and lightning_attn_backward(_varlen).
+ */
+LA_API size_t lightning_attn_saved_size(int64_t total_tokens, int nseq, int heads, int head_dim,
+                                        int block, int chunk_tokens, la_dtype dtype);
+LA_API la_status lightning_attn_prefill_save(const void* q, const void* k, const void* v,
+                                             const void* gate, const void* norm_weight, void* out,
+                                             const float* initial_state, float* final_state,
+                                             int batch, int64_t seqlen, int heads, int head_dim,
+                                             int block, int chunk_tokens, float eps,
+                                             la_dtype dtype, void* saved, size_t saved_bytes,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+LA_API la_status lightning_attn_prefill_varlen_save(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    void* out, const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+    const float* initial_state, float* final_state, int heads, int head_dim, int block,
+    int chunk_tokens, float eps, la_dtype dtype, void* saved, size_t saved_bytes,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+LA_API la_status lightning_attn_backward_saved(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    const void* dout, const float* initial_state, const float* d_final_state, void* dq, void* dk,
+    void* dv, void* dgate, float* dweight, float* d_initial_state, int batch, int64_t seqlen,
+    int heads, int head_dim, int block, int chunk_tokens, float eps, la_dtype dtype,
+    const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
+LA_API la_status lightning_attn_backward_varlen_saved(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    const void* dout, const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+    const float* initial_state, const float* d_final_state, void* dq, void* dk, void* dv,
+    void* dgate, float* dweight, float* d_initial_state, int heads, int head_dim, int block,
+    int chunk_tokens, float eps, la_dtype dtype, const void* saved, size_t saved_bytes,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The whole layer on a batch of B rows of N tokens, with the projections on
  * either side of the attention (Mechanism step 1: q, k, v and the gate are
  * linear maps of the layer input; the output is mapped back to the hidden

@@ -173,6 +173,45 @@ bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block
     return true;
 }
 
+// Activations a prefill keeps for lightning_attn_backward_saved: y (the
+// attention output before the norm, bf16 [total][H][D]) and then the fp32
+// state entering every chunk ([max_chunks][H][D][D]), in the chunk layout that
+// both passes derive from the same arguments.  Only the fused bf16 MFMA path
+// (head_dim 128, block 64, heads <= CUs) saves them.
+struct SavedLayout {
+    int chunk = 0, max_chunks = 0;
+    size_t off_states = 0, bytes = 0;
+};
+
+bool saved_layout(int64_t total, int nseq, int heads, int head_dim, int block, int chunk_tokens,
+                  la_dtype dtype, SavedLayout* S) {
+    if (!fused_path(head_dim, block, dtype)) return false;
+    Layout L;
+    if (!plan_layout(total, nseq, heads, head_dim, block, chunk_tokens, true, &L) || !L.fused)
+        return false;
+    BwdLayout B;
+    if (!backward_layout(total, nseq, heads, head_dim, block, chunk_tokens, dtype, &B) ||
+        !B.mfma || B.chunk != L.chunk || B.max_chunks != L.max_chunks)
+        return false;
+    S->chunk = L.chunk;
+    S->max_chunks = L.max_chunks;
+    S->off_states = align_up(sizeof(uint16_t) * (size_t)total * heads * head_dim);
+    S->bytes = S->off_states + sizeof(float) * (size_t)L.max_chunks * heads * head_dim * head_dim;
+    return true;
+}
+
+// Checks a saved-activations buffer for a call with these arguments.
+la_status check_saved(const void* saved, size_t saved_bytes, int64_t total, int nseq, int heads,
+                      int head_dim, int block, int chunk_tokens, la_dtype dtype,
+                      SavedLayout* S) {
+    if (!saved_layout(total, nseq, heads, head_dim, block, chunk_tokens, dtype, S))
+        return LA_ERR_UNSUPPORTED;
+    if (!saved) return LA_ERR_NULL_POINTER;
+    if (!aligned16(saved)) return LA_ERR_MISALIGNED;
+    if (saved_bytes < S->bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    return LA_OK;
+}
+
 la_status check_dtype(la_dtype dtype) {
     return (dtype == LA_DTYPE_F32 || dtype == LA_DTYPE_BF16) ? LA_OK : LA_ERR_UNSUPPORTED;
 }
@@ -201,7 +240,8 @@ la_status run_prefill(la::PrefillArgs& a, const Layout& L, void* workspace, hipS
     a.hdr = reinterpret_cast<la::PlanHeader*>(ws);
     a.segs = reinterpret_cast<la::SegEntry*>(ws + L.off_segs);
     a.chunks = reinterpret_cast<la::ChunkEntry*>(ws + L.off_chunks);
-    a.states = reinterpret_cast<float*>(ws + L.off_states);
+    // (states already set: the caller keeps them, in a saved-activations buffer)
+    if (a.states == nullptr) a.states = reinterpret_cast<float*>(ws + L.off_states);
     // the layout decided the kernels: the fused MFMA walk needs its exchange
     // words, which only a fused layout holds
     const bool mfma = L.fused && la::mfma_supported(a);
@@ -386,7 +426,8 @@ static la_status prefill_impl(const void* q, const void* k, const void* v, const
                               float* final_state, int batch, int64_t seqlen, int heads,
                               int head_dim, int block, int chunk_tokens, float eps,
                               la_dtype dtype, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, Marks marks) {
+                              hipStream_t stream, Marks marks, void* saved = nullptr,
+                              size_t saved_bytes = 0, bool save = false) {
     if (batch < 0 || seqlen < 0 || heads < 1 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
     if (chunk_tokens < 0) return LA_ERR_BAD_SHAPE;
     if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
@@ -406,8 +447,18 @@ static la_status prefill_impl(const void* q, const void* k, const void* v, const
     if (!workspace) return LA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
     if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    SavedLayout S;
+    if (save) {
+        const la_status st = check_saved(saved, saved_bytes, total, batch, heads, head_dim, block,
+                                         chunk_tokens, dtype, &S);
+        if (st != LA_OK) return st;
+    }
     if (batch == 0) return LA_OK;
     la::PrefillArgs a{};
+    if (save) {
+        a.y_save = saved;
+        a.states = reinterpret_cast<float*>(static_cast<char*>(saved) + S.off_states);
+    }
     a.q = q; a.k = k; a.v = v; a.g = gate; a.w = norm_weight; a.out = out;
     a.init_state = initial_state;
     a.final_state = final_state;
@@ -459,13 +510,14 @@ const char* lightning_attn_decode_stage_name(int stage) {
     return (stage >= 0 && stage < kDecodeStageCount) ? kDecodeStages[stage] : nullptr;
 }
 
-la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void* v,
-                                        const void* gate, const void* norm_weight, void* out,
-                                        const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
-                                        const float* initial_state, float* final_state, int heads,
-                                        int head_dim, int block, int chunk_tokens, float eps,
-                                        la_dtype dtype, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
+static la_status prefill_varlen_impl(const void* q, const void* k, const void* v,
+                                     const void* gate, const void* norm_weight, void* out,
+                                     const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+                                     const float* initial_state, float* final_state, int heads,
+                                     int head_dim, int block, int chunk_tokens, float eps,
+                                     la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream, void* saved, size_t saved_bytes,
+                                     bool save) {
     if (nseq < 0 || total_tokens < 0 || total_tokens > 0x7fffffffLL || heads < 1 ||
         !(eps >= 0.0f) || chunk_tokens < 0)
         return LA_ERR_BAD_SHAPE;
@@ -487,8 +539,18 @@ la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void
     if (!workspace) return LA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
     if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    SavedLayout S;
+    if (save) {
+        const la_status st = check_saved(saved, saved_bytes, total_tokens, nseq, heads, head_dim,
+                                         block, chunk_tokens, dtype, &S);
+        if (st != LA_OK) return st;
+    }
     if (nseq == 0) return LA_OK;
     la::PrefillArgs a{};
+    if (save) {
+        a.y_save = saved;
+        a.states = reinterpret_cast<float*>(static_cast<char*>(saved) + S.off_states);
+    }
     a.q = q; a.k = k; a.v = v; a.g = gate; a.w = norm_weight; a.out = out;
     a.init_state = initial_state;
     a.final_state = final_state;
@@ -500,6 +562,51 @@ la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void
     a.eps = eps;
     a.bf16 = dtype == LA_DTYPE_BF16;
     return run_prefill(a, L, workspace, stream);
+}
+
+la_status lightning_attn_prefill_varlen(const void* q, const void* k, const void* v,
+                                        const void* gate, const void* norm_weight, void* out,
+                                        const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+                                        const float* initial_state, float* final_state, int heads,
+                                        int head_dim, int block, int chunk_tokens, float eps,
+                                        la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    return prefill_varlen_impl(q, k, v, gate, norm_weight, out, cu_seqlens, nseq, total_tokens,
+                               initial_state, final_state, heads, head_dim, block, chunk_tokens,
+                               eps, dtype, workspace, workspace_bytes, stream, nullptr, 0, false);
+}
+
+size_t lightning_attn_saved_size(int64_t total_tokens, int nseq, int heads, int head_dim,
+                                 int block, int chunk_tokens, la_dtype dtype) {
+    if (check_dtype(dtype) != LA_OK || chunk_tokens < 0) return 0;
+    SavedLayout S;
+    if (!saved_layout(total_tokens, nseq, heads, head_dim, block, chunk_tokens, dtype, &S))
+        return 0;
+    return S.bytes;
+}
+
+la_status lightning_attn_prefill_save(const void* q, const void* k, const void* v,
+                                      const void* gate, const void* norm_weight, void* out,
+                                      const float* initial_state, float* final_state, int batch,
+                                      int64_t seqlen, int heads, int head_dim, int block,
+                                      int chunk_tokens, float eps, la_dtype dtype, void* saved,
+                                      size_t saved_bytes, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return prefill_impl(q, k, v, gate, norm_weight, out, initial_state, final_state, batch, seqlen,
+                        heads, head_dim, block, chunk_tokens, eps, dtype, workspace,
+                        workspace_bytes, stream, Marks(), saved, saved_bytes, true);
+}
+
+la_status lightning_attn_prefill_varlen_save(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    void* out, const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+    const float* initial_state, float* final_state, int heads, int head_dim, int block,
+    int chunk_tokens, float eps, la_dtype dtype, void* saved, size_t saved_bytes,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return prefill_varlen_impl(q, k, v, gate, norm_weight, out, cu_seqlens, nseq, total_tokens,
+                               initial_state, final_state, heads, head_dim, block, chunk_tokens,
+                               eps, dtype, workspace, workspace_bytes, stream, saved, saved_bytes,
+                               true);
 }
 
 size_t lightning_attn_state_workspace_size(int64_t total_tokens, int nseq, int heads,
@@ -624,7 +731,9 @@ static la_status backward_impl(const void* q, const void* k, const void* v, cons
                                float* d_initial_state, const int32_t* cu, int nseq,
                                int64_t seqlen, int64_t total, int heads, int head_dim, int block,
                                int chunk_tokens, float eps, la_dtype dtype, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               size_t workspace_bytes, hipStream_t stream,
+                               const void* saved = nullptr, size_t saved_bytes = 0,
+                               bool use_saved = false) {
     if (heads < 1 || chunk_tokens < 0 || !(eps >= 0.0f)) return LA_ERR_BAD_SHAPE;
     if (check_dtype(dtype) != LA_OK || !supported_dim(head_dim) || !supported_block(block))
         return LA_ERR_UNSUPPORTED;
@@ -645,6 +754,12 @@ static la_status backward_impl(const void* q, const void* k, const void* v, cons
     if (!workspace) return LA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return LA_ERR_MISALIGNED;
     if (workspace_bytes < L.bytes) return LA_ERR_WORKSPACE_TOO_SMALL;
+    SavedLayout S;
+    if (use_saved) {
+        const la_status st = check_saved(saved, saved_bytes, total, nseq, heads, head_dim, block,
+                                         chunk_tokens, dtype, &S);
+        if (st != LA_OK) return st;
+    }
     if (nseq == 0) return LA_OK;
     char* ws = static_cast<char*>(workspace);
     la::BackwardArgs a{};
@@ -678,6 +793,13 @@ static la_status backward_impl(const void* q, const void* k, const void* v, cons
         a.vs = reinterpret_cast<float*>(ws + L.off_vs);
     }
     a.y = reinterpret_cast<float*>(ws + L.off_y);
+    if (use_saved) {
+        // y and the states entering the chunks come from the prefill
+        a.saved = true;
+        a.y = static_cast<float*>(const_cast<void*>(saved));
+        p.states = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(saved)) +
+                                            S.off_states);
+    }
     a.dy = ws + L.off_dy;
     a.dw_part = reinterpret_cast<float*>(ws + L.off_dw);
     a.n_tb = L.n_tb;
@@ -717,6 +839,38 @@ la_status lightning_attn_backward_varlen(
                          dv, dgate, dweight, d_initial_state, cu_seqlens, nseq, 0, total_tokens,
                          heads, head_dim, block, chunk_tokens, eps, dtype, workspace,
                          workspace_bytes, stream);
+}
+
+la_status lightning_attn_backward_saved(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    const void* dout, const float* initial_state, const float* d_final_state, void* dq, void* dk,
+    void* dv, void* dgate, float* dweight, float* d_initial_state, int batch, int64_t seqlen,
+    int heads, int head_dim, int block, int chunk_tokens, float eps, la_dtype dtype,
+    const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+    if (batch < 0 || seqlen < 0) return LA_ERR_BAD_SHAPE;
+    if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return LA_ERR_BAD_SHAPE;
+    return backward_impl(q, k, v, gate, norm_weight, dout, initial_state, d_final_state, dq, dk,
+                         dv, dgate, dweight, d_initial_state, nullptr, batch, seqlen,
+                         (int64_t)batch * seqlen, heads, head_dim, block, chunk_tokens, eps, dtype,
+                         workspace, workspace_bytes, stream, saved, saved_bytes, true);
+}
+
+la_status lightning_attn_backward_varlen_saved(
+    const void* q, const void* k, const void* v, const void* gate, const void* norm_weight,
+    const void* dout, const int32_t* cu_seqlens, int nseq, int64_t total_tokens,
+    const float* initial_state, const float* d_final_state, void* dq, void* dk, void* dv,
+    void* dgate, float* dweight, float* d_initial_state, int heads, int head_dim, int block,
+    int chunk_tokens, float eps, la_dtype dtype, const void* saved, size_t saved_bytes,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (nseq < 0 || total_tokens < 0 || total_tokens > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
+    if (nseq == 0 && total_tokens != 0) return LA_ERR_BAD_SHAPE;
+    if (nseq > 0 && !cu_seqlens) return LA_ERR_NULL_POINTER;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return LA_ERR_MISALIGNED;
+    return backward_impl(q, k, v, gate, norm_weight, dout, initial_state, d_final_state, dq, dk,
+                         dv, dgate, dweight, d_initial_state, cu_seqlens, nseq, 0, total_tokens,
+                         heads, head_dim, block, chunk_tokens, eps, dtype, workspace,
+                         workspace_bytes, stream, saved, saved_bytes, true);
 }
 
 // Layer workspace: the prefill's (automatic chunks), then SiLU(q), SiLU(k),

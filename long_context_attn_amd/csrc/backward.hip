@@ -447,15 +447,17 @@ hipError_t backward_mfma(const BackwardArgs& a) {
     const PrefillArgs& p = a.p;
     hipStream_t st = a.stream;
     const int HD = p.H * p.D;
-    hipError_t e = launch_chunk_sums_mfma(p, p.k, p.v, true, true, p.states, SumSkip::last, st);
-    if (e != hipSuccess) return e;
-    {
+    hipError_t e = hipSuccess;
+    if (!a.saved) {
+        if ((e = launch_chunk_sums_mfma(p, p.k, p.v, true, true, p.states, SumSkip::last, st)) !=
+            hipSuccess)
+            return e;
         PrefillArgs s = p;
         s.final_state = nullptr;
         s.skip_last = true;
         if ((e = launch_state_scan(s, st)) != hipSuccess) return e;
+        if ((e = launch_backward_walk_y(a)) != hipSuccess) return e;
     }
-    if ((e = launch_backward_walk_y(a)) != hipSuccess) return e;
     if ((e = norm_backward<__bf16, __bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
     if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
     // each sequence's first chunk sum only feeds dS0

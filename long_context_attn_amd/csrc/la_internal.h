@@ -66,6 +66,9 @@ struct PrefillArgs {
     bool preact;
     // with preact: the gate holds sigmoid(gate) already (else it is raw)
     bool gate_act;
+    // MFMA walk: also store y, the attention output before the norm (bf16,
+    // [total][H][D]), for a later backward pass; null = not stored
+    void* y_save;
     // MFMA prefill of uniform rows (cu == null): no plan kernel; the chunk-sum
     // kernel computes its chunks from (nseq, seqlen, chunk), and extra
     // workgroups of it write the plan tables, reset the header and clear the
@@ -128,6 +131,9 @@ struct BackwardArgs {
     void* dy;
     int n_tb;
     bool mfma;
+    // y and the states entering the chunks (p.states) come from the prefill
+    // (MFMA path): no chunk sums of k~^T v~, scan or y walk
+    bool saved;
 };
 int64_t backward_norm_tokens(int64_t total);  // tokens per dw partial sum row
 int backward_dw_slices();     // extra dw rows for the second reduction level

@@ -89,7 +89,7 @@ template <bool ACT, bool GSIG>
 __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ gate, const __bf16* __restrict__ wgt, __bf16* __restrict__ out,
-    PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
+    __bf16* __restrict__ y_save, PlanHeader* __restrict__ hdr, const SegEntry* __restrict__ segs,
     const ChunkEntry* __restrict__ chunks, const float* __restrict__ init_state,
     float* __restrict__ final_state, const float* __restrict__ entry,
     uint64_t* __restrict__ part, uint64_t* __restrict__ rsub, int H, int nseq,
@@ -154,6 +154,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
             // left by wave 2 in the previous iteration), then stage q and k
             const int jf = b - FIN;
             u32x4 od[4];  // stored output, kept live until barrier A
+            u32x4 oy[4];  // stored y (y_save), likewise
             if (jf >= 0 && jf < nblk) {
                 // All LDS reads come before the first output store (their
                 // results must not land in registers a store is reading).
@@ -182,6 +183,15 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
                     od[r] = __builtin_bit_cast(u32x4, o[r]);
                     __builtin_amdgcn_raw_buffer_store_b128(od[r], ro, voff, r * rstride, NT);
                 }
+                if (y_save != nullptr) {
+                    const __amdgpu_buffer_rsrc_t ry =
+                        tile_rsrc(y_save + off0 + (int64_t)jf * MB * HD, rows(jf), HD);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        oy[r] = __builtin_bit_cast(u32x4, y[r]);
+                        __builtin_amdgcn_raw_buffer_store_b128(oy[r], ry, voff, r * rstride, NT);
+                    }
+                }
             }
             load(gate, jf + 2, tg);  // finalised in iteration it + 2, same register set
             if (b < nblk) {
@@ -197,9 +207,13 @@ __global__ __launch_bounds__(NTHREADS) void prefill_mfma_kernel(
             load(q, it + 2, tq);
             load(k, it + 2, tk);
             __syncthreads();  // A
-            if (jf >= 0 && jf < nblk)
+            if (jf >= 0 && jf < nblk) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) keep(od[r]);
+                if (y_save != nullptr)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) keep(oy[r]);
+            }
             // ---- phase 2: stage V~
             if (b < nblk) {
                 bf16x8 vs[4];
@@ -446,7 +460,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
                         : &prefill_mfma_kernel<true, true>;
     hipLaunchKernelGGL(fn, grid, dim3(NTHREADS), 0, st, (const __bf16*)a.q, (const __bf16*)a.k,
                        (const __bf16*)a.v, (const __bf16*)a.g, (const __bf16*)a.w, (__bf16*)a.out,
-                       a.hdr, a.segs, a.chunks, a.init_state, a.final_state, a.states, a.part,
+                       (__bf16*)a.y_save, a.hdr, a.segs, a.chunks, a.init_state, a.final_state, a.states, a.part,
                        a.rsub, a.H, a.nseq, a.chunk / MB, a.eps);
     return hipGetLastError();
 }

@@ -79,6 +79,22 @@ def library():
         lib.lightning_attn_backward_varlen.argtypes = ([_P] * 7 + [_I, _I64] + [_P] * 8 +
                                                        [_I, _I, _I, _I, _F, _I, _P, _SZ, _P])
         lib.lightning_attn_backward_varlen.restype = _I
+        lib.lightning_attn_saved_size.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        lib.lightning_attn_saved_size.restype = _SZ
+        lib.lightning_attn_prefill_save.argtypes = [_P] * 8 + [_I, _I64, _I, _I, _I, _I, _F, _I,
+                                                               _P, _SZ, _P, _SZ, _P]
+        lib.lightning_attn_prefill_save.restype = _I
+        lib.lightning_attn_prefill_varlen_save.argtypes = ([_P] * 7 + [_I, _I64, _P, _P] +
+                                                           [_I, _I, _I, _I, _F, _I, _P, _SZ, _P,
+                                                            _SZ, _P])
+        lib.lightning_attn_prefill_varlen_save.restype = _I
+        lib.lightning_attn_backward_saved.argtypes = ([_P] * 14 + [_I, _I64, _I, _I, _I, _I, _F,
+                                                                   _I, _P, _SZ, _P, _SZ, _P])
+        lib.lightning_attn_backward_saved.restype = _I
+        lib.lightning_attn_backward_varlen_saved.argtypes = ([_P] * 7 + [_I, _I64] + [_P] * 8 +
+                                                             [_I, _I, _I, _I, _F, _I, _P, _SZ, _P,
+                                                              _SZ, _P])
+        lib.lightning_attn_backward_varlen_saved.restype = _I
         lib.lightning_attn_layer_workspace_size.argtypes = [_I64, _I, _I, _I, _I]
         lib.lightning_attn_layer_workspace_size.restype = _SZ
         lib.lightning_attn_layer_prefill.argtypes = [_P] * 7 + [_I, _I64, _I, _I, _I, _I, _F, _P,
@@ -215,14 +231,31 @@ def _workspace(nbytes, device, given):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+def saved_size(total_tokens, nseq, heads, head_dim, block=64, chunk_tokens=0,
+               dtype=torch.bfloat16) -> int:
+    """Bytes of the activations a prefill saves for its backward (0 where the
+    path does not save: only bf16, head_dim 128, block 64)."""
+    return int(library().lightning_attn_saved_size(
+        int(total_tokens), int(nseq), int(heads), int(head_dim), int(block), int(chunk_tokens),
+        LA_DTYPE[dtype]))
+
+
+def _saved_buffer(nbytes, device, given):
+    if nbytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    return _workspace(nbytes, device, given)
+
+
 def prefill(q, k, v, gate, weight, *, block=64, eps=1e-6, initial_state=None,
             return_final_state=False, chunk_tokens=0, out=None, final_state=None,
-            workspace=None, check=None):
+            workspace=None, check=None, save_for_backward=False, saved=None):
     """Causal Lightning Attention prefill of B rows of N tokens.
 
     q, k, v, gate: [B, N, H, D] (float32 or bfloat16, contiguous, one device);
     weight: [H*D]; initial_state: [B, H, D, D] float32 or None (zeros).
     Returns out [B, N, H, D] (and the final state [B, H, D, D] if requested).
+    With save_for_backward, also returns (last) the saved activations (a uint8
+    tensor, or `saved` filled in place) for backward(..., saved=...).
     """
     _same(q, k, v, gate, weight)
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or gate.shape != q.shape:
@@ -243,21 +276,33 @@ def prefill(q, k, v, gate, weight, *, block=64, eps=1e-6, initial_state=None,
     if ws_bytes == 0:
         raise LightningAttnError(3, status_string(3))
     ws = _workspace(ws_bytes, dev, workspace)
-    _check(library().lightning_attn_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(init), _ptr(fs),
-        B, N, H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes,
-        _stream(dev)))
+    if save_for_backward:
+        sv_bytes = saved_size(B * N, B, H, D, block, chunk_tokens, q.dtype)
+        sv = _saved_buffer(sv_bytes, dev, saved)
+        _check(library().lightning_attn_prefill_save(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(init), _ptr(fs),
+            B, N, H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(sv), sv_bytes,
+            _ptr(ws), ws_bytes, _stream(dev)))
+    else:
+        _check(library().lightning_attn_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(init), _ptr(fs),
+            B, N, H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes,
+            _stream(dev)))
     _check_device(ws, check)
-    return (out, fs) if return_final_state else out
+    res = (out, fs) if return_final_state else (out,)
+    if save_for_backward:
+        res = res + (sv,)
+    return res if len(res) > 1 else res[0]
 
 
 def prefill_varlen(q, k, v, gate, weight, cu_seqlens, *, block=64, eps=1e-6, initial_state=None,
                    return_final_state=False, chunk_tokens=0, out=None, final_state=None,
-                   workspace=None, check=None):
+                   workspace=None, check=None, save_for_backward=False, saved=None):
     """Causal prefill of sequences packed back to back.
 
     q, k, v, gate: [T, H, D]; cu_seqlens: int32 [nseq+1] on the same device
     (0 = cu[0] <= ... <= cu[nseq] = T); initial_state: [nseq, H, D, D] or None.
+    save_for_backward / saved: as for `prefill`.
     """
     _same(q, k, v, gate, weight)
     if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or gate.shape != q.shape:
@@ -284,12 +329,23 @@ def prefill_varlen(q, k, v, gate, weight, cu_seqlens, *, block=64, eps=1e-6, ini
     if ws_bytes == 0:
         raise LightningAttnError(3, status_string(3))
     ws = _workspace(ws_bytes, dev, workspace)
-    _check(library().lightning_attn_prefill_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(cu_seqlens), nseq,
-        T, _ptr(init), _ptr(fs), H, D, int(block), int(chunk_tokens), float(eps), _dtype(q),
-        _ptr(ws), ws_bytes, _stream(dev)))
+    if save_for_backward:
+        sv_bytes = saved_size(T, nseq, H, D, block, chunk_tokens, q.dtype)
+        sv = _saved_buffer(sv_bytes, dev, saved)
+        _check(library().lightning_attn_prefill_varlen_save(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(cu_seqlens),
+            nseq, T, _ptr(init), _ptr(fs), H, D, int(block), int(chunk_tokens), float(eps),
+            _dtype(q), _ptr(sv), sv_bytes, _ptr(ws), ws_bytes, _stream(dev)))
+    else:
+        _check(library().lightning_attn_prefill_varlen(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(out), _ptr(cu_seqlens),
+            nseq, T, _ptr(init), _ptr(fs), H, D, int(block), int(chunk_tokens), float(eps),
+            _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
     _check_device(ws, check)
-    return (out, fs) if return_final_state else out
+    res = (out, fs) if return_final_state else (out,)
+    if save_for_backward:
+        res = res + (sv,)
+    return res if len(res) > 1 else res[0]
 
 
 def state_workspace_size(total_tokens, nseq, heads, head_dim, block=64, chunk_tokens=0,
@@ -368,13 +424,27 @@ def _backward_outputs(q, nseq, H, D, want_d_init):
     return grads, dw, d_init
 
 
+def _saved_arg(saved, nbytes, device):
+    if not isinstance(saved, torch.Tensor) or saved.dtype != torch.uint8 or \
+            not saved.is_contiguous() or saved.device != device:
+        raise ValueError("saved must be the uint8 tensor a prefill with save_for_backward returned "
+                         "(contiguous, on the activations' device)")
+    if nbytes == 0:
+        raise LightningAttnError(3, status_string(3))
+    if saved.numel() < nbytes:
+        raise ValueError("saved too small: need %d bytes" % nbytes)
+    return saved, saved.numel()
+
+
 def backward(q, k, v, gate, weight, dout, *, block=64, eps=1e-6, initial_state=None,
              d_final_state=None, return_d_initial_state=False, chunk_tokens=0, workspace=None,
-             check=None):
+             check=None, saved=None):
     """Gradients of `prefill` for a loss with gradient `dout` w.r.t. the output (and
     `d_final_state` w.r.t. the final states).  q, k, v, gate, dout: [B, N, H, D].
     Returns (dq, dk, dv, dgate, dweight, d_initial_state or None); dweight and
-    d_initial_state are float32."""
+    d_initial_state are float32.  saved: the activations `prefill(...,
+    save_for_backward=True)` returned for the same inputs (y and the chunk
+    states are then read instead of recomputed)."""
     _same(q, q, k, v, gate, weight, dout)
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, gate, dout)):
         raise ValueError("q, k, v, gate, dout must share one [B, N, H, D] shape")
@@ -389,18 +459,29 @@ def backward(q, k, v, gate, weight, dout, *, block=64, eps=1e-6, initial_state=N
     if ws_bytes == 0:
         raise LightningAttnError(3, status_string(3))
     ws = _workspace(ws_bytes, dev, workspace)
-    _check(library().lightning_attn_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(init), _ptr(dfin),
-        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), B, N, H, D, int(block),
-        int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    if saved is not None:
+        sv, sv_bytes = _saved_arg(saved, saved_size(B * N, B, H, D, block, chunk_tokens, q.dtype),
+                                 dev)
+        _check(library().lightning_attn_backward_saved(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(init),
+            _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), B, N, H,
+            D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(sv), sv_bytes, _ptr(ws),
+            ws_bytes, _stream(dev)))
+    else:
+        _check(library().lightning_attn_backward(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(init),
+            _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), B, N, H,
+            D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes,
+            _stream(dev)))
     _check_device(ws, check)
     return dq, dk, dv, dg, dw, d_init
 
 
 def backward_varlen(q, k, v, gate, weight, dout, cu_seqlens, *, block=64, eps=1e-6,
                     initial_state=None, d_final_state=None, return_d_initial_state=False,
-                    chunk_tokens=0, workspace=None, check=None):
-    """Gradients of `prefill_varlen`; q, k, v, gate, dout: [T, H, D], cu_seqlens int32."""
+                    chunk_tokens=0, workspace=None, check=None, saved=None):
+    """Gradients of `prefill_varlen`; q, k, v, gate, dout: [T, H, D], cu_seqlens int32.
+    saved: as for `backward`."""
     _same(q, q, k, v, gate, weight, dout)
     if q.dim() != 3 or any(t.shape != q.shape for t in (k, v, gate, dout)):
         raise ValueError("q, k, v, gate, dout must share one [T, H, D] shape")
@@ -421,10 +502,19 @@ def backward_varlen(q, k, v, gate, weight, dout, cu_seqlens, *, block=64, eps=1e
     if ws_bytes == 0:
         raise LightningAttnError(3, status_string(3))
     ws = _workspace(ws_bytes, dev, workspace)
-    _check(library().lightning_attn_backward_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(cu_seqlens), nseq, T,
-        _ptr(init), _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw), _ptr(d_init), H,
-        D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws), ws_bytes, _stream(dev)))
+    if saved is not None:
+        sv, sv_bytes = _saved_arg(saved, saved_size(T, nseq, H, D, block, chunk_tokens, q.dtype), dev)
+        _check(library().lightning_attn_backward_varlen_saved(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(cu_seqlens),
+            nseq, T, _ptr(init), _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw),
+            _ptr(d_init), H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(sv),
+            sv_bytes, _ptr(ws), ws_bytes, _stream(dev)))
+    else:
+        _check(library().lightning_attn_backward_varlen(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(weight), _ptr(dout), _ptr(cu_seqlens),
+            nseq, T, _ptr(init), _ptr(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw),
+            _ptr(d_init), H, D, int(block), int(chunk_tokens), float(eps), _dtype(q), _ptr(ws),
+            ws_bytes, _stream(dev)))
     _check_device(ws, check)
     return dq, dk, dv, dg, dw, d_init
 

@@ -44,9 +44,11 @@ def test_header_declares_the_three_calls():
               "lightning_attn_softmax_prefill", "lightning_attn_softmax_prefill_varlen",
               "lightning_attn_softmax_workspace_size", "lightning_attn_softmax_decode",
               "lightning_attn_softmax_decode_workspace_size", "lightning_attn_workspace_status",
-              "lightning_attn_decode_noalloc"):
+              "lightning_attn_decode_noalloc", "lightning_attn_saved_size",
+              "lightning_attn_prefill_save", "lightning_attn_prefill_varlen_save",
+              "lightning_attn_backward_saved", "lightning_attn_backward_varlen_saved"):
         assert n in names
-    assert len(names) == 27
+    assert len(names) == 32
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -461,3 +463,51 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("CPU oracle", ""), os.path.join(dirpath, f)
+
+
+def test_saved_activations_validation(lib):
+    """Saving (and starting the backward from saved activations) is only for
+    the fused bf16 path; the buffer is checked like a workspace."""
+    sz = lib.lightning_attn_saved_size
+    y = 8192 * 64 * 128 * 2
+    assert y + 5 * 64 * 128 * 128 * 4 <= sz(8192, 1, 64, 128, 64, 0, BF16) < y + 5 * 64 * 128 * 128 * 4 + 4096
+    assert sz(8192, 1, 64, 128, 64, 0, F32) == 0          # fp32: portable kernels, no save
+    assert sz(8192, 1, 64, 64, 64, 0, BF16) == 0          # head_dim 64
+    assert sz(8192, 1, 64, 128, 32, 0, BF16) == 0         # block 32
+    assert sz(8192, 1, 257, 128, 64, 0, BF16) == 0        # more heads than CUs
+    assert sz(8192, 1, 64, 128, 64, -1, BF16) == 0
+    need = sz(1000, 2, 3, 128, 64, 0, BF16)
+    assert need > 0
+
+    def pre(saved=A, saved_bytes=1 << 40, dtype=BF16, d=128, block=64):
+        return lib.lightning_attn_prefill_save(A, A, A, A, A, A, None, None, 2, 500, 3, d, block,
+                                               0, 1e-6, dtype, saved, saved_bytes, A, 1 << 40, None)
+    assert pre(saved=None) == NULLP
+    assert pre(saved=A + 8) == MISAL
+    assert pre(saved_bytes=need - 1) == WS
+    assert pre(dtype=F32) == UNSUP
+    assert pre(d=64) == UNSUP
+    assert pre(block=32) == UNSUP
+
+    def bwd(saved=A, saved_bytes=1 << 40, dtype=BF16):
+        return lib.lightning_attn_backward_saved(A, A, A, A, A, A, None, None, A, A, A, A, A, None,
+                                                 2, 500, 3, 128, 64, 0, 1e-6, dtype, saved,
+                                                 saved_bytes, A, 1 << 40, None)
+    assert bwd(saved=None) == NULLP
+    assert bwd(saved_bytes=need - 1) == WS
+    assert bwd(dtype=F32) == UNSUP
+
+    def vpre(saved=A, saved_bytes=1 << 40, cu=A):
+        return lib.lightning_attn_prefill_varlen_save(A, A, A, A, A, A, cu, 2, 1000, None, None, 3,
+                                                      128, 64, 0, 1e-6, BF16, saved, saved_bytes,
+                                                      A, 1 << 40, None)
+    assert vpre(saved=None) == NULLP
+    assert vpre(saved_bytes=need - 1) == WS
+    assert vpre(cu=None) == NULLP
+
+    def vbwd(saved=A, saved_bytes=1 << 40):
+        return lib.lightning_attn_backward_varlen_saved(A, A, A, A, A, A, A, 2, 1000, None, None, A,
+                                                        A, A, A, A, None, 3, 128, 64, 0, 1e-6,
+                                                        BF16, saved, saved_bytes, A, 1 << 40, None)
+    assert vbwd(saved=None) == NULLP
+    assert vbwd(saved_bytes=need - 1) == WS

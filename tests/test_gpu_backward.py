@@ -190,3 +190,81 @@ def test_backward_8k_workload():
     dq, dk, dv, dg, dw, d_init = grads
     compare(tuple(t.view(N, H, D) for t in (dq, dk, dv, dg)) + (dw, d_init), ref, torch.bfloat16,
             "backward 8K x 64 heads")
+
+
+def grads_close(a, b, what, bar=1e-2):
+    """Two GPU gradient sets that differ only where y was rounded once more:
+    every tensor within `bar` of the largest magnitude of the first."""
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dw", "d_init"), a, b):
+        if x is None:
+            assert y is None
+            continue
+        scale = max(x.float().abs().max().item(), 1e-30)
+        err = (x.float() - y.float()).abs().max().item() / scale
+        say("%s %s: saved vs recomputed, max rel diff %.2e" % (what, name, err))
+        assert err < bar
+
+
+@pytest.mark.parametrize("B,N,H", [(2, 1000, 3), (1, 777, 2)])
+def test_backward_from_saved_activations(B, N, H):
+    """A prefill that saves y and the chunk states gives the same outputs as the
+    plain prefill (bit for bit); the backward from them matches the oracle, and
+    the backward that recomputes them to bf16 rounding."""
+    D, dtype = 128, torch.bfloat16
+    args, ref = batch_case(B, N, H, D, dtype, "unit", key=61)
+    q, k, v, g, w, dout, init, dfin = args
+    x = [dev(a, dtype).view(B, N, H, D) for a in (q, k, v, g)]
+    wd = dev(w, dtype)
+    gd = dev(dout, dtype).view(B, N, H, D)
+    st = lambda a: torch.from_numpy(a).cuda()
+    say("prefill with saved activations B", B, "N", N, "H", H)
+    plain, fs_plain = la.prefill(*x, wd, initial_state=st(init), return_final_state=True)
+    out, fs, saved = la.prefill(*x, wd, initial_state=st(init), return_final_state=True,
+                                save_for_backward=True, check=True)
+    torch.cuda.synchronize()
+    assert saved.numel() == la.saved_size(B * N, B, H, D)
+    assert torch.equal(out, plain) and torch.equal(fs, fs_plain)
+    # y as saved: the oracle's pre-norm output, to the bf16 bar
+    y_saved = saved[:B * N * H * D * 2].view(torch.bfloat16).view(B * N, H, D)
+    _, y_ref = oracle.prefill(q, k, v, g, w, cu_seqlens=np.arange(B + 1) * N, init_state=init,
+                              return_y=True)
+    check(host(y_saved), y_ref, dtype, "saved y")
+    say("backward from the saved activations")
+    kw = dict(initial_state=st(init), d_final_state=st(dfin), return_d_initial_state=True)
+    from_saved = la.backward(*x, wd, gd, saved=saved, check=True, **kw)
+    recomputed = la.backward(*x, wd, gd, **kw)
+    torch.cuda.synchronize()
+    T = B * N
+    flat = lambda gr: tuple(t.view(T, H, D) for t in gr[:4]) + tuple(gr[4:])
+    compare(flat(from_saved), ref, dtype, "from saved")
+    grads_close(flat(recomputed), flat(from_saved), "B=%d N=%d" % (B, N))
+
+
+def test_backward_varlen_from_saved_activations():
+    """Packed sequences (empty ones, several chunks each at 64-token chunks)."""
+    D, dtype, H = 128, torch.bfloat16, 3
+    lens = [0, 1, 200, 64, 0, 331]
+    seg = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, nseq = int(seg[-1]), len(lens)
+    q, k, v, g, w = inputs(T, H, D, "unit", key=62)
+    dout = host(dev(rnd(162, (T, H, D)), dtype))
+    init = rnd(163, (nseq, H, D, D), 0.5)
+    dfin = rnd(164, (nseq, H, D, D), 0.1)
+    ref = oracle.backward(q, k, v, g, w, dout, cu_seqlens=seg, init_state=init, d_final_state=dfin)
+    cu = torch.from_numpy(seg.astype(np.int32)).cuda()
+    x = [dev(a, dtype) for a in (q, k, v, g, w)]
+    st = lambda a: torch.from_numpy(a).cuda()
+    for chunk in (0, 64):
+        say("varlen saved activations, chunk", chunk)
+        plain = la.prefill_varlen(*x, cu, initial_state=st(init), chunk_tokens=chunk)
+        out, saved = la.prefill_varlen(*x, cu, initial_state=st(init), chunk_tokens=chunk,
+                                       save_for_backward=True, check=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain)
+        kw = dict(initial_state=st(init), d_final_state=st(dfin), return_d_initial_state=True,
+                  chunk_tokens=chunk)
+        from_saved = la.backward_varlen(*x, dev(dout, dtype), cu, saved=saved, check=True, **kw)
+        recomputed = la.backward_varlen(*x, dev(dout, dtype), cu, **kw)
+        torch.cuda.synchronize()
+        compare(from_saved, ref, dtype, "varlen from saved chunk=%d" % chunk)
+        grads_close(recomputed, from_saved, "varlen chunk=%d" % chunk)
