@@ -9,6 +9,10 @@ portable fp32 kernels (every tensor within 1e-4).  bf16 inputs at head_dim
 128 take the MFMA walks, whose operands (SiLU outputs, dy, the running
 state) are bf16 as in the forward: every gradient, including the fp32
 dweight and initial-state gradient, is then held to the bf16 bar.
+
+The backward from saved activations (a prefill that keeps y and the chunk
+states) is held to the same bar against the oracle, and compared with the
+recomputing backward, which it matches bit for bit on these shapes.
 """
 import numpy as np
 import pytest
@@ -183,9 +187,18 @@ def test_backward_8k_workload():
     dout = host(dev(rnd(8192, (N, H, D)), torch.bfloat16))
     say("backward 8K: inputs ready")
     x = [dev(a, torch.bfloat16).view(1, N, H, D) for a in (q, k, v, g, dout)]
-    grads = la.backward(*x[:4], dev(w, torch.bfloat16), x[4], return_d_initial_state=True)
+    wd = dev(w, torch.bfloat16)
+    grads = la.backward(*x[:4], wd, x[4], return_d_initial_state=True)
     torch.cuda.synchronize()
     say("backward 8K: GPU done")
+    # the training order at the same shape: a saving prefill, then the
+    # backward from its activations
+    _, saved = la.prefill(*x[:4], wd, save_for_backward=True, check=True)
+    from_saved = la.backward(*x[:4], wd, x[4], return_d_initial_state=True, saved=saved,
+                             check=True)
+    torch.cuda.synchronize()
+    grads_close(grads, from_saved, "backward 8K")
+    del saved, from_saved
     ref = oracle.backward(q, k, v, g, w, dout)
     dq, dk, dv, dg, dw, d_init = grads
     compare(tuple(t.view(N, H, D) for t in (dq, dk, dv, dg)) + (dw, d_init), ref, torch.bfloat16,
