@@ -40,7 +40,7 @@
 #define GEMM_NS 4
 #endif
 #ifndef GEMM_GROUP_M
-#define GEMM_GROUP_M 8
+#define GEMM_GROUP_M 4
 #endif
 #ifndef GEMM_WAVES
 #define GEMM_WAVES 8
