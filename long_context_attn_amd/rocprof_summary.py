@@ -49,6 +49,12 @@ def short_name(name: str) -> str:
     if m:  # still mangled (bf16 template arguments): keep namespace and identifier
         k = int(m.group(1))
         ident = n[m.end():m.end() + k]
+        # literal template arguments (bool and int), e.g. ILb1ELb0EE -> <true, false>
+        t = re.match(r"I((?:L[bi]\d+E)+)E", n[m.end() + k:])
+        if t:
+            args = re.findall(r"L([bi])(\d+)E", t.group(1))
+            return "la::%s<%s>" % (ident, ", ".join(
+                ("true" if v == "1" else "false") if ty == "b" else v for ty, v in args))
         return "la::" + ident + ("<bf16>" if "DF16b" in n else "")
     # kernels in an anonymous namespace: "la::(anonymous namespace)::name(args)"
     n = n.replace("(anonymous namespace)::", "")
