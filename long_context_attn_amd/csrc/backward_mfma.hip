@@ -193,9 +193,9 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
         const int64_t tbase = G.off0 + (int64_t)max(blk, 0) * MB * HD;
         // output positions: token t = 32 tb + l32, dims 32 w + 8 q + 4 g .. + 3
         const int ooff = l32 * HD + 32 * w + 4 * g;
-        // the raw inputs of the SiLU' factor, loaded ahead of the products
-        // (LEAN: after the products with the scores, when fewer registers are
-        // in use)
+        // the raw inputs of the SiLU' factor: loaded at the start of the
+        // iteration, so that both phases cover their latency (LEAN: after the
+        // products with the scores, where fewer registers are in use)
         bf16x4 rw[2][4];
         auto load_raw = [&]() {
             const __amdgpu_buffer_rsrc_t rr = tile_rsrc(raw + tbase, n, HD);
@@ -209,6 +209,7 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
         };
         // ---- phase 1: R^T X^T and the scores
         if (comp) {
+            if (EPI == 1 && !LEAN) load_raw();
             state_term();
             if (scores) {
                 constexpr int SH = LEAN ? MD / 32 : MD / 16;  // operands read at once
@@ -256,7 +257,6 @@ __device__ __forceinline__ void walk_consumer(const WalkGeom<REV>& G, const __bf
         }
         // ---- phase 2: V^T P^T into O, the state update, the outputs
         if (comp) {
-            if (EPI == 1 && !LEAN) load_raw();
             bf16x8 vop[MB / 16];
             bf16x8 pb[MB / 16][2];
             // P^T operand of token slice s for output tile tb (the slice that
