@@ -71,14 +71,14 @@ struct PrefillArgs {
     void* y_save;
     // MFMA prefill of uniform rows (cu == null): no plan kernel; the chunk-sum
     // kernel computes its chunks from (nseq, seqlen, chunk), and extra
-    // workgroups of it write the plan tables, reset the header and clear the
-    // exchange words for the kernels after it
+    // workgroups of it write the plan tables and reset the header; the state
+    // scan after it clears the exchange words
     bool inline_plan;
     // cross-head RMSNorm exchange of the fused MFMA walk, one slot per
     // (chunk, 64-token block): slot = chunk * (chunk_len / 64) + block.
     // Each word holds a float in its low half and 1 in its high half once
     // written (0 = not yet written); cleared on every call by the plan kernel
-    // (or, for uniform rows, by the chunk-sum kernel's extra workgroups).
+    // (or, for uniform rows, by the state scan).
     int n_slots;
     uint64_t* part;           // [n_slots][H][64] per-head sums of y^2 per token
     uint64_t* rsub;           // [n_slots][ceil(H / 16)][64] sums over groups of 16 heads

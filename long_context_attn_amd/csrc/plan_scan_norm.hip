@@ -59,12 +59,22 @@ hipError_t launch_plan(const PrefillArgs& a, hipStream_t st) {
 // sequence's chunks in order, replacing each chunk sum by the state that
 // enters the chunk, and stores the state after the last chunk.  With
 // skip_last the last chunk of a sequence has no sum (only its entering
-// state is written, and no final state).
+// state is written, and no final state).  For uniform rows on the MFMA path
+// the scan also zeroes the walk's exchange words (`clear`): done here, after
+// the chunk sums, the 5.6 MB of stores at 8192 x 64 heads no longer compete
+// with the chunk sums' reads (3-4 us less per prefill).
 constexpr int SCAN_THREADS = 256;
 
 __global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(
     float* __restrict__ states, const SegEntry* __restrict__ segs, const float* init,
-    float* fin, int H, int DD, int tiles, bool skip_last) {
+    float* fin, int H, int DD, int tiles, bool skip_last, uint64_t* __restrict__ clear,
+    int64_t clear_words) {
+    {
+        const int64_t stride = (int64_t)gridDim.x * SCAN_THREADS;
+        for (int64_t i = (int64_t)blockIdx.x * SCAN_THREADS + threadIdx.x; i < clear_words;
+             i += stride)
+            clear[i] = 0;
+    }
     const int pair = blockIdx.x / tiles;  // sequence * H + head
     const int tile = blockIdx.x - pair * tiles;
     const int e = (tile * SCAN_THREADS + threadIdx.x) * 4;
@@ -92,9 +102,12 @@ hipError_t launch_state_scan(const PrefillArgs& a, hipStream_t st) {
     const int tiles = (DD / 4 + SCAN_THREADS - 1) / SCAN_THREADS;
     const int64_t grid = (int64_t)a.nseq * a.H * tiles;
     if (grid == 0) return hipSuccess;
+    // uniform rows on the MFMA path: the chunk-sum kernel wrote the plan but
+    // left the exchange words to this kernel
+    const bool clr = a.inline_plan && a.clear != nullptr;
     hipLaunchKernelGGL(state_scan_kernel, dim3((unsigned)grid), dim3(SCAN_THREADS), 0, st,
                        a.states, a.segs, a.init_state, a.final_state, a.H, DD, tiles,
-                       a.skip_last);
+                       a.skip_last, clr ? a.clear : nullptr, clr ? a.clear_words : (int64_t)0);
     return hipGetLastError();
 }
 

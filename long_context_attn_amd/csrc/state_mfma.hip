@@ -37,7 +37,8 @@ struct StateLds {
 // per prefill than 512 threads with two rows each).
 // Uniform rows without a plan kernel: nseq rows of seqlen tokens cut into
 // cps = ceil(seqlen / chunk) chunks each; the last `extra` workgroups of the
-// grid write what the plan kernel would (tables, header, cleared words).
+// grid write what the plan kernel would (tables and header; the state scan
+// that follows clears the exchange words).
 struct InlinePlan {
     int extra;  // 0: the plan kernel ran, read its tables
     int nseq, cps, chunk;
@@ -187,8 +188,10 @@ hipError_t launch_chunk_sums_mfma(const PrefillArgs& a, const void* x, const voi
         ip.hdr = a.hdr;
         ip.segs = a.segs;
         ip.chunks = a.chunks;
-        ip.clear = a.clear;
-        ip.clear_words = a.clear_words;
+        // the exchange words are cleared by the scan after this kernel
+        // (stores here would compete with the sums' reads)
+        ip.clear = nullptr;
+        ip.clear_words = 0;
     }
     const dim3 grid((unsigned)((int64_t)a.max_chunks * a.H + ip.extra));
     auto* fn = silu_x ? (silu_y ? &chunk_state_mfma_kernel<true, true>
