@@ -90,6 +90,9 @@ def markdown(groups, title, command, min_calls=1):
         out.append("| %s | %d x %d | %d | %.1f | %.1f | %.1f | %.1f | %s | %s | %s |" % (
             name, nwg, wg, len(d), statistics.mean(d), statistics.median(d), min(d), max(d),
             g["vgpr"], g["agpr"], g["lds"]))
+    out += ["", "VGPR and AGPR are rocprofv3's VGPR_Count and Accum_VGPR_Count fields as the tool "
+            "reports them; for the large kernels they read about half of the register count in "
+            "the compiled code object (the walk: 124 here, .vgpr_count 242)."]
     return "\n".join(out) + "\n"
 
 
