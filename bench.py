@@ -11,11 +11,12 @@ gate ~ N(0,1), norm weight ~ N(1, 0.02), eps 1e-6 -- the whole layer: SiLU on
 q/k/v, causal Y = Q(K^T V) against the running fp32 state, RMSNorm(Y) *
 sigmoid(gate).  Inputs are synthetic (seeded), resident in HBM before timing.
 
-value = prefill tokens/s in steady state: the headline prefill is timed
-last among the GPU legs (W warm-up calls, then K timed calls), so that the
-clocks have settled under the other legs' load; the first few dozen calls on
-an idle GPU run ~20-30% slower.  Also reported: TFLOP/s on the block-tiled
-FLOP count, the per-kernel split (HIP events recorded between the library's
+value = prefill tokens/s in steady state: the headline prefill is the first
+GPU leg; 200 profiled calls (the per-kernel split) carry it past the clocks'
+ramp (the first ~100 calls on an idle GPU run up to 30% slower), then come W
+warm-up calls and K timed calls with no pause in between.  Also reported: TFLOP/s on the block-tiled
+FLOP count, the median and fastest single call (HIP events around each call of
+the settled stretch), the per-kernel split (HIP events recorded between the library's
 kernels on the stream they run on: the chunk sums, the scan of the states
 entering the chunks, and the walk with the RMSNorm fused), the roofline of
 the walk kernel and the whole call's HBM fraction, the state-only pass on the
@@ -26,8 +27,9 @@ layer with its projections (hidden 6144: four input GEMMs with SiLU in the
 epilogue, the attention, the output GEMM) as time per call, the hybrid's
 softmax attention layer on the same shape (rotary embedding on half of the
 head dimension, causal) as TFLOP/s and its decode step against a KV cache
-(32 sequences, cache lengths 1K..16K) as KV GB/s, the decode workload (256 sequences x 64 heads, fp32 state, 64 single-token steps)
-as state GB/s, the two 1,048,576-token prefills (a varlen pack and a single
+(32 sequences, cache lengths 1K..16K) as KV GB/s, the decode workload (256
+sequences x 64 heads, fp32 state, 64 single-token steps) as state GB/s with
+the 64 steps' total and the median and fastest single step, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores on
 bounded samples of the 8K prefill, the decode step and the two 1M-token
 workloads (65,536-token slices), each beside the GPU's figure.
@@ -39,6 +41,7 @@ import ctypes
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -190,25 +193,30 @@ def bench_prefill(args, la, torch, hip, inputs):
                out.data_ptr(), None, None, B, N, H, D, blk, 0, cfg["eps"], 1, ws.data_ptr(),
                ws_bytes, stream, evs[i], nst + 1)
         assert st == 0, st
-    torch.cuda.synchronize()
-    # the split averages the last `steps` profiled calls (the settled ones)
-    per = {n: 0.0 for n in names}
-    for i in range(nprof - args.steps, nprof):
-        for j, n in enumerate(names):
-            per[n] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / args.steps
-    for e in evs:
-        hip.destroy(e)
 
-    # the headline: W warm-up calls, then K timed calls
+    # the headline: W warm-up calls, then K timed calls, enqueued behind the
+    # profiled ones with no synchronisation in between: an idle spell of a few
+    # milliseconds (reading back the events above) restarts the clocks' ramp,
+    # and K = 20 calls right after it run up to 25% slower
     for _ in range(args.warmup):
         call()
-    torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
         call()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+
+    # the split averages the last `steps` profiled calls (the settled ones)
+    per = {n: 0.0 for n in names}
+    for i in range(nprof - args.steps, nprof):
+        for j, n in enumerate(names):
+            per[n] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / args.steps
+    # whole calls of the same settled stretch, one by one (first to last event)
+    per_call = sorted(hip.elapsed_ms(evs[i][0], evs[i][nst]) * 1e3
+                      for i in range(nprof - args.steps, nprof))
+    for e in evs:
+        hip.destroy(e)
     tokens = B * N
     tok_s = tokens / (ms * 1e-3)
     fl = flops_per_token(H, D, blk) * tokens
@@ -220,6 +228,9 @@ def bench_prefill(args, la, torch, hip, inputs):
     res = dict(
         ms_per_step=ms, tokens_per_s=tok_s, tflops=fl / (ms * 1e-3) / 1e12,
         layer_hbm_frac=call_frac,
+        # single calls from the per-kernel split (HIP events around each call,
+        # the last K of its calls): median and fastest
+        call_us_median=round(statistics.median(per_call), 2), call_us_min=round(per_call[0], 2),
         # the kernels of one call, from HIP events between them (uniform rows run
         # no plan kernel and the RMSNorm is fused into the walk: those stages
         # launch nothing and are not listed)
@@ -533,6 +544,7 @@ def bench_decode(args, la, torch, hip):
     for i in range(nprof):
         for j, n in enumerate(names):
             per[n] += hip.elapsed_ms(evs[i][j], evs[i][j + 1]) / nprof
+    step_us = sorted(hip.elapsed_ms(evs[i][0], evs[i][len(names)]) * 1e3 for i in range(nprof))
     for e in evs:
         hip.destroy(e)
     state_bytes = 2 * S * H * D * D * 4  # read + write of the fp32 state
@@ -557,6 +569,10 @@ def bench_decode(args, la, torch, hip):
     if not fused:
         kernels["decode_norm_kernel"] = round(per["decode_norm"] * 1e3, 2)
     res = dict(workload=cfg["workload"], steps=steps, ms_per_step=round(ms, 4),
+               ms_total=round(ms * steps, 3),
+               # single steps (HIP events around each of 16 further steps)
+               us_per_step_median=round(statistics.median(step_us), 2),
+               us_per_step_min=round(step_us[0], 2),
                tokens_per_s=round(S / (ms * 1e-3), 1),
                state_GBps=round(state_bytes / (ms * 1e-3) / 1e9, 1),
                state_hbm_frac=round(state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -776,17 +792,19 @@ def main():
         return
     hip = Hip()
     inputs = prefill_inputs()
-    # The other legs run first: they keep the GPU busy for a few seconds, so the
-    # headline prefill (W warm-up calls, then K timed ones) is measured at the
-    # clocks a loaded GPU holds.  Timed right after an idle spell, the first ~50
-    # calls run up to 30% slower while the clocks ramp up.
+    # The headline prefill runs first: its 200 profiled calls carry it past the
+    # clocks' ramp on a fresh burst (the first ~100 calls after an idle spell
+    # run up to 30% slower), and the W warm-up and K timed calls follow them
+    # with no pause.  Timed after the other legs instead (half a minute of
+    # backward, GEMM, softmax and 1M-token work), the same calls ran 20-25%
+    # slower on some boxes: the heat of unrelated work, not the prefill's rate.
+    pre = bench_prefill(args, la, torch, hip, inputs)
     bwd = None if args.no_backward else bench_backward(args, la, torch, inputs)
     layer = None if args.no_layer else bench_layer(args, la, torch)
     smx = None if args.no_softmax else bench_softmax(args, la, torch)
     smd = None if args.no_softmax else bench_softmax_decode(args, la, torch)
     dec = None if args.no_decode else bench_decode(args, la, torch, hip)
     long_ctx = None if args.no_long else bench_long(args, la, torch)
-    pre = bench_prefill(args, la, torch, hip, inputs)
     cpu = None
     if not args.no_cpu:
         gpu = {PREFILL_8K["workload"]: pre["tokens_per_s"]}
@@ -807,6 +825,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pre["ms_per_step"], 5),
+        "call_us_median": pre["call_us_median"],
+        "call_us_min": pre["call_us_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
