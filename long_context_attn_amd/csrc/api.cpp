@@ -104,10 +104,10 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
 
 // Backward workspace: [PlanHeader][SegEntry x nseq][ChunkEntry x max_chunks],
 // the forward chunk states and the reverse ones [max_chunks][H][D][D] fp32,
-// y [total][H][D] fp32, dy [total][H][D] (bf16 on the MFMA path, else
-// fp32), on the portable path q~, k~, v~ [total][H][D] fp32, and the dw
-// partial sums [ceil(total / norm tokens) + slices][H*D] fp32.  Automatic chunks: the
-// MFMA walks (a 512-thread workgroup per CU) take the prefill's choice; the
+// y and dy [total][H][D] (bf16 on the MFMA path, else fp32), on the portable
+// path q~, k~, v~ [total][H][D] fp32, and the dw partial sums
+// [ceil(total / norm tokens) + slices][H*D] fp32.  Automatic chunks: the
+// MFMA walks (one workgroup per CU) take the prefill's choice; the
 // portable walks, a workgroup of only head_dim threads each, the longest
 // power of two (at least the block) that gives about 8 walks per CU.
 bool backward_mfma_path(int head_dim, la_dtype dtype) {
