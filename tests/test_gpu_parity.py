@@ -87,6 +87,22 @@ def test_bf16_ragged(D, block, dist):
         assert rel_state(host(fs), st) < STATE_TOL[torch.bfloat16]
 
 
+def test_bf16_more_heads_than_cus():
+    """bf16, head_dim 128, block 64 with more heads than the device has CUs:
+    the fused walk's cross-head exchange needs every head of a chunk resident
+    at once, so such calls run the portable kernels (walk, then the separate
+    norm); they must still match the oracle, with a ragged tail and a final
+    state."""
+    H = torch.cuda.get_device_properties(0).multi_processor_count + 4
+    N, D = 130, 128
+    q, k, v, g, w = inputs(N, H, D, "unit", key=13)
+    ref, st = oracle_prefill(q, k, v, g, w, 1)
+    say("bf16 with", H, "heads (more than the CUs)")
+    out, fs = run_prefill(q, k, v, g, w, 1, torch.bfloat16, 64, 0)
+    check(out, ref, torch.bfloat16, "bf16 H=%d" % H)
+    assert rel_state(host(fs), st) < STATE_TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype,D,block", [(torch.float32, 64, 32), (torch.bfloat16, 128, 64)])
 def test_varlen_packed(dtype, D, block):
     lens = [0, 1, 63, 64, 65, 130, 700, 0, 3, 2 * block + 7]
