@@ -639,9 +639,12 @@ def bench_long(args, la, torch):
     return res
 
 
-def pmc_pass(args, la, torch):
+def pmc_pass(args, la, torch, compute=False):
     """Kernels for one rocprofv3 --pmc pass: a copy of exactly 1 GiB (the
-    calibration reference for the traffic counters) and the prefill workload."""
+    calibration reference for the traffic counters), the prefill workload and
+    the decode step; with `compute` also the layer with its projections and
+    the softmax layer (compute-counter passes only: the traffic summary keys
+    kernels by name, and the layer's attention kernels share the prefill's)."""
     from long_context_attn_amd import synth
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -674,7 +677,28 @@ def pmc_pass(args, la, torch):
     for _ in range(args.steps):
         la.decode(*x, wdd, state, out=torch.empty_like(x[0]), workspace=dws)
     torch.cuda.synchronize()
-    log("pmc pass done: copy 1 GiB + %d prefill calls + %d decode steps" % (args.steps, args.steps))
+    del state, x, dws
+    if not compute:
+        log("pmc pass done: copy 1 GiB + %d prefill calls + %d decode steps" % (args.steps, args.steps))
+        return
+    # the layer with its projections (the library's GEMM kernel) and the softmax
+    # layer, at their bench shapes (8192 tokens, hidden 6144 / 64 heads x 128)
+    hidden, HD = LAYER_HIDDEN, H * D
+    xl = torch.randn(1, 8192, hidden, device="cuda", generator=gen).to(torch.bfloat16)
+    wq = (torch.randn(4, hidden, HD, device="cuda", generator=gen) / math.sqrt(hidden)).to(torch.bfloat16)
+    wo = (torch.randn(HD, hidden, device="cuda", generator=gen) / math.sqrt(HD)).to(torch.bfloat16)
+    lws = torch.empty(la.layer_workspace_size(8192, 1, hidden, H, D), dtype=torch.uint8, device="cuda")
+    for _ in range(args.steps):
+        la.layer_prefill(xl, wq, wdd, wo, eps=cfg["eps"], workspace=lws, gemm="mfma")
+    torch.cuda.synchronize()
+    del xl, wq, wo, lws
+    xs = [torch.randn(1, 8192, H, D, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(3)]
+    sws = torch.empty(la.softmax_workspace_size(8192, 1, H, D, D // 2), dtype=torch.uint8, device="cuda")
+    for _ in range(args.steps):
+        la.softmax_prefill(*xs, workspace=sws)
+    torch.cuda.synchronize()
+    log("pmc pass done: copy 1 GiB + %d prefill calls + %d decode steps + %d layer calls + %d "
+        "softmax-layer calls" % ((args.steps,) * 4))
 
 
 def _timed(fn, min_s, max_runs=10):
@@ -774,6 +798,9 @@ def main():
                     help="counter-collection run: a 1 GiB device copy (calibrates FETCH_SIZE / "
                          "WRITE_SIZE against a known byte count), then --steps prefill calls and "
                          "--steps decode steps; prints no JSON")
+    ap.add_argument("--pmc-compute", action="store_true",
+                    help="as --pmc-pass, and also --steps calls each of the layer with its "
+                         "projections and the softmax layer (for compute counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the layer "
@@ -787,8 +814,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     la.library()  # fail loudly if the HIP library is missing
-    if args.pmc_pass:
-        pmc_pass(args, la, torch)
+    if args.pmc_pass or args.pmc_compute:
+        pmc_pass(args, la, torch, compute=args.pmc_compute)
         return
     hip = Hip()
     inputs = prefill_inputs()

@@ -117,7 +117,12 @@ def counters_summary(path, title, command, simds=1024):
             name = r["Kernel_Name"]
             if "la::" not in name and not name.startswith("_ZN2la"):
                 continue
+            # one row per kernel and launch shape (a kernel launched on two
+            # shapes, such as the two projection GEMMs, gets two rows)
+            wg = int(r.get("Workgroup_Size") or 0)
+            grid = int(r.get("Grid_Size") or 0)
             k = short_name(name).replace("la::", "")
+            k = "%s | %s" % (k, "%d x %d" % (grid // wg, wg) if wg > 0 else "-")
             vals.setdefault(k, OrderedDict()).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
     names = []
@@ -133,8 +138,8 @@ def counters_summary(path, title, command, simds=1024):
                  "unit's busy cycles over all %d SIMDs, and the cycles the CUs spend issuing "
                  "vector-ALU instructions, each against the GPU's active cycles." % simds)
     out += ["", note, "",
-            "| kernel | dispatches | " + " | ".join(names) + " |",
-            "|---|---|" + "---|" * len(names)]
+            "| kernel | workgroups x threads | dispatches | " + " | ".join(names) + " |",
+            "|---|---|---|" + "---|" * len(names)]
     for k, d in vals.items():
         row = [k, str(max(len(v) for v in d.values()))]
         for c in names:
