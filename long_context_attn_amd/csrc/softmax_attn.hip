@@ -339,6 +339,13 @@ __global__ __launch_bounds__(64 * NW, 2) void softmax_fwd_kernel(
             const __bf16* sK = L.k[1 - P];
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) Sn[qt][0] = Sn[qt][1] = f32x16{};
+            // The two waves on a SIMD come from different workgroups and run
+            // out of step; raising this wave's issue priority while it
+            // interleaves its score products with the exponentials, and
+            // dropping it for the P.V products, lets the SIMD favour the phase
+            // that feeds both units (8192 x 64 heads: 1131 -> 1088 us per
+            // call, identical outputs; priorities 1 to 3 measure alike).
+            __builtin_amdgcn_s_setprio(1);
             bf16x8 ka[3][2];  // K operands, read two steps ahead
             ka[0][0] = ld_row_operand(sK, l32, 8 * g);
             ka[0][1] = ld_row_operand(sK, 32 + l32, 8 * g);
@@ -383,6 +390,7 @@ __global__ __launch_bounds__(64 * NW, 2) void softmax_fwd_kernel(
             }
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) lsum[qt] += ps[qt];
+            __builtin_amdgcn_s_setprio(0);
             // O^T += V^T P^T, V operands read three products ahead (LDS latency
             // is what the products wait on here)
             const __bf16* sV = L.v[P];
