@@ -29,7 +29,8 @@ softmax attention layer on the same shape (rotary embedding on half of the
 head dimension, causal) as TFLOP/s and its decode step against a KV cache
 (32 sequences, cache lengths 1K..16K) as KV GB/s, the decode workload (256
 sequences x 64 heads, fp32 state, 64 single-token steps) as state GB/s with
-the 64 steps' total and the median and fastest single step, the two 1,048,576-token prefills (a varlen pack and a single
+the 64 steps' total, the median and fastest single step, and the rate of the
+64 steps replayed from one HIP graph, the two 1,048,576-token prefills (a varlen pack and a single
 sequence) as time per call, and the CPU oracle timed on this host's cores on
 bounded samples of the 8K prefill, the decode step and the two 1M-token
 workloads (65,536-token slices), each beside the GPU's figure.
@@ -522,6 +523,26 @@ def bench_decode(args, la, torch, hip):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the same 64 steps captured in one HIP graph and replayed (one launch for
+    # the whole sequence of steps; the state advances as in the eager loop)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(inp[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(inp[i])
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    del graph
     # per-kernel split
     lib = la.library()
     names = stage_names(lib, "decode")
@@ -570,6 +591,8 @@ def bench_decode(args, la, torch, hip):
         kernels["decode_norm_kernel"] = round(per["decode_norm"] * 1e3, 2)
     res = dict(workload=cfg["workload"], steps=steps, ms_per_step=round(ms, 4),
                ms_total=round(ms * steps, 3),
+               # the 64 steps replayed from one HIP graph
+               ms_per_step_graph=round(graph_ms, 4),
                # single steps (HIP events around each of 16 further steps)
                us_per_step_median=round(statistics.median(step_us), 2),
                us_per_step_min=round(step_us[0], 2),
