@@ -106,7 +106,7 @@ bool plan_layout(int64_t total, int nseq, int heads, int head_dim, int block, in
 // the forward chunk states and the reverse ones [max_chunks][H][D][D] fp32,
 // y and dy [total][H][D] (bf16 on the MFMA path, else fp32), on the portable
 // path q~, k~, v~ [total][H][D] fp32, and the dw partial sums
-// [ceil(total / norm tokens) + slices][H*D] fp32.  Automatic chunks: the
+// [ceil(total / norm tokens)][H*D] fp32.  Automatic chunks: the
 // MFMA walks (one workgroup per CU) take the prefill's choice; the
 // portable walks, a workgroup of only head_dim threads each, the longest
 // power of two (at least the block) that gives about 8 walks per CU.
@@ -168,7 +168,7 @@ bool backward_layout(int64_t total, int nseq, int heads, int head_dim, int block
         }
     }
     L->off_dw = off;
-    off = align_up(off + sizeof(float) * (size_t)(ntb + la::backward_dw_slices()) * heads * head_dim);
+    off = align_up(off + sizeof(float) * (size_t)ntb * heads * head_dim);
     L->bytes = off;
     return true;
 }

@@ -344,30 +344,57 @@ __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
     }
 }
 
-// dw from the partial sum rows in two fixed-order levels: slice s of
-// DW_SLICES adds rows [s n / S, (s + 1) n / S) into row n + s, then the
-// slices are added in order.
-constexpr int DW_SLICES = 32;
-__global__ __launch_bounds__(EW_THREADS) void dw_slice_kernel(float* __restrict__ part, int nparts,
-                                                              int HD) {
-    const int i = blockIdx.x * EW_THREADS + threadIdx.x;
-    const int s = blockIdx.y;
-    if (i >= HD) return;
-    const int p0 = (int)((int64_t)s * nparts / DW_SLICES);
-    const int p1 = (int)((int64_t)(s + 1) * nparts / DW_SLICES);
-    float acc = 0.f;
-    for (int p = p0; p < p1; ++p) acc += part[(int64_t)p * HD + i];
-    part[(int64_t)(nparts + s) * HD + i] = acc;
-}
-__global__ __launch_bounds__(EW_THREADS) void dw_final_kernel(const float* __restrict__ part,
-                                                              float* __restrict__ dw, int nparts,
-                                                              int HD) {
-    const int i = blockIdx.x * EW_THREADS + threadIdx.x;
-    if (i >= HD) return;
-    float acc = 0.f;
+// dw from the partial sum rows in one launch, in an order fixed by the row
+// count alone: a workgroup owns DW_COLS columns; its thread (j, i), j < 8
+// the column quad and i < DW_GROUPS the row group, adds rows i, i +
+// DW_GROUPS, i + 2 DW_GROUPS, ... of its quad (all of a thread's loads in
+// flight at once for up to 8 DW_GROUPS rows), then the row groups are added
+// in LDS, 8 at a time and then the 16 results, in index order.
+constexpr int DW_THREADS = 1024;
+constexpr int DW_GROUPS = DW_THREADS / 8;  // 128 row groups
+constexpr int DW_COLS = 32;                // 8 quads of 4 columns
+__global__ __launch_bounds__(DW_THREADS) void dw_reduce_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ dw, int nparts,
+                                                               int HD) {
+    __shared__ float4 lv[DW_GROUPS][8];
+    __shared__ float4 lv2[16][8];
+    const int tid = threadIdx.x, j = tid & 7, i = tid >> 3;
+    const int col = blockIdx.x * DW_COLS + 4 * j;  // HD is a multiple of 16
+    const bool in = col < HD;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (in) {
+        const float* p = part + col;
+        int r = i;
+        for (; r + 7 * DW_GROUPS < nparts; r += 8 * DW_GROUPS) {
+            float4 x[8];
 #pragma unroll
-    for (int s = 0; s < DW_SLICES; ++s) acc += part[(int64_t)(nparts + s) * HD + i];
-    dw[i] = acc;
+            for (int u = 0; u < 8; ++u)
+                x[u] = *reinterpret_cast<const float4*>(p + (int64_t)(r + u * DW_GROUPS) * HD);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += x[u];
+        }
+        for (; r < nparts; r += DW_GROUPS)
+            acc += *reinterpret_cast<const float4*>(p + (int64_t)r * HD);
+    }
+    lv[i][j] = acc;
+    __syncthreads();
+    if (tid < 128) {
+        const int g = tid >> 3;
+        float4 s = lv[8 * g][j];
+#pragma unroll
+        for (int u = 1; u < 8; ++u) s += lv[8 * g + u][j];
+        lv2[g][j] = s;
+    }
+    __syncthreads();
+    if (tid < 8 && in) {
+        float4 s = lv2[0][j];
+#pragma unroll
+        for (int u = 1; u < 16; ++u) s += lv2[u][j];
+        dw[col] = s.x;  // the caller's dweight may be only 4-byte aligned
+        dw[col + 1] = s.y;
+        dw[col + 2] = s.z;
+        dw[col + 3] = s.w;
+    }
 }
 
 // Walk block: 16 tokens whatever the forward's block (the result does not
@@ -397,13 +424,9 @@ hipError_t walk(const BackwardArgs& a, const float* X, const float* K, const flo
 }
 
 hipError_t dw_reduce(const BackwardArgs& a, int HD) {
-    const unsigned cols = (unsigned)((HD + EW_THREADS - 1) / EW_THREADS);
-    hipLaunchKernelGGL(dw_slice_kernel, dim3(cols, DW_SLICES), dim3(EW_THREADS), 0, a.stream,
-                       a.dw_part, a.n_tb, HD);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dw_final_kernel, dim3(cols), dim3(EW_THREADS), 0, a.stream, a.dw_part, a.dw,
-                       a.n_tb, HD);
+    const unsigned grid = (unsigned)((HD + DW_COLS - 1) / DW_COLS);
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3(grid), dim3(DW_THREADS), 0, a.stream, a.dw_part,
+                       a.dw, a.n_tb, HD);
     return hipGetLastError();
 }
 
@@ -528,7 +551,6 @@ int64_t backward_norm_tokens(int64_t total) {
     const int64_t t = (total + NB_GROUPS - 1) / NB_GROUPS;
     return t > NB_TOKENS ? t : (int64_t)NB_TOKENS;
 }
-int backward_dw_slices() { return DW_SLICES; }
 int backward_max_hd() { return 16 * 8 * EW_THREADS; }
 
 // After the plan: every kernel of the backward.  With no token at all the

@@ -125,8 +125,7 @@ struct BackwardArgs {
     // workspace: y [T][H][D] and dy [T][H][D] (fp32; bf16 on the MFMA path,
     // where y is read through a cast); q~, k~, v~ [T][H][D] fp32 (portable
     // path only); reverse chunk
-    // sums / G_exit [max_chunks][H][D][D]; dw partial sums
-    // [n_tb + backward_dw_slices()][H*D]
+    // sums / G_exit [max_chunks][H][D][D]; dw partial sums [n_tb][H*D]
     float *qs, *ks, *vs, *y, *gstates, *dw_part;
     void* dy;
     int n_tb;
@@ -136,7 +135,6 @@ struct BackwardArgs {
     bool saved;
 };
 int64_t backward_norm_tokens(int64_t total);  // tokens per dw partial sum row
-int backward_dw_slices();     // extra dw rows for the second reduction level
 int backward_max_hd();        // largest heads * head_dim of the norm backward
 hipError_t launch_backward(const BackwardArgs& a);
 // bf16 MFMA walks of the backward (bf16, head_dim 128)
