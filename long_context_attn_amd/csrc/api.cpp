@@ -803,7 +803,9 @@ static la_status backward_impl(const void* q, const void* k, const void* v, cons
     a.dy = ws + L.off_dy;
     a.dw_part = reinterpret_cast<float*>(ws + L.off_dw);
     a.n_tb = L.n_tb;
-    hipError_t e = la::launch_plan(p, stream);
+    // uniform rows on the MFMA path: the first chunk-sum kernel writes the plan
+    p.inline_plan = L.mfma && cu == nullptr && seqlen > 0;
+    hipError_t e = p.inline_plan ? hipSuccess : la::launch_plan(p, stream);
     if (e == hipSuccess) e = la::launch_backward(a);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

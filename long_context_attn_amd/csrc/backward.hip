@@ -467,13 +467,17 @@ hipError_t reverse_scan(const BackwardArgs& a) {
 // bf16 MFMA path (bf16, head_dim 128): chunk sums and walks on MFMA, the
 // operands read from the activations with SiLU applied on load; dy is bf16.
 hipError_t backward_mfma(const BackwardArgs& a) {
-    const PrefillArgs& p = a.p;
+    // With an inline plan (uniform rows), the first chunk-sum launch writes
+    // the plan tables that the later kernels read; the others take `p`.
+    const PrefillArgs& first = a.p;
+    PrefillArgs p = a.p;
+    p.inline_plan = false;
     hipStream_t st = a.stream;
     const int HD = p.H * p.D;
     hipError_t e = hipSuccess;
     if (!a.saved) {
-        if ((e = launch_chunk_sums_mfma(p, p.k, p.v, true, true, p.states, SumSkip::last, st)) !=
-            hipSuccess)
+        if ((e = launch_chunk_sums_mfma(first, p.k, p.v, true, true, p.states, SumSkip::last,
+                                        st)) != hipSuccess)
             return e;
         PrefillArgs s = p;
         s.final_state = nullptr;
@@ -484,7 +488,7 @@ hipError_t backward_mfma(const BackwardArgs& a) {
     if ((e = norm_backward<__bf16, __bf16, __bf16>(a, (__bf16*)a.dy)) != hipSuccess) return e;
     if ((e = dw_reduce(a, HD)) != hipSuccess) return e;
     // each sequence's first chunk sum only feeds dS0
-    if ((e = launch_chunk_sums_mfma(p, p.q, a.dy, true, false, a.gstates,
+    if ((e = launch_chunk_sums_mfma(a.saved ? first : p, p.q, a.dy, true, false, a.gstates,
                                     a.d_init ? SumSkip::none : SumSkip::first, st)) != hipSuccess)
         return e;
     if ((e = reverse_scan(a)) != hipSuccess) return e;
