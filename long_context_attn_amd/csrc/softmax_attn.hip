@@ -524,8 +524,10 @@ __global__ __launch_bounds__(DEC_THREADS) void softmax_split_kernel(
 #pragma unroll
         for (int u = 0; u < DEC_UNROLL; ++u) {
             const int jj = min(j + u * DEC_KEYS, nk - 1);
-            kk[u] = *reinterpret_cast<const bf16x8*>(kc + base + (int64_t)jj * MD);
-            vv[u] = *reinterpret_cast<const bf16x8*>(vc + base + (int64_t)jj * MD);
+            kk[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const bf16x8*>(kc + base + (int64_t)jj * MD));
+            vv[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const bf16x8*>(vc + base + (int64_t)jj * MD));
         }
 #pragma unroll
         for (int u = 0; u < DEC_UNROLL; ++u) {
