@@ -220,7 +220,9 @@ struct Piece<float> {
 template <>
 struct Piece<__bf16> {
     bf16x8 v;
-    __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ void load(const __bf16* p) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+    }
     __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
     __device__ __forceinline__ void fence() {
         f32x4 x = __builtin_bit_cast(f32x4, v);
