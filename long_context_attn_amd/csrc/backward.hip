@@ -201,6 +201,17 @@ __device__ __forceinline__ void store8(__bf16* p, const float (&x)[8]) {
     for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
     *reinterpret_cast<bf16x8*>(p) = v;
 }
+// the same with the non-temporal hint, for values nothing reads again
+__device__ __forceinline__ void store8_nt(float* p, const float (&x)[8]) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p + 4));
+}
+__device__ __forceinline__ void store8_nt(__bf16* p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+}
 
 // 8 consecutive elements kept in their storage type (bf16 pieces take half
 // the registers of fp32 ones), widened to fp32 where they are used
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(EW_THREADS) void norm_backward_kernel(
                     dwp[c][i][tid] += go[c][i] * yh * sg;
                 }
                 store8(dy + base + 8 * ch, d1);
-                store8(dg + base + 8 * ch, d2);
+                store8_nt(dg + base + 8 * ch, d2);
             }
         }
     }
