@@ -127,8 +127,10 @@ __global__ __launch_bounds__(ST_THREADS) void chunk_state_mfma_kernel(
     for (int i = 0; i < SPF; ++i) {
         load_rows(k, i, tk[i]);
         load_rows(v, i, tv[i]);
-        // sets issued in order: the loop then waits for set i with the later
-        // sets still in flight (reordered, the first wait would drain them all)
+        // keeps the compiler from issuing all sets' loads of one tensor first;
+        // it still issues k1 k2 k3 before v1 v2 v3, so two steps of every
+        // pass wait one set early (issuing the sets in order, which needs the
+        // loads marked volatile, measured the same)
         __builtin_amdgcn_sched_barrier(0);
     }
     const int l32 = lane & 31, g = lane >> 5;
