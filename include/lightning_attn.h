@@ -389,7 +389,7 @@ LA_API la_status lightning_attn_softmax_prefill_varlen(
  *                     untouched) and marked 1 in the workspace's first nseq int32
  *                     words (0 for the others), written on every call.
  * bf16 and head_dim 128 only.  Work: the cached keys and values are read once
- * (split over ranges of 512 keys, then combined).
+ * (split over ranges of 768 keys, then combined).
  */
 LA_API size_t lightning_attn_softmax_decode_workspace_size(int nseq, int max_len, int heads,
                                                            int head_dim);

@@ -21,6 +21,9 @@
 namespace la {
 
 constexpr int DEC_THREADS = 1024;
+#ifndef LA_DEC_ROT
+#define LA_DEC_ROT 1
+#endif
 
 // One (sequence, head) pair: S += k~^T v~ in place, y = q~ S.  Leaves y[j] in
 // ysum[j] and returns sum_j y_j^2 in every thread of the workgroup.
@@ -125,12 +128,20 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_seq_kernel(
     const int tid = threadIdx.x;
     const int cq = tid % TPR, rg = tid / TPR, j0 = cq * 4;
     const int64_t DD = (int64_t)D * D;
-    // rows of head hh's state with the non-temporal hint; a head past the last
+    // The heads are visited in an order rotated by the sequence: step i takes
+    // head (i + rot) mod H.  All workgroups run in step, so without the
+    // rotation every one of them would stream the state of the same head,
+    // addresses a multiple of H * 64 KiB apart.  y and the sums of squares are
+    // kept per head and summed in head order, so the output does not depend
+    // on the rotation.
+    const int rot = (int)((s * LA_DEC_ROT) % H);
+    auto head = [&](int i) { return i + rot < H ? i + rot : i + rot - H; };
+    // rows of step i's head with the non-temporal hint; a step past the last
     // gets an empty range (its loads return zeros and touch no memory)
-    auto load_rows = [&](int hh, f32x4 (&r)[RPT]) {
-        const bool in = hh < H;
+    auto load_rows = [&](int i, f32x4 (&r)[RPT]) {
+        const bool in = i < H;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(state + (s * H + (in ? hh : 0)) * DD), (short)0,
+            (void*)(state + (s * H + (in ? head(i) : 0)) * DD), (short)0,
             __builtin_amdgcn_readfirstlane(in ? (int)(DD * 4) : 0), 0x00020000);
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
@@ -139,21 +150,22 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_seq_kernel(
                 f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i * TPR + cq) * 16, 0, 2));
         }
     };
-    auto silu_qkv = [&](int hh) {
-        if (hh < H && tid < D) {
-            const int64_t idx = (s * H + hh) * D + tid;
-            qkv[hh % 3][0][tid] = silu_f(to_f32(q[idx]));
-            qkv[hh % 3][1][tid] = silu_f(to_f32(k[idx]));
-            qkv[hh % 3][2][tid] = silu_f(to_f32(v[idx]));
+    auto silu_qkv = [&](int i) {
+        if (i < H && tid < D) {
+            const int64_t idx = (s * H + head(i)) * D + tid;
+            qkv[i % 3][0][tid] = silu_f(to_f32(q[idx]));
+            qkv[i % 3][1][tid] = silu_f(to_f32(k[idx]));
+            qkv[i % 3][2][tid] = silu_f(to_f32(v[idx]));
         }
     };
-    // y of head hh (sum over the row groups, in order) and its sum of squares
-    // per wave
-    auto finish = [&](int hh) {
+    // y of step i's head (sum over the row groups, in order) and its sum of
+    // squares per wave
+    auto finish = [&](int i) {
+        const int hh = head(i);
         float sq = 0.f;
         if (tid < D) {
             float yj = 0.f;
-            for (int r = 0; r < NW; ++r) yj += red[hh & 1][r][tid / 4][tid % 4];
+            for (int r = 0; r < NW; ++r) yj += red[i & 1][r][tid / 4][tid % 4];
             ys[hh * D + tid] = yj;
             sq = yj * yj;
         }
@@ -177,7 +189,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_seq_kernel(
         const float* vs = qkv[h % 3][2];
         const f32x4 vj = {vs[j0], vs[j0 + 1], vs[j0 + 2], vs[j0 + 3]};
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        f32x4* S = reinterpret_cast<f32x4*>(state + (s * H + h) * DD);
+        f32x4* S = reinterpret_cast<f32x4*>(state + (s * H + head(h)) * DD);
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + m * NRG;

@@ -447,13 +447,20 @@ __global__ __launch_bounds__(64 * NW, 2) void softmax_fwd_kernel(
 // the keys of one (sequence, head) are one contiguous stream.  Step 1: per sequence, rotate the new key at
 // position len and store it with the value at slot len; rotate the query
 // (kept in fp32).  Step 2: one 256-thread workgroup per (sequence, head,
-// 512-key range): 16 threads per key (8 features each), 16 keys at a time,
+// 768-key range): 16 threads per key (8 features each), 16 keys at a time,
 // each thread keeping a running maximum, sum and 8 output features over the
 // keys it saw; the 16 key slots are merged in LDS into one partial.  Step 3:
 // the partials of a (sequence, head) are merged and normalised.
-constexpr int DEC_THREADS = 256;
+#ifndef LA_SM_DEC_THREADS
+#define LA_SM_DEC_THREADS 256
+#endif
+#ifndef LA_SM_DEC_UNROLL
+#define LA_SM_DEC_UNROLL 4
+#endif
+constexpr int DEC_THREADS = LA_SM_DEC_THREADS;
 constexpr int DEC_KEYS = DEC_THREADS / 16;  // keys per pass
-constexpr int DEC_UNROLL = 4;               // passes whose loads are in flight together
+constexpr int DEC_UNROLL = LA_SM_DEC_UNROLL;  // passes whose loads are in flight together
+static_assert(DEC_THREADS >= MD && DEC_THREADS % 64 == 0, "the merge uses one thread per feature");
 
 __global__ __launch_bounds__(DEC_THREADS) void softmax_append_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,

@@ -134,6 +134,7 @@ def _decode_case(lens, H, max_len, key):
 
 @pytest.mark.parametrize("lens,H,max_len", [
     ([0, 1, 511, 512, 513, 1500, 7], 2, 1600),   # empty cache, one key, split edges
+    ([767, 768, 769, 1535, 1536, 3], 2, 2400),    # edges of the 768-key ranges
     ([4000, 2048], 4, 4096),
 ])
 def test_softmax_decode(lens, H, max_len):
